@@ -1,0 +1,226 @@
+"""Seeded synthetic inputs for the block-scaled GEMM workloads.
+
+This module only draws random operands and encodes them into the storage formats
+(bf16, e4m3 codes, e2m1 nibbles, UE8M0 exponent bytes).  It holds none of the
+GEMM's arithmetic; the GPU library and the CPU oracle both take its bytes as
+they are.  Every draw uses an explicit ``torch.Generator`` so a (workload, seed,
+device) triple always yields the same bytes.
+
+Workloads (the shapes follow the dense 4096x7168x16384 case and the MoE routing
+shape of 16384 tokens, hidden 7168, top-6 of 256 experts that the pages report
+on: "DeepSeek lanza kernels de DeepGEMM para Huawei Ascend 950", section "Que
+alcance tienen las pruebas de rendimiento"; "DeepSeek publica bibliotecas Ascend
+para calculo e comunicacao de IA", section "Resultados de kernel e comunicacao"):
+
+  bf16_small    BF16 256x256x512, N(0,1) rounded to bf16
+  fp8_mid       FP8 1024x2048x4096, 1x128 (A) and 128x128 (B) UE8M0 scales
+  bf16_large    BF16 4096x7168x16384
+  fp8_large     FP8 4096x7168x16384, scales as fp8_mid
+  moe_fp8       M-grouped FP8: 256 experts, N=2048, K=7168, Zipf(1.1) routing
+  fp4_large     FP4 4096x7168x16384, 1x32 UE8M0 scales on both operands
+
+Value recipes:
+  * FP8: for every scale entry an exponent e ~ U{-8..4}; a value is
+    e4m3(clip(x / 2^e, -448, 448)) with x ~ N(0,1); torch's cast rounds to
+    nearest even.  The scale byte is e + 127.
+  * FP4: per 32-wide K-block, e = floor(log2(amax)) - 2 (the OCP MX rule, e2m1's
+    largest exponent is 2); x / 2^e is rounded to nearest (ties to the even code)
+    onto the e2m1 grid, saturating at 6.  An all-zero block gets e = 0.
+  * MoE routing: 16384 tokens x top-6 = 98304 assignments drawn multinomially
+    over 256 experts with popularity p_r ~ r^-1.1 (rank r = 1..256), ranks mapped
+    to expert ids by a seeded permutation; every count is padded up to a multiple
+    of 128.  Padding rows hold zero codes and scale byte 127.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+# e2m1 magnitude codes 0..7 are 0, .5, 1, 1.5, 2, 3, 4, 6.  Rounding to nearest
+# with ties to the even code means the decision points below (a tie at a point
+# that excludes it goes down, one that includes it goes up).
+_E2M1_UP_STRICT = (0.25, 1.25, 2.5, 5.0)      # at the tie, stay on the even code below
+_E2M1_UP_INCL = (0.75, 1.75, 3.5)             # at the tie, move up to the even code above
+
+
+def _gen(device, seed: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def bf16_normal(rows: int, cols: int, g: torch.Generator, device) -> torch.Tensor:
+    """N(0,1) rounded to bf16 (round to nearest even), shape [rows][cols]."""
+    x = torch.randn(rows, cols, generator=g, device=device, dtype=torch.float32)
+    return x.to(torch.bfloat16)
+
+
+def fp8_operand(rows: int, K: int, gran_mn: int, g: torch.Generator, device,
+                exp_lo: int = -8, exp_hi: int = 4):
+    """e4m3 codes uint8 [rows][K] and UE8M0 bytes uint8 [ceil(rows/gran_mn)][K/128]."""
+    if K % 128:
+        raise ValueError("K must be a multiple of 128")
+    srows = (rows + gran_mn - 1) // gran_mn
+    kb = K // 128
+    e = torch.randint(exp_lo, exp_hi + 1, (srows, kb), generator=g, device=device,
+                      dtype=torch.int32)
+    x = torch.randn(rows, K, generator=g, device=device, dtype=torch.float32)
+    inv = torch.exp2(-e.to(torch.float32))                        # exact powers of two
+    inv = inv.repeat_interleave(gran_mn, dim=0)[:rows].repeat_interleave(128, dim=1)
+    q = (x * inv).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    sf = (e + 127).to(torch.uint8)
+    return q, sf
+
+
+def e2m1_encode(v: torch.Tensor) -> torch.Tensor:
+    """Round fp32 values onto the e2m1 grid (nearest, ties to the even code,
+    saturating at +-6) and return 4-bit codes (uint8, 0..15)."""
+    a = v.abs()
+    code = torch.zeros_like(a, dtype=torch.uint8)
+    for t in _E2M1_UP_STRICT:
+        code += (a > t).to(torch.uint8)
+    for t in _E2M1_UP_INCL:
+        code += (a >= t).to(torch.uint8)
+    sign = (torch.signbit(v)).to(torch.uint8) << 3
+    return code | sign
+
+
+def fp4_operand(rows: int, K: int, g: torch.Generator, device):
+    """e2m1 values packed two per byte (even k in the low nibble) uint8
+    [rows][K/2] and UE8M0 bytes uint8 [rows][K/32]."""
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    x = torch.randn(rows, K, generator=g, device=device, dtype=torch.float32)
+    blocks = x.view(rows, K // 32, 32)
+    amax = blocks.abs().amax(dim=2)
+    e = torch.floor(torch.log2(amax)).to(torch.int32) - 2
+    e = torch.where(amax > 0, e, torch.zeros_like(e)).clamp_(-127, 127)
+    v = blocks * torch.exp2(-e.to(torch.float32)).unsqueeze(2)
+    codes = e2m1_encode(v).view(rows, K)
+    packed = codes[:, 0::2] | (codes[:, 1::2] << 4)
+    sf = (e + 127).to(torch.uint8)
+    return packed.contiguous(), sf
+
+
+def moe_counts(g: torch.Generator, device, tokens: int = 16384, topk: int = 6,
+               experts: int = 256, zipf: float = 1.1):
+    """Per-expert routed row counts (int64 [experts])."""
+    ranks = torch.arange(1, experts + 1, dtype=torch.float64)
+    p = ranks.pow(-zipf)
+    p = (p / p.sum()).to(torch.float32).to(device)
+    draws = torch.multinomial(p, tokens * topk, replacement=True, generator=g)
+    by_rank = torch.bincount(draws, minlength=experts).to(torch.int64)
+    perm = torch.randperm(experts, generator=g, device=device)
+    counts = torch.empty_like(by_rank)
+    counts[perm] = by_rank
+    return counts
+
+
+def pad_offsets(counts: torch.Tensor, align: int = 128) -> torch.Tensor:
+    """int32 [G+1] start rows of every expert after padding each count up to
+    a multiple of ``align``."""
+    padded = (counts + align - 1) // align * align
+    off = torch.zeros(counts.numel() + 1, dtype=torch.int64, device=counts.device)
+    off[1:] = torch.cumsum(padded, 0)
+    return off.to(torch.int32)
+
+
+@dataclass
+class Workload:
+    name: str
+    kind: str                # 'bf16' | 'fp8' | 'fp4' | 'grouped_fp8'
+    M: int
+    N: int
+    K: int
+    tensors: dict = field(default_factory=dict)
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def flops(self) -> float:
+        """Algorithmic flops, 2*M*N*K (useful rows only for the grouped case)."""
+        if self.kind == "grouped_fp8":
+            return 2.0 * float(self.meta["useful_rows"]) * self.N * self.K
+        return 2.0 * self.M * self.N * self.K
+
+
+SHAPES = {
+    "bf16_small": ("bf16", 256, 256, 512, 1001),
+    "fp8_mid": ("fp8", 1024, 2048, 4096, 1002),
+    "bf16_large": ("bf16", 4096, 7168, 16384, 1003),
+    "moe_fp8": ("grouped_fp8", None, 2048, 7168, 1004),
+    "fp4_large": ("fp4", 4096, 7168, 16384, 1005),
+    "fp8_large": ("fp8", 4096, 7168, 16384, 1006),
+}
+
+
+def dense(kind: str, M: int, N: int, K: int, seed: int, device="cpu", name: str = "custom"):
+    g = _gen(device, seed)
+    w = Workload(name, kind, M, N, K)
+    if kind == "bf16":
+        w.tensors["A"] = bf16_normal(M, K, g, device)
+        w.tensors["B"] = bf16_normal(N, K, g, device)
+    elif kind == "fp8":
+        w.tensors["A"], w.tensors["sfa"] = fp8_operand(M, K, 1, g, device)
+        w.tensors["B"], w.tensors["sfb"] = fp8_operand(N, K, 128, g, device)
+    elif kind == "fp4":
+        w.tensors["A"], w.tensors["sfa"] = fp4_operand(M, K, g, device)
+        w.tensors["B"], w.tensors["sfb"] = fp4_operand(N, K, g, device)
+        w.meta["fp4_scale_rule"] = "ocp_mx: floor(log2(amax32)) - 2"
+    else:
+        raise ValueError(kind)
+    w.meta["seed"] = seed
+    return w
+
+
+def grouped(G: int, N: int, K: int, seed: int, device="cpu", counts=None, name="custom",
+            align: int = 128, tokens: int = 16384, topk: int = 6, zipf: float = 1.1):
+    """M-grouped FP8 inputs.  ``counts`` (int sequence, length G) overrides the
+    Zipf routing draw; counts are padded to multiples of ``align``."""
+    g = _gen(device, seed)
+    if counts is None:
+        counts = moe_counts(g, device, tokens=tokens, topk=topk, experts=G, zipf=zipf)
+    else:
+        counts = torch.as_tensor(list(counts), dtype=torch.int64, device=device)
+    off = pad_offsets(counts, align)
+    m_total = int(off[-1].item())
+    A, sfa = fp8_operand(max(m_total, 1), K, 1, g, device)
+    A = A[:m_total]
+    sfa = sfa[:m_total]
+    # zero the padding rows of every expert (codes 0, scale byte 127)
+    valid = torch.zeros(m_total, dtype=torch.bool, device=device)
+    starts = off[:-1].to(torch.int64)
+    for e in range(G):
+        s = int(starts[e])
+        c = int(counts[e])
+        if c:
+            valid[s:s + c] = True
+    A[~valid] = 0
+    sfa[~valid] = 127
+    Bs, sfbs = [], []
+    for _ in range(G):
+        b, sb = fp8_operand(N, K, 128, g, device)
+        Bs.append(b)
+        sfbs.append(sb)
+    w = Workload(name, "grouped_fp8", m_total, N, K)
+    w.tensors.update(A=A.contiguous(), sfa=sfa.contiguous(), B=torch.stack(Bs),
+                     sfb=torch.stack(sfbs), offsets=off, counts=counts)
+    w.meta.update(seed=seed, G=G, useful_rows=int(counts.sum().item()), m_total=m_total,
+                  routing=f"multinomial({tokens}x{topk}), zipf {zipf}, pad {align}")
+    return w
+
+
+def make(name: str, device="cpu", seed: int | None = None) -> Workload:
+    """One of the named workloads in ``SHAPES``."""
+    kind, M, N, K, default_seed = SHAPES[name]
+    seed = default_seed if seed is None else seed
+    if kind == "grouped_fp8":
+        w = grouped(256, N, K, seed, device=device, name=name)
+    else:
+        w = dense(kind, M, N, K, seed, device=device, name=name)
+    w.name = name
+    return w
+
+
+def ceil_div(a: int, b: int) -> int:
+    return -(-a // b)

@@ -1,0 +1,512 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test ties one part of the oracle to a library conversion, a printed fixture,
+a closed form, an invariant or an exact-rational brute force, so that a plausible
+mistake (a dropped term, a wrong sign, a swapped byte or index, a transposed
+operand) fails at least one of them.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import exact
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------------------
+# element formats
+# ---------------------------------------------------------------------------
+
+def test_e4m3_table_matches_torch(orc):
+    tab = orc.e4m3_table()
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(tab), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(tab[ok], ref[ok])
+    assert np.array_equal(np.signbit(tab[ok]), np.signbit(ref[ok]))
+    assert tab[0x38] == 1.0 and tab[0x7E] == 448.0 and tab[0x01] == 2.0 ** -9
+
+
+def test_ue8m0_table_matches_torch(orc):
+    tab = orc.ue8m0_table()
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    assert np.isnan(tab[255]) and np.isnan(ref[255])
+    assert np.array_equal(tab[:255], ref[:255])
+    assert tab[127] == 1.0 and tab[0] == 2.0 ** -127
+
+
+def test_bf16_decode_matches_torch(orc):
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    tab = orc.bf16_to_f64(codes)
+    ref = torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(tab), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(tab[ok], ref[ok])
+    assert np.array_equal(np.signbit(tab[ok]), np.signbit(ref[ok]))
+
+
+def test_e2m1_table_matches_printed_grid(orc):
+    tab = orc.e2m1_table()
+    grid = exact.e2m1_grid()
+    assert list(tab) == grid
+    assert np.array_equal(np.signbit(tab), np.signbit(np.array(grid)))
+
+
+def test_bf16_rne_matches_exact_rounding(orc):
+    r = _rng(1)
+    xs = list(r.standard_normal(400) * np.exp2(r.integers(-140, 130, 400)))
+    # ties and near-ties around a few binades, subnormals, overflow, zero
+    for e in (-133, -127, -126, -1, 0, 5, 127):
+        q = 2.0 ** (e - 7)
+        base = 2.0 ** e
+        for m in range(0, 6):
+            xs.append(base + (m + 0.5) * q)          # exact tie
+            xs.append(base + (m + 0.5) * q * (1 + 2 ** -40))
+            xs.append(-(base + (m + 0.5) * q))
+    xs += [0.0, -0.0, 2.0 ** 128, (2 - 2 ** -8) * 2.0 ** 127, (2 - 2 ** -9) * 2.0 ** 127,
+           2.0 ** -134, 2.0 ** -133, 3 * 2.0 ** -135, 1e-300]
+    got = orc.bf16_rne(np.array(xs))
+    for x, g in zip(xs, got):
+        want = exact.bf16_round_exact(Fraction(x))
+        assert g == exact.bf16_bits(want) or (want == 0 and (g & 0x7FFF) == 0), (x, hex(g))
+
+
+def test_bf16_rne_matches_torch_on_fp32_values(orc):
+    # torch's fp32 -> bf16 cast rounds to nearest even; on values that are exact
+    # in fp32 the oracle's single rounding from fp64 must agree with it.
+    x = torch.randn(20000, dtype=torch.float32) * torch.exp2(torch.randint(-30, 30, (20000,)).float())
+    ref = x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = orc.bf16_rne(x.to(torch.float64).numpy())
+    assert np.array_equal(got, ref)
+
+
+# ---------------------------------------------------------------------------
+# packed scales
+# ---------------------------------------------------------------------------
+
+def _read_pack_fixture():
+    blocks = []
+    with open(os.path.join(HERE, "golden", "pack_example.txt")) as f:
+        lines = [l.strip() for l in f if l.strip() and not l.startswith("#")]
+    i = 0
+    while i < len(lines):
+        tag, a, b = lines[i].split()
+        a, b = int(a), int(b)
+        rows = [[int(t, 16) for t in lines[i + 1 + j].split()] for j in range(a)]
+        blocks.append((tag, np.array(rows)))
+        i += 1 + a
+    return blocks
+
+
+def test_pack_worked_example(orc):
+    blocks = _read_pack_fixture()
+    assert len(blocks) == 4
+    for (t1, sf), (t2, packed) in zip(blocks[0::2], blocks[1::2]):
+        assert t1 == "sf" and t2 == "packed"
+        sf = sf.astype(np.uint8)
+        want = packed.astype(np.uint16).view(np.int16)
+        got = orc.pack_scales(sf)
+        assert np.array_equal(got, want)
+        assert np.array_equal(orc.unpack_scales(got, *sf.shape), sf)
+    # the signed view of the first example, as the int16 values themselves
+    assert orc.pack_scales(np.array([[0x77, 0x83], [0x7F, 0x80]], np.uint8))[0].tolist() == \
+        [-31881, -32641]
+
+
+@pytest.mark.parametrize("mn,kb,ldp", [(1, 1, 1), (1, 7, 4), (5, 2, 5), (13, 9, 16), (64, 32, 64),
+                                       (3, 31, 8)])
+def test_pack_unpack_round_trip(orc, mn, kb, ldp):
+    r = _rng(mn * 100 + kb)
+    sf = r.integers(0, 256, (mn, kb), dtype=np.uint8)
+    p = orc.pack_scales(sf, ld_packed=max(ldp, mn))
+    assert p.shape == ((kb + 1) // 2, max(ldp, mn))
+    assert np.array_equal(orc.unpack_scales(p, mn, kb), sf)
+    # byte-level definition: little-endian view of K-ordered pairs, MN-major
+    for kp in range(p.shape[0]):
+        for m in range(mn):
+            w = int(p[kp, m]) & 0xFFFF
+            assert w & 0xFF == sf[m, 2 * kp]
+            assert (w >> 8) == (sf[m, 2 * kp + 1] if 2 * kp + 1 < kb else 0x7F)
+            assert orc.scale_byte(p, m, 2 * kp) == sf[m, 2 * kp]
+    # every byte value survives the round trip (bytes >= 0x80 make negative int16)
+    sf_all = np.arange(256, dtype=np.uint8).reshape(2, 128)
+    assert np.array_equal(orc.unpack_scales(orc.pack_scales(sf_all), 2, 128), sf_all)
+
+
+def test_pack_of_unpack_is_identity_on_canonical(orc):
+    r = _rng(7)
+    words = r.integers(-32768, 32768, (6, 11)).astype(np.int16)
+    assert np.array_equal(orc.pack_scales(orc.unpack_scales(words, 11, 12)), words)
+
+
+# ---------------------------------------------------------------------------
+# helpers to build operands
+# ---------------------------------------------------------------------------
+
+def _bf16(x):
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).view(
+        torch.int16).numpy().view(np.uint16)
+
+
+def _e4m3(x):
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.float8_e4m3fn).view(
+        torch.uint8).numpy()
+
+
+def _e2m1_pack(codes):
+    codes = np.asarray(codes, dtype=np.uint8)
+    return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+
+
+def _rand_e4m3(r, rows, K):
+    c = r.integers(0, 256, (rows, K), dtype=np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x38       # no NaN codes
+    return c
+
+
+# ---------------------------------------------------------------------------
+# identity and diagonal
+# ---------------------------------------------------------------------------
+
+def test_identity_bf16(orc):
+    K = 48
+    r = _rng(2)
+    B = _bf16(r.standard_normal((20, K)))
+    A = _bf16(np.eye(K))
+    D = orc.gemm_bf16(A, B)
+    assert np.array_equal(orc.bf16_rne(D), B.T)
+    D2 = orc.gemm_bf16(B, A)                     # B = I on the right gives D = A
+    assert np.array_equal(orc.bf16_rne(D2), B)
+
+
+def test_identity_fp8_is_dequant_b(orc):
+    K = 256
+    r = _rng(3)
+    B = _rand_e4m3(r, 130, K)
+    sfb_u8 = r.integers(120, 135, (2, 2), dtype=np.uint8)
+    A = np.zeros((K, K), np.uint8)
+    A[np.arange(K), np.arange(K)] = 0x38
+    sfa_u8 = np.full((K, 2), 127, np.uint8)
+    D = orc.gemm_fp8(A, orc.pack_scales(sfa_u8), B, orc.pack_scales(sfb_u8))
+    want = exact.dequant_e4m3(B, sfb_u8, 128, 128).T
+    assert np.array_equal(D, want)              # exact in fp64
+    # bit-exact after rounding (a sum of zeros is +0, so compare magnitudes of zeros)
+    got, ref = orc.bf16_rne(D), orc.bf16_rne(want)
+    zero = (ref & 0x7FFF) == 0
+    assert np.array_equal(got[~zero], ref[~zero]) and np.all((got[zero] & 0x7FFF) == 0)
+
+
+def test_identity_fp4_is_dequant_b(orc):
+    K = 64
+    r = _rng(4)
+    Bc = r.integers(0, 16, (9, K), dtype=np.uint8)
+    B = _e2m1_pack(Bc)
+    sfb = r.integers(100, 150, (9, 2), dtype=np.uint8)
+    Ac = np.zeros((K, K), np.uint8)
+    Ac[np.arange(K), np.arange(K)] = 0x2            # e2m1 1.0
+    A = _e2m1_pack(Ac)
+    sfa = np.full((K, 2), 127, np.uint8)
+    D = orc.gemm_fp4(A, orc.pack_scales(sfa), B, orc.pack_scales(sfb), K)
+    want = exact.dequant_e2m1(B, sfb, K).T
+    assert np.array_equal(D, want)
+
+
+def test_diagonal_fp8(orc):
+    K = 128
+    r = _rng(5)
+    d = r.choice([0.5, 1.0, -2.0, 3.0, -0.25, 448.0], K)
+    A = np.zeros((K, K), np.uint8)
+    A[np.arange(K), np.arange(K)] = _e4m3(d)
+    sfa = r.integers(125, 130, (K, 1), dtype=np.uint8)
+    B = _rand_e4m3(r, 40, K)
+    sfb = r.integers(125, 130, (1, 1), dtype=np.uint8)
+    D = orc.gemm_fp8(A, orc.pack_scales(sfa), B, orc.pack_scales(sfb))
+    bq = exact.dequant_e4m3(B, sfb, 128, 128)
+    want = (d * np.exp2(sfa[:, 0].astype(np.float64) - 127))[:, None] * bq.T
+    assert np.array_equal(D, want)
+
+
+# ---------------------------------------------------------------------------
+# closed forms
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("K", [512, 4096])
+def test_all_ones_gives_K(orc, K):
+    one = np.full((3, K), 0x3F80, np.uint16)
+    assert np.all(orc.gemm_bf16(one, one[:2]) == K)
+    A8 = np.full((3, K), 0x38, np.uint8)
+    s8 = orc.pack_scales(np.full((3, K // 128), 127, np.uint8))
+    assert np.all(orc.gemm_fp8(A8, s8, A8, s8) == K)
+    A4 = np.full((3, K // 2), 0x22, np.uint8)
+    s4 = orc.pack_scales(np.full((3, K // 32), 127, np.uint8))
+    assert np.all(orc.gemm_fp4(A4, s4, A4, s4, K) == K)
+
+
+def test_alternating_signs_cancel(orc):
+    K = 256
+    r = _rng(6)
+    v = _bf16(r.standard_normal(1)).astype(np.uint32)
+    Brow = np.where(np.arange(K) % 2 == 0, v, v ^ 0x8000).astype(np.uint16)
+    B = np.tile(Brow, (4, 1))
+    A = np.full((5, K), 0x3F80, np.uint16)        # ones
+    assert np.all(orc.gemm_bf16(A, B) == 0.0)
+    # the same with fp8 codes and arbitrary (K-block-uniform) scales
+    code = int(_e4m3([1.5])[0])
+    B8 = np.tile(np.where(np.arange(K) % 2 == 0, code, code | 0x80).astype(np.uint8), (4, 1))
+    A8 = np.full((5, K), 0x38, np.uint8)
+    sfa = orc.pack_scales(r.integers(100, 150, (5, 2), dtype=np.uint8))
+    sfb = orc.pack_scales(r.integers(100, 150, (1, 2), dtype=np.uint8))
+    assert np.all(orc.gemm_fp8(A8, sfa, B8, sfb) == 0.0)
+
+
+def test_scale_only_closed_form_fp8(orc):
+    """q_a = q_b = 1.0: D[i][j] = 128 * sum_kb 2^(ea(i,kb) + eb(j/128,kb)).
+    Pins the scale indexing, MN-major addressing and B's 128-row blocks."""
+    M, N, K = 7, 300, 128 * 5
+    r = _rng(8)
+    ea = r.integers(-8, 5, (M, 5))
+    eb = r.integers(-8, 5, (3, 5))
+    A = np.full((M, K), 0x38, np.uint8)
+    B = np.full((N, K), 0x38, np.uint8)
+    sfa = orc.pack_scales((ea + 127).astype(np.uint8), ld_packed=M + 3)
+    sfb = orc.pack_scales((eb + 127).astype(np.uint8), ld_packed=8)
+    D = orc.gemm_fp8(A, sfa, B, sfb)
+    for i in range(M):
+        for j in range(N):
+            want = sum(128 * 2.0 ** (ea[i, kb] + eb[j // 128, kb]) for kb in range(5))
+            assert D[i, j] == want
+
+
+def test_scale_only_closed_form_fp4(orc):
+    M, N, K = 5, 6, 32 * 7
+    r = _rng(9)
+    ea = r.integers(-10, 10, (M, 7))
+    eb = r.integers(-10, 10, (N, 7))
+    A = np.full((M, K // 2), 0x22, np.uint8)
+    B = np.full((N, K // 2), 0x22, np.uint8)
+    D = orc.gemm_fp4(A, orc.pack_scales((ea + 127).astype(np.uint8)), B,
+                     orc.pack_scales((eb + 127).astype(np.uint8)), K)
+    for i in range(M):
+        for j in range(N):
+            assert D[i, j] == sum(32 * 2.0 ** (ea[i, kb] + eb[j, kb]) for kb in range(7))
+
+
+def test_fp4_nibble_order(orc):
+    # A picks element k=1 (the high nibble of byte 0) only; B's byte 0 holds 3.0
+    # in the low nibble and 0.5 in the high nibble -> D = 0.5.
+    K = 32
+    A = np.zeros((1, K // 2), np.uint8)
+    A[0, 0] = 0x20                                # k=0: 0, k=1: 1.0
+    B = np.zeros((1, K // 2), np.uint8)
+    B[0, 0] = 0x15                                # k=0: 3.0 (code 5), k=1: 0.5 (code 1)
+    s = orc.pack_scales(np.full((1, 1), 127, np.uint8))
+    assert orc.gemm_fp4(A, s, B, s, K)[0, 0] == 0.5
+
+
+# ---------------------------------------------------------------------------
+# exact-rational brute force
+# ---------------------------------------------------------------------------
+
+def _compare_exact(orc, D, exact_D):
+    for i, row in enumerate(exact_D):
+        for j, x in enumerate(row):
+            assert abs(Fraction(D[i, j]) - x) <= abs(x) * Fraction(1, 2 ** 40) + Fraction(1, 2 ** 1000)
+            assert orc.bf16_rne(np.array([D[i, j]]))[0] == exact.bf16_bits(exact.bf16_round_exact(x))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_brute_force_bf16(orc, seed):
+    r = _rng(10 + seed)
+    M, N, K = 5, 7, 40
+    A = _bf16(r.standard_normal((M, K)) * 3)
+    B = _bf16(r.standard_normal((N, K)))
+    D = orc.gemm_bf16(A, B)
+    _compare_exact(orc, D, exact.exact_nt(exact.dequant_bf16(A), exact.dequant_bf16(B)))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_brute_force_fp8(orc, seed):
+    r = _rng(20 + seed)
+    M, N, K = 6, 133, 256
+    A = _rand_e4m3(r, M, K)
+    B = _rand_e4m3(r, N, K)
+    sfa = r.integers(110, 140, (M, 2), dtype=np.uint8)
+    sfb = r.integers(110, 140, (2, 2), dtype=np.uint8)
+    cols = np.array([0, 1, 127, 128, 129, 132])
+    D = orc.gemm_fp8(A, orc.pack_scales(sfa), B, orc.pack_scales(sfb), cols=cols)
+    ex = exact.exact_nt(exact.dequant_e4m3(A, sfa, 1, 128),
+                        exact.dequant_e4m3(B, sfb, 128, 128)[cols])
+    _compare_exact(orc, D, ex)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_brute_force_fp4(orc, seed):
+    r = _rng(30 + seed)
+    M, N, K = 4, 5, 96
+    A = r.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    B = r.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    sfa = r.integers(115, 140, (M, 3), dtype=np.uint8)
+    sfb = r.integers(115, 140, (N, 3), dtype=np.uint8)
+    D = orc.gemm_fp4(A, orc.pack_scales(sfa), B, orc.pack_scales(sfb), K)
+    _compare_exact(orc, D, exact.exact_nt(exact.dequant_e2m1(A, sfa, K),
+                                          exact.dequant_e2m1(B, sfb, K)))
+
+
+def test_library_dgemm_special_case(orc):
+    """Decoded by torch, multiplied by numpy's fp64 matmul: agrees to 1e-12."""
+    r = _rng(40)
+    M, N, K = 64, 160, 1024
+    A = _rand_e4m3(r, M, K)
+    B = _rand_e4m3(r, N, K)
+    sfa = r.integers(119, 132, (M, 8), dtype=np.uint8)
+    sfb = r.integers(119, 132, (2, 8), dtype=np.uint8)
+    D = orc.gemm_fp8(A, orc.pack_scales(sfa), B, orc.pack_scales(sfb))
+    a = exact.dequant_e4m3(A, sfa, 1, 128)
+    b = exact.dequant_e4m3(B, sfb, 128, 128)
+    ref = a @ b.T
+    nrm = np.linalg.norm(a, axis=1)[:, None] * np.linalg.norm(b, axis=1)[None, :]
+    assert np.max(np.abs(D - ref) / nrm) < 1e-12
+    na = orc.row_norms("e4m3", A, orc.pack_scales(sfa))
+    nb = orc.row_norms("e4m3", B, orc.pack_scales(sfb), gran_mn=128)
+    assert np.allclose(na, np.linalg.norm(a, axis=1), rtol=1e-13)
+    assert np.allclose(nb, np.linalg.norm(b, axis=1), rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# invariants
+# ---------------------------------------------------------------------------
+
+def test_row_permutation_and_selection(orc):
+    r = _rng(50)
+    A = _bf16(r.standard_normal((12, 64)))
+    B = _bf16(r.standard_normal((9, 64)))
+    D = orc.gemm_bf16(A, B)
+    p = r.permutation(12)
+    assert np.array_equal(orc.gemm_bf16(A[p], B), D[p])
+    rows, cols = np.array([3, 0, 11]), np.array([8, 2])
+    assert np.array_equal(orc.gemm_bf16(A, B, rows=rows, cols=cols), D[np.ix_(rows, cols)])
+
+
+def test_transpose_symmetry(orc):
+    r = _rng(51)
+    A = _bf16(r.standard_normal((10, 96)))
+    B = _bf16(r.standard_normal((7, 96)))
+    assert np.array_equal(orc.gemm_bf16(A, B).T, orc.gemm_bf16(B, A))
+    A4 = r.integers(0, 256, (6, 48), dtype=np.uint8)
+    B4 = r.integers(0, 256, (5, 48), dtype=np.uint8)
+    sa = orc.pack_scales(r.integers(120, 135, (6, 3), dtype=np.uint8))
+    sb = orc.pack_scales(r.integers(120, 135, (5, 3), dtype=np.uint8))
+    assert np.array_equal(orc.gemm_fp4(A4, sa, B4, sb, 96).T, orc.gemm_fp4(B4, sb, A4, sa, 96))
+
+
+def test_kblock_permutation_invariance(orc):
+    r = _rng(52)
+    M, N, K = 5, 140, 512
+    A = _rand_e4m3(r, M, K)
+    B = _rand_e4m3(r, N, K)
+    # small integer-valued codes keep every partial sum exact, so any order agrees
+    A = _e4m3(r.integers(-3, 4, (M, K)).astype(np.float32))
+    B = _e4m3(r.integers(-3, 4, (N, K)).astype(np.float32))
+    sfa = r.integers(124, 131, (M, 4), dtype=np.uint8)
+    sfb = r.integers(124, 131, (2, 4), dtype=np.uint8)
+    D = orc.gemm_fp8(A, orc.pack_scales(sfa), B, orc.pack_scales(sfb))
+    perm = np.array([2, 0, 3, 1])
+    kperm = (perm[:, None] * 128 + np.arange(128)[None, :]).ravel()
+    D2 = orc.gemm_fp8(A[:, kperm], orc.pack_scales(sfa[:, perm]), B[:, kperm],
+                      orc.pack_scales(sfb[:, perm]))
+    assert np.array_equal(D, D2)
+
+
+def test_scale_byte_plus_one_doubles(orc):
+    r = _rng(53)
+    M, N, K = 4, 200, 384
+    A = _rand_e4m3(r, M, K)
+    B = _rand_e4m3(r, N, K)
+    sfa = r.integers(120, 130, (M, 3), dtype=np.uint8)
+    sfb = r.integers(120, 130, (2, 3), dtype=np.uint8)
+    D = orc.gemm_fp8(A, orc.pack_scales(sfa), B, orc.pack_scales(sfb))
+    D2 = orc.gemm_fp8(A, orc.pack_scales(sfa + 1), B, orc.pack_scales(sfb))
+    assert np.array_equal(D2, 2 * D)
+    # raising only row i's scale doubles only row i
+    s3 = sfa.copy()
+    s3[2] += 1
+    D3 = orc.gemm_fp8(A, orc.pack_scales(s3), B, orc.pack_scales(sfb))
+    assert np.array_equal(D3[2], 2 * D[2]) and np.array_equal(D3[[0, 1, 3]], D[[0, 1, 3]])
+    # raising B's second 128-row block doubles only columns 128..199
+    s4 = sfb.copy()
+    s4[1] += 1
+    D4 = orc.gemm_fp8(A, orc.pack_scales(sfa), B, orc.pack_scales(s4))
+    assert np.array_equal(D4[:, 128:], 2 * D[:, 128:]) and np.array_equal(D4[:, :128], D[:, :128])
+
+
+def test_linear_in_a_bf16(orc):
+    r = _rng(54)
+    A = _bf16(r.standard_normal((6, 64)))
+    B = _bf16(r.standard_normal((5, 64)))
+    A2 = _bf16(exact.dequant_bf16(A) * -2.0)
+    assert np.array_equal(orc.gemm_bf16(A2, B), -2.0 * orc.gemm_bf16(A, B))
+
+
+# ---------------------------------------------------------------------------
+# grouped
+# ---------------------------------------------------------------------------
+
+def _grouped_case(orc, r, counts, N=136, K=256):
+    off = np.zeros(len(counts) + 1, np.int32)
+    off[1:] = np.cumsum(counts)
+    G = len(counts)
+    Mt = int(off[-1]) + 128                       # extra rows beyond off[G]
+    A = _rand_e4m3(r, Mt, K)
+    sfa = r.integers(120, 134, (Mt, K // 128), dtype=np.uint8)
+    B = np.stack([_rand_e4m3(r, N, K) for _ in range(G)])
+    sfb_u8 = r.integers(120, 134, (G, (N + 127) // 128, K // 128), dtype=np.uint8)
+    sfb = np.stack([orc.pack_scales(s) for s in sfb_u8])
+    return A, sfa, B, sfb_u8, sfb, off
+
+
+def test_grouped_is_dense_per_group(orc):
+    r = _rng(60)
+    counts = [128, 0, 256, 128, 0]
+    A, sfa, B, sfb_u8, sfb, off = _grouped_case(orc, r, counts)
+    sfa_p = orc.pack_scales(sfa)
+    rows = np.arange(A.shape[0])
+    D = orc.grouped_fp8(A, sfa_p, B, sfb, off, rows=rows)
+    for g in range(len(counts)):
+        lo, hi = off[g], off[g + 1]
+        if hi > lo:
+            Dg = orc.gemm_fp8(A[lo:hi], orc.pack_scales(sfa[lo:hi]), B[g], sfb[g])
+            assert np.array_equal(D[lo:hi], Dg)
+    assert np.all(np.isnan(D[off[-1]:]))
+
+
+def test_grouped_single_group_equals_dense(orc):
+    r = _rng(61)
+    A, sfa, B, sfb_u8, sfb, off = _grouped_case(orc, r, [384])
+    sfa_p = orc.pack_scales(sfa)
+    D = orc.grouped_fp8(A, sfa_p, B, sfb, off, rows=np.arange(384))
+    assert np.array_equal(D, orc.gemm_fp8(A[:384], orc.pack_scales(sfa[:384]), B[0], sfb[0]))
+
+
+def test_grouped_expert_selection_scale_only(orc):
+    """Each expert gets a distinct B scale; with unit codes D = K * 2^(ea+eb_g)."""
+    K, N = 128, 8
+    counts = [128, 0, 128, 128]
+    G = len(counts)
+    off = np.array([0, 128, 128, 256, 384], np.int32)
+    A = np.full((384, K), 0x38, np.uint8)
+    sfa = np.full((384, 1), 127, np.uint8)
+    B = np.full((G, N, K), 0x38, np.uint8)
+    sfb = np.stack([orc.pack_scales(np.full((1, 1), 127 + g, np.uint8)) for g in range(G)])
+    D = orc.grouped_fp8(A, orc.pack_scales(sfa), B, sfb, off)
+    assert np.all(D[:128] == 128.0 * 1)
+    assert np.all(D[128:256] == 128.0 * 4)      # expert 2
+    assert np.all(D[256:384] == 128.0 * 8)      # expert 3
