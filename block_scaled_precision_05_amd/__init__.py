@@ -1,0 +1,256 @@
+"""Python binding of the block-scaled GEMM library for MI355X (gfx950).
+
+Every function here only marshals torch tensors (device memory and streams) into
+the C ABI declared in ``include/bsg.h`` and raises on a non-zero status; every
+step of the computation runs in the library's HIP kernels.  There is no fallback:
+if ``libbsg.so`` is missing or cannot be loaded, every call raises.
+
+    D = gemm_bf16(A, B)                         # bf16 [M,K] x bf16 [N,K] -> bf16 [M,N]
+    D = gemm_fp8_blockscaled(A, sfa, B, sfb)    # e4m3 with UE8M0 1x128 / 128x128 scales
+    D = gemm_fp4_blockscaled(A, sfa, B, sfb)    # e2m1 (2 per byte) with UE8M0 1x32 scales
+    D = m_grouped_gemm_fp8(A, sfa, B, sfb, offsets)
+    P = pack_ue8m0_scales(sf)                   # uint8 [mn, kb] -> int16 [ceil(kb/2), mn]
+    sf = unpack_ue8m0_scales(P, mn, kb)
+    P = ensure_packed(sf, mn, kb)               # reuse if already packed, else pack
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbsg.so")
+
+BSG_OK = 0
+BSG_ERR_INVALID_ARG = 1
+BSG_ERR_UNSUPPORTED_SHAPE = 2
+BSG_ERR_MISALIGNED = 3
+BSG_ERR_HIP = 4
+
+_lock = threading.Lock()
+_lib = None
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+
+EXPORTS = {
+    "gemm_bf16": [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp],
+    "gemm_fp8_blockscaled": [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                             _i64, _i64, _i64, _vp],
+    "gemm_fp4_blockscaled": [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                             _i64, _i64, _i64, _vp],
+    "m_grouped_gemm_fp8": [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64,
+                           _vp, _i32, _i64, _i64, _i64, _vp],
+    "pack_ue8m0_scales": [_vp, _i64, _i64, _i64, _vp, _i64, _vp],
+    "unpack_ue8m0_scales": [_vp, _i64, _i64, _i64, _vp, _i64, _vp],
+}
+
+
+class BsgError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libbsg.so; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it with "
+                    "`python -m block_scaled_precision_05_amd.build` (hipcc, gfx950)")
+            l = ctypes.CDLL(LIB_PATH)
+            for name, argtypes in EXPORTS.items():
+                f = getattr(l, name)
+                f.argtypes = argtypes
+                f.restype = ctypes.c_int
+            l.bsg_status_string.argtypes = [ctypes.c_int]
+            l.bsg_status_string.restype = ctypes.c_char_p
+            _lib = l
+        return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().bsg_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int):
+    if status != BSG_OK:
+        raise BsgError(fn, status)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: torch.Tensor | None) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _mat(t: torch.Tensor, name: str) -> int:
+    """Leading dimension of a 2-D tensor whose rows are contiguous."""
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit stride along its last dimension")
+    return t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must live on the GPU")
+
+
+def _bytes_u8(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.uint8) if t.dtype != torch.uint8 else t
+
+
+def _out(out, M, N, device):
+    if out is None:
+        return torch.empty((M, N), dtype=torch.bfloat16, device=device)
+    if out.dtype != torch.bfloat16 or out.shape[0] < M or out.shape[1] < N:
+        raise ValueError("out must be a bfloat16 tensor of at least [M, N]")
+    return out
+
+
+def gemm_bf16(A: torch.Tensor, B: torch.Tensor, out: torch.Tensor | None = None, stream=None):
+    """D[M,N] = A[M,K] @ B[N,K]^T, bf16 in, fp32 accumulate, bf16 out."""
+    _dev(A, B, out)
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise TypeError("A and B must be bfloat16")
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K:
+        raise ValueError("K mismatch")
+    D = _out(out, M, N, A.device)
+    _check("gemm_bf16", lib().gemm_bf16(_ptr(A), _mat(A, "A"), _ptr(B), _mat(B, "B"), _ptr(D),
+                                        _mat(D, "out"), M, N, K, _stream(stream)))
+    return D
+
+
+def _packed(sf: torch.Tensor, name: str) -> int:
+    if sf.dtype != torch.int16:
+        raise TypeError(f"{name} must be packed int16 scales (see ensure_packed)")
+    return _mat(sf, name)
+
+
+def gemm_fp8_blockscaled(A, sfa, B, sfb, out=None, stream=None):
+    """FP8 e4m3 GEMM with UE8M0 scales: sfa packed int16 [ceil(K/256), >=M] (1x128
+    per row of A), sfb packed int16 [ceil(K/256), >=ceil(N/128)] (128x128 blocks
+    of B).  A and B are float8_e4m3fn or uint8 codes."""
+    _dev(A, sfa, B, sfb, out)
+    A, B = _bytes_u8(A), _bytes_u8(B)
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K:
+        raise ValueError("K mismatch")
+    D = _out(out, M, N, A.device)
+    _check("gemm_fp8_blockscaled", lib().gemm_fp8_blockscaled(
+        _ptr(A), _mat(A, "A"), _ptr(sfa), _packed(sfa, "sfa"), _ptr(B), _mat(B, "B"), _ptr(sfb),
+        _packed(sfb, "sfb"), _ptr(D), _mat(D, "out"), M, N, K, _stream(stream)))
+    return D
+
+
+def gemm_fp4_blockscaled(A, sfa, B, sfb, K: int | None = None, out=None, stream=None):
+    """FP4 e2m1 GEMM: A uint8 [M, K/2] and B uint8 [N, K/2] hold two values per
+    byte (even K index in the low nibble); sfa / sfb packed int16 [ceil(K/64), >=M]
+    / [.., >=N] (one UE8M0 byte per row per 32-wide K-block)."""
+    _dev(A, sfa, B, sfb, out)
+    A, B = _bytes_u8(A), _bytes_u8(B)
+    M = A.shape[0]
+    N = B.shape[0]
+    if K is None:
+        K = 2 * A.shape[1]
+    if A.shape[1] * 2 < K or B.shape[1] * 2 < K:
+        raise ValueError("K larger than the operands")
+    D = _out(out, M, N, A.device)
+    _check("gemm_fp4_blockscaled", lib().gemm_fp4_blockscaled(
+        _ptr(A), _mat(A, "A"), _ptr(sfa), _packed(sfa, "sfa"), _ptr(B), _mat(B, "B"), _ptr(sfb),
+        _packed(sfb, "sfb"), _ptr(D), _mat(D, "out"), M, N, K, _stream(stream)))
+    return D
+
+
+def m_grouped_gemm_fp8(A, sfa, B, sfb, offsets, out=None, stream=None):
+    """M-grouped FP8 GEMM.  A e4m3 [M_total, K]; B e4m3 [G, N, K]; sfa packed int16
+    [ceil(K/256), >=M_total]; sfb packed int16 [G, ceil(K/256), >=ceil(N/128)];
+    offsets int32 [G+1] on the GPU (rows [off[g], off[g+1]) use expert g).  Rows
+    outside [off[0], off[G]) of ``out`` are left untouched."""
+    _dev(A, sfa, B, sfb, offsets, out)
+    A, B = _bytes_u8(A), _bytes_u8(B)
+    if B.dim() != 3 or sfb.dim() != 3:
+        raise ValueError("B must be [G, N, K] and sfb [G, kp, ld]")
+    if offsets.dtype != torch.int32 or offsets.dim() != 1 or not offsets.is_contiguous():
+        raise TypeError("offsets must be a contiguous int32 vector")
+    G, N, K = B.shape
+    if offsets.numel() != G + 1:
+        raise ValueError("offsets must have G+1 entries")
+    M = A.shape[0]
+    if A.shape[1] != K:
+        raise ValueError("K mismatch")
+    if B.stride(2) != 1 or sfb.stride(2) != 1 or sfb.dtype != torch.int16:
+        raise ValueError("B and sfb must be contiguous along their last dimension")
+    D = _out(out, M, N, A.device)
+    _check("m_grouped_gemm_fp8", lib().m_grouped_gemm_fp8(
+        _ptr(A), _mat(A, "A"), _ptr(sfa), _packed(sfa, "sfa"), _ptr(B), B.stride(1), B.stride(0),
+        _ptr(sfb), sfb.stride(1), sfb.stride(0), _ptr(D), _mat(D, "out"), _ptr(offsets), G, M, N,
+        K, _stream(stream)))
+    return D
+
+
+def pack_ue8m0_scales(sf: torch.Tensor, ld_packed: int | None = None, out=None, stream=None):
+    """uint8 (or float8_e8m0fnu) [mn, kb] -> packed int16 [ceil(kb/2), ld_packed]."""
+    _dev(sf, out)
+    sf = _bytes_u8(sf)
+    mn, kb = sf.shape
+    ldp = mn if ld_packed is None else int(ld_packed)
+    if out is None:
+        out = torch.empty(((kb + 1) // 2, ldp), dtype=torch.int16, device=sf.device)
+    _check("pack_ue8m0_scales", lib().pack_ue8m0_scales(_ptr(sf), mn, kb, _mat(sf, "sf"),
+                                                        _ptr(out), _mat(out, "out"),
+                                                        _stream(stream)))
+    return out
+
+
+def unpack_ue8m0_scales(packed: torch.Tensor, mn: int, kb: int, out=None, stream=None):
+    """packed int16 [ceil(kb/2), >=mn] -> uint8 [mn, kb]."""
+    _dev(packed, out)
+    if out is None:
+        out = torch.empty((mn, kb), dtype=torch.uint8, device=packed.device)
+    _check("unpack_ue8m0_scales", lib().unpack_ue8m0_scales(_ptr(packed), mn, kb,
+                                                            _packed(packed, "packed"), _ptr(out),
+                                                            _mat(out, "out"), _stream(stream)))
+    return out
+
+
+def is_packed(sf: torch.Tensor, mn: int, kb: int) -> bool:
+    """True if ``sf`` already has the packed layout: int16 [ceil(kb/2), >=mn] with
+    unit stride along MN."""
+    return (sf.dtype == torch.int16 and sf.dim() == 2 and sf.shape[0] == (kb + 1) // 2
+            and sf.shape[1] >= mn and (sf.shape[1] <= 1 or sf.stride(1) == 1))
+
+
+def ensure_packed(sf: torch.Tensor, mn: int, kb: int, stream=None) -> torch.Tensor:
+    """Reuse-or-convert, decided on every call: an already packed tensor is
+    returned as it is; UE8M0 bytes ([mn, kb] uint8 or float8_e8m0fnu) are packed
+    on the GPU.  The pages describe this helper and note the conversion costs
+    time when it is needed ("DeepGEMM-Ascend cobre quantas operacoes no Ascend
+    950?", section "Fatores de escala FP8 e o formato UE8M0 no Ascend")."""
+    if is_packed(sf, mn, kb):
+        return sf
+    if sf.dtype in (torch.uint8, torch.float8_e8m0fnu) and sf.dim() == 2 and \
+            tuple(sf.shape) == (mn, kb):
+        return pack_ue8m0_scales(sf, stream=stream)
+    raise TypeError(
+        f"scales must be packed int16 [{(kb + 1) // 2}, >={mn}] or UE8M0 bytes [{mn}, {kb}]; "
+        f"got {sf.dtype} {tuple(sf.shape)}")

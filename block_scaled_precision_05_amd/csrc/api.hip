@@ -1,0 +1,295 @@
+// api.hip -- C ABI entry points of the block-scaled GEMM library (see include/bsg.h).
+//
+// Every entry point validates its arguments on the host before any HIP call and
+// returns a status code; kernels are launched asynchronously on the caller's
+// stream; nothing is allocated and nothing is synchronised.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/bsg.h"
+#include "gemm_kernel.h"
+
+namespace bsg {
+
+// ---------------------------------------------------------------------------
+// Scale pack / unpack kernels: one thread per packed int16.
+// The pages describe the packed layout (pairs of UE8M0 factors along K in one
+// 16-bit integer, MN-major) and the reuse-or-convert step that produces it
+// ("DeepGEMM-Ascend cobre quantas operacoes no Ascend 950?", section "Fatores de
+// escala FP8 e o formato UE8M0 no Ascend").  Reading adopted: the even K-block
+// is the low byte; an odd K-block count pads the last high byte with 0x7F.
+// Consecutive threads walk the MN index, so the packed stores are coalesced.
+// ---------------------------------------------------------------------------
+__global__ void pack_kernel(const uint8_t* __restrict__ sf, int64_t mn, int64_t kb, int64_t ld_sf,
+                            int16_t* __restrict__ packed, int64_t ld_packed) {
+  const int64_t kp_n = (kb + 1) / 2;
+  const int64_t total = kp_n * mn;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t kp = idx / mn, r = idx - kp * mn;
+    const uint32_t lo = sf[r * ld_sf + 2 * kp];
+    const uint32_t hi = (2 * kp + 1 < kb) ? sf[r * ld_sf + 2 * kp + 1] : 0x7Fu;
+    packed[kp * ld_packed + r] = (int16_t)(uint16_t)(lo | (hi << 8));
+  }
+}
+
+__global__ void unpack_kernel(const int16_t* __restrict__ packed, int64_t mn, int64_t kb,
+                              int64_t ld_packed, uint8_t* __restrict__ sf, int64_t ld_sf) {
+  const int64_t kp_n = (kb + 1) / 2;
+  const int64_t total = kp_n * mn;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t kp = idx / mn, r = idx - kp * mn;
+    const uint32_t w = (uint16_t)packed[kp * ld_packed + r];
+    sf[r * ld_sf + 2 * kp] = (uint8_t)(w & 0xFF);
+    if (2 * kp + 1 < kb) sf[r * ld_sf + 2 * kp + 1] = (uint8_t)((w >> 8) & 0xFF);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Tile configurations.
+// ---------------------------------------------------------------------------
+// Dense: 256x256 workgroup tile, 2x2 waves of 128x128 (16 fragments of 32x32 per
+// wave, 256 fp32 accumulators per lane).  Two 64 KiB LDS stages.
+#define BSG_DENSE_CFG 256, 256, 2, 2
+// Grouped: 128-row tiles so 128-aligned experts waste no rows; 1x4 waves of
+// 128x128 over a 512-wide N tile.  Two 80 KiB LDS stages.
+#define BSG_GROUPED_CFG 128, 512, 1, 4
+
+static int g_num_cus[64];
+
+static int num_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (g_num_cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    g_num_cus[dev] = n;
+  }
+  return g_num_cus[dev];
+}
+
+template <int KIND, int BM, int BN, int WM, int WN, bool GROUPED>
+static int launch(GemmArgs a, hipStream_t stream) {
+  using T = GemmTile<KIND, BM, BN, WM, WN, GROUPED>;
+  a.d_vec = (((uintptr_t)a.D & 7) == 0 && (a.ldd % 4) == 0) ? 1 : 0;
+  a.tiles_m = (a.M + BM - 1) / BM;
+  a.tiles_n = (a.N + BN - 1) / BN;
+  int grid;
+  if (GROUPED) {
+    grid = num_cus();
+  } else {
+    const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
+    grid = (int)(tiles < num_cus() ? tiles : num_cus());
+  }
+  (void)hipGetLastError();
+  hipLaunchKernelGGL((gemm_kernel<KIND, BM, BN, WM, WN, GROUPED>), dim3(grid), dim3(T::NT), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? BSG_OK : BSG_ERR_HIP;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// Byte strides must keep 256 rows of offsets inside 31 bits.
+static const int64_t kMaxRowBytes = (int64_t(1) << 31) / 256 - 1;
+static const int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+// Shared checks of the dense entry points.  elem: bytes per stored element of A/B
+// (2 for bf16, 1 for e4m3, 1/2 for e2m1 expressed as k_bytes = K/2).
+static int check_dense(const void* A, int64_t lda, const void* B, int64_t ldb, const void* D,
+                       int64_t ldd, int64_t M, int64_t N, int64_t K, int64_t kgran, int64_t k_bytes,
+                       int64_t elem_bytes) {
+  if (M < 0 || N < 0 || K < 0) return BSG_ERR_INVALID_ARG;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return BSG_ERR_UNSUPPORTED_SHAPE;
+  if (K % kgran) return BSG_ERR_UNSUPPORTED_SHAPE;
+  if (M == 0 || N == 0) return BSG_OK;
+  if (!D || ldd < N) return BSG_ERR_INVALID_ARG;
+  if ((uintptr_t)D & 1) return BSG_ERR_MISALIGNED;
+  if (ldd > kMaxDim) return BSG_ERR_UNSUPPORTED_SHAPE;
+  if (K == 0) return BSG_OK;  // A and B are not read
+  if (!A || !B) return BSG_ERR_INVALID_ARG;
+  if (lda * elem_bytes < k_bytes || ldb * elem_bytes < k_bytes) return BSG_ERR_INVALID_ARG;
+  if (lda * elem_bytes > kMaxRowBytes || ldb * elem_bytes > kMaxRowBytes)
+    return BSG_ERR_UNSUPPORTED_SHAPE;
+  if (!aligned16(A) || !aligned16(B)) return BSG_ERR_MISALIGNED;
+  if ((lda * elem_bytes) % 16 || (ldb * elem_bytes) % 16) return BSG_ERR_MISALIGNED;
+  return BSG_OK;
+}
+
+}  // namespace bsg
+
+using namespace bsg;
+
+extern "C" {
+
+const char* bsg_status_string(int status) {
+  switch (status) {
+    case BSG_OK: return "BSG_OK";
+    case BSG_ERR_INVALID_ARG: return "BSG_ERR_INVALID_ARG";
+    case BSG_ERR_UNSUPPORTED_SHAPE: return "BSG_ERR_UNSUPPORTED_SHAPE";
+    case BSG_ERR_MISALIGNED: return "BSG_ERR_MISALIGNED";
+    case BSG_ERR_HIP: return "BSG_ERR_HIP";
+    default: return "BSG_ERR_UNKNOWN";
+  }
+}
+
+int gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, void* D, int64_t ldd,
+              int64_t M, int64_t N, int64_t K, void* stream) {
+  int st = check_dense(A, lda, B, ldb, D, ldd, M, N, K, 8, 2 * K, 2);
+  if (st != BSG_OK || M == 0 || N == 0) return st;
+  GemmArgs a = {};
+  a.A = (const uint8_t*)A;
+  a.B = (const uint8_t*)B;
+  a.D = (uint16_t*)D;
+  a.lda = lda * 2;
+  a.ldb = ldb * 2;
+  a.ldd = ldd;
+  a.M = (int32_t)M;
+  a.N = (int32_t)N;
+  a.K = (int32_t)K;
+  a.k_bytes = (int32_t)(2 * K);
+  a.nk = (int32_t)((2 * K + 127) / 128);
+  return launch<KIND_BF16, BSG_DENSE_CFG, false>(a, (hipStream_t)stream);
+}
+
+static int check_scales(const int16_t* sfa, int64_t ld_sfa, int64_t rows_a, const int16_t* sfb,
+                        int64_t ld_sfb, int64_t rows_b, int64_t K) {
+  if (K == 0) return BSG_OK;
+  if (!sfa || !sfb) return BSG_ERR_INVALID_ARG;
+  if (ld_sfa < rows_a || ld_sfb < rows_b) return BSG_ERR_INVALID_ARG;
+  if (((uintptr_t)sfa & 1) || ((uintptr_t)sfb & 1)) return BSG_ERR_MISALIGNED;
+  return BSG_OK;
+}
+
+int gemm_fp8_blockscaled(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
+                         const void* B, int64_t ldb, const int16_t* sfb, int64_t ld_sfb,
+                         void* D, int64_t ldd, int64_t M, int64_t N, int64_t K, void* stream) {
+  int st = check_dense(A, lda, B, ldb, D, ldd, M, N, K, 128, K, 1);
+  if (st != BSG_OK || M == 0 || N == 0) return st;
+  st = check_scales(sfa, ld_sfa, M, sfb, ld_sfb, (N + 127) / 128, K);
+  if (st != BSG_OK) return st;
+  GemmArgs a = {};
+  a.A = (const uint8_t*)A;
+  a.B = (const uint8_t*)B;
+  a.D = (uint16_t*)D;
+  a.sfa = sfa;
+  a.sfb = sfb;
+  a.lda = lda;
+  a.ldb = ldb;
+  a.ldd = ldd;
+  a.ld_sfa = ld_sfa;
+  a.ld_sfb = ld_sfb;
+  a.M = (int32_t)M;
+  a.N = (int32_t)N;
+  a.K = (int32_t)K;
+  a.k_bytes = (int32_t)K;
+  a.nk = (int32_t)(K / 128);
+  a.kp_count = (int32_t)((K / 128 + 1) / 2);
+  a.sfb_rows = (int32_t)((N + 127) / 128);
+  return launch<KIND_FP8, BSG_DENSE_CFG, false>(a, (hipStream_t)stream);
+}
+
+int gemm_fp4_blockscaled(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
+                         const void* B, int64_t ldb, const int16_t* sfb, int64_t ld_sfb,
+                         void* D, int64_t ldd, int64_t M, int64_t N, int64_t K, void* stream) {
+  int st = check_dense(A, lda, B, ldb, D, ldd, M, N, K, 32, K / 2, 1);
+  if (st != BSG_OK || M == 0 || N == 0) return st;
+  st = check_scales(sfa, ld_sfa, M, sfb, ld_sfb, N, K);
+  if (st != BSG_OK) return st;
+  GemmArgs a = {};
+  a.A = (const uint8_t*)A;
+  a.B = (const uint8_t*)B;
+  a.D = (uint16_t*)D;
+  a.sfa = sfa;
+  a.sfb = sfb;
+  a.lda = lda;
+  a.ldb = ldb;
+  a.ldd = ldd;
+  a.ld_sfa = ld_sfa;
+  a.ld_sfb = ld_sfb;
+  a.M = (int32_t)M;
+  a.N = (int32_t)N;
+  a.K = (int32_t)K;
+  a.k_bytes = (int32_t)(K / 2);
+  a.nk = (int32_t)((K / 2 + 127) / 128);
+  a.kp_count = (int32_t)((K / 32 + 1) / 2);
+  a.sfb_rows = (int32_t)N;
+  return launch<KIND_FP4, BSG_DENSE_CFG, false>(a, (hipStream_t)stream);
+}
+
+int m_grouped_gemm_fp8(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
+                       const void* B, int64_t ldb, int64_t stride_b,
+                       const int16_t* sfb, int64_t ld_sfb, int64_t stride_sfb,
+                       void* D, int64_t ldd, const int32_t* group_offsets, int32_t G,
+                       int64_t M_total, int64_t N, int64_t K, void* stream) {
+  if (G < 0 || G > 1024) return G < 0 ? BSG_ERR_INVALID_ARG : BSG_ERR_UNSUPPORTED_SHAPE;
+  int st = check_dense(A, lda, B, ldb, D, ldd, M_total, N, K, 128, K, 1);
+  if (st != BSG_OK || M_total == 0 || N == 0 || G == 0) return st;
+  if (!group_offsets) return BSG_ERR_INVALID_ARG;
+  st = check_scales(sfa, ld_sfa, M_total, sfb, ld_sfb, (N + 127) / 128, K);
+  if (st != BSG_OK) return st;
+  const int64_t kp = (K / 128 + 1) / 2;
+  if (G > 1 && (stride_b < (N - 1) * ldb + K || (K > 0 && stride_sfb < kp * ld_sfb)))
+    return BSG_ERR_INVALID_ARG;
+  if (stride_b < 0 || stride_sfb < 0) return BSG_ERR_INVALID_ARG;
+  if (stride_b % 16) return BSG_ERR_MISALIGNED;
+  GemmArgs a = {};
+  a.A = (const uint8_t*)A;
+  a.B = (const uint8_t*)B;
+  a.D = (uint16_t*)D;
+  a.sfa = sfa;
+  a.sfb = sfb;
+  a.offsets = group_offsets;
+  a.lda = lda;
+  a.ldb = ldb;
+  a.ldd = ldd;
+  a.ld_sfa = ld_sfa;
+  a.ld_sfb = ld_sfb;
+  a.stride_b = stride_b;
+  a.stride_sfb = stride_sfb;
+  a.M = (int32_t)M_total;
+  a.N = (int32_t)N;
+  a.K = (int32_t)K;
+  a.k_bytes = (int32_t)K;
+  a.nk = (int32_t)(K / 128);
+  a.kp_count = (int32_t)kp;
+  a.sfb_rows = (int32_t)((N + 127) / 128);
+  a.G = G;
+  return launch<KIND_FP8, BSG_GROUPED_CFG, true>(a, (hipStream_t)stream);
+}
+
+static int launch_pack(bool unpack, const void* src, int64_t mn, int64_t kb, int64_t ld_src,
+                       void* dst, int64_t ld_dst, void* stream) {
+  const int64_t total = (kb + 1) / 2 * mn;
+  const int threads = 256;
+  int64_t blocks = (total + threads - 1) / threads;
+  if (blocks > 65536) blocks = 65536;
+  (void)hipGetLastError();
+  if (unpack)
+    hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)blocks), dim3(threads), 0, (hipStream_t)stream,
+                       (const int16_t*)src, mn, kb, ld_src, (uint8_t*)dst, ld_dst);
+  else
+    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(threads), 0, (hipStream_t)stream,
+                       (const uint8_t*)src, mn, kb, ld_src, (int16_t*)dst, ld_dst);
+  return hipGetLastError() == hipSuccess ? BSG_OK : BSG_ERR_HIP;
+}
+
+int pack_ue8m0_scales(const uint8_t* sf, int64_t mn, int64_t kb, int64_t ld_sf, int16_t* packed,
+                      int64_t ld_packed, void* stream) {
+  if (mn < 0 || kb < 0) return BSG_ERR_INVALID_ARG;
+  if (mn == 0 || kb == 0) return BSG_OK;
+  if (!sf || !packed || ld_sf < kb || ld_packed < mn) return BSG_ERR_INVALID_ARG;
+  if ((uintptr_t)packed & 1) return BSG_ERR_MISALIGNED;
+  return launch_pack(false, sf, mn, kb, ld_sf, packed, ld_packed, stream);
+}
+
+int unpack_ue8m0_scales(const int16_t* packed, int64_t mn, int64_t kb, int64_t ld_packed,
+                        uint8_t* sf, int64_t ld_sf, void* stream) {
+  if (mn < 0 || kb < 0) return BSG_ERR_INVALID_ARG;
+  if (mn == 0 || kb == 0) return BSG_OK;
+  if (!sf || !packed || ld_sf < kb || ld_packed < mn) return BSG_ERR_INVALID_ARG;
+  if ((uintptr_t)packed & 1) return BSG_ERR_MISALIGNED;
+  return launch_pack(true, packed, mn, kb, ld_packed, sf, ld_sf, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+/*
+ * bsg.h -- C ABI of the block-scaled GEMM library for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes D = A * B^T on one GPU:
+ *   - BF16 x BF16,
+ *   - FP8 e4m3 x e4m3 with UE8M0 block scales,
+ *   - FP4 e2m1 x e2m1 with UE8M0 block scales,
+ *   - an M-grouped FP8 variant for mixture-of-experts layers,
+ * always accumulating in fp32 and writing bf16 (round to nearest even).  It also
+ * packs and unpacks UE8M0 scales into the int16, MN-major layout the scaled GEMMs
+ * read.
+ *
+ * The pages this follows list BF16, FP8 and FP4 dense GEMM plus grouped (MoE)
+ * GEMM as the library's coverage ("DeepGEMM-Ascend cobre quantas operacoes no
+ * Ascend 950?", section "Cobertura de operacoes e a lacuna declarada no
+ * repositorio"; "DeepSeek lanza kernels de DeepGEMM para Huawei Ascend 950",
+ * section "Que incluye el lanzamiento"), and describe the scale layout: UE8M0
+ * scale factors packed in pairs along K into 16-bit integers, stored MN-major,
+ * reused as they are when already in that layout and converted otherwise (first
+ * page, section "Fatores de escala FP8 e o formato UE8M0 no Ascend").  Formulas,
+ * layouts and bit formats are not on the pages; the readings below are this
+ * library's.
+ *
+ * Common conventions
+ *  - Layout (NT): A is [M][K] and B is [N][K], K contiguous; D is [M][N], N
+ *    contiguous.  Leading dimensions (lda, ldb, ldd, ld_sf*) count storage
+ *    elements: bf16 elements for BF16 operands and D, bytes for FP8 and FP4
+ *    operands (an FP4 byte holds two values, the even K index in the low nibble).
+ *  - Formats: FP8 is OCP e4m3fn (bias 7, max 448, no infinities); FP4 is OCP
+ *    e2m1 ({0, .5, 1, 1.5, 2, 3, 4, 6} with sign); a UE8M0 byte b is 2^(b-127).
+ *  - Packed scales: int16 P[ceil(Kb/2)][ld_sf] where Kb is the number of K-blocks;
+ *    element (kp, mn) sits at kp*ld_sf + mn, its low byte is K-block 2kp and its
+ *    high byte K-block 2kp+1 (0x7F when Kb is odd).  "Scale rows" (mn) are the
+ *    rows of A, the 128-row blocks of B (FP8) or the rows of B (FP4).
+ *  - Every pointer is a device pointer owned by the caller; the library allocates nothing, keeps no state between
+ *    calls and never synchronises.  Work is enqueued on `stream` (a hipStream_t;
+ *    NULL is the default stream) and is complete when the stream says so.
+ *  - Every call validates its arguments on the host before touching the GPU and
+ *    returns a status code; nothing is launched when the status is not BSG_OK.
+ *    A launch failure reported by the runtime returns BSG_ERR_HIP.
+ *  - M == 0 or N == 0 is a no-op.  K == 0 writes zeros to D and reads neither
+ *    A, B nor the scales (their pointers may then be NULL).
+ *  - A wrongly laid out scale array cannot be detected: it gives wrong numbers,
+ *    not an error (the pages warn of exactly this failure mode).
+ *  - Sizes: every leading dimension times 256 must stay below 2^31 bytes.
+ */
+#ifndef BSG_H
+#define BSG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum bsg_status {
+  BSG_OK = 0,
+  BSG_ERR_INVALID_ARG = 1,       /* null pointer, negative size, leading dimension too small */
+  BSG_ERR_UNSUPPORTED_SHAPE = 2, /* K not a multiple of the format's K granularity, too large */
+  BSG_ERR_MISALIGNED = 3,        /* base pointer or row stride not 16-byte aligned */
+  BSG_ERR_HIP = 4,               /* the HIP runtime reported an error at launch */
+};
+
+/* Human-readable name of a status code (static storage). */
+const char* bsg_status_string(int status);
+
+/* BF16 GEMM: D[m][n] = bf16( sum_k A[m][k] * B[n][k] ), fp32 accumulation.
+ *   A: bf16 [M][lda], B: bf16 [N][ldb], D: bf16 [M][ldd] (device pointers).
+ *   Requires K % 8 == 0, lda >= K, ldb >= K, ldd >= N; A and B 16-byte aligned,
+ *   lda and ldb multiples of 8; D 2-byte aligned (rows that are 8-byte aligned
+ *   are written with wider stores). */
+int gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, void* D, int64_t ldd,
+              int64_t M, int64_t N, int64_t K, void* stream);
+
+/* FP8 block-scaled GEMM:
+ *   D[m][n] = bf16( sum_k a[m][k] * 2^(sa[m][k/128]-127) * b[n][k] * 2^(sb[n/128][k/128]-127) )
+ *   A: e4m3 [M][lda] bytes; sfa: packed int16 [K/256 rounded up][ld_sfa], scale rows = M
+ *   (one scale per row of A per 128-wide K-block).
+ *   B: e4m3 [N][ldb] bytes; sfb: packed int16 [..][ld_sfb], scale rows = ceil(N/128)
+ *   (one scale per 128x128 block of B).
+ *   D: bf16 [M][ldd].
+ *   Requires K % 128 == 0, ld_sfa >= M, ld_sfb >= ceil(N/128), lda, ldb >= K,
+ *   ldd >= N; A and B 16-byte aligned, lda and ldb multiples of 16; D, sfa and
+ *   sfb 2-byte aligned. */
+int gemm_fp8_blockscaled(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
+                         const void* B, int64_t ldb, const int16_t* sfb, int64_t ld_sfb,
+                         void* D, int64_t ldd, int64_t M, int64_t N, int64_t K, void* stream);
+
+/* FP4 block-scaled GEMM:
+ *   D[m][n] = bf16( sum_k a[m][k] * 2^(sa[m][k/32]-127) * b[n][k] * 2^(sb[n][k/32]-127) )
+ *   A: e2m1 [M][lda] bytes (two values per byte), B: e2m1 [N][ldb] bytes;
+ *   sfa: packed int16 [K/64 rounded up][ld_sfa], scale rows = M;
+ *   sfb: packed int16 [..][ld_sfb], scale rows = N (one scale per row per 32-wide
+ *   K-block on both operands).  D: bf16 [M][ldd].
+ *   Requires K % 32 == 0, lda, ldb >= K/2 (bytes), ld_sfa >= M, ld_sfb >= N,
+ *   ldd >= N; A and B 16-byte aligned, lda and ldb multiples of 16; D, sfa and
+ *   sfb 2-byte aligned. */
+int gemm_fp4_blockscaled(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
+                         const void* B, int64_t ldb, const int16_t* sfb, int64_t ld_sfb,
+                         void* D, int64_t ldd, int64_t M, int64_t N, int64_t K, void* stream);
+
+/* M-grouped FP8 GEMM for mixture-of-experts layers (the pages name M-grouped GEMM
+ * among the released kernels: "aireiter.com -- DeepSeek Ascend infrastructure
+ * components", table "Mapa de componentes").
+ *   Rows [off[g], off[g+1]) of A and D belong to expert g (0 <= g < G) and use
+ *   expert g's weights B_g = B + g*stride_b (e4m3 [N][ldb] bytes) and scales
+ *   sfb_g = sfb + g*stride_sfb (packed int16, scale rows = ceil(N/128)):
+ *     D[m][n] = bf16( sum_k a[m][k] * 2^(sa[m][k/128]-127) * b_g[n][k] * 2^(sb_g[n/128][k/128]-127) )
+ *   A: e4m3 [M_total][lda]; sfa packed, scale rows = M_total; D: bf16 [M_total][ldd].
+ *   group_offsets: DEVICE int32 [G+1].  Precondition (not checked, the offsets
+ *   live on the device): 0 <= off[0] <= off[1] <= ... <= off[G] <= M_total.
+ *   Rows outside [off[0], off[G]) are not written.  Empty groups are allowed.
+ *   Offsets need no alignment; 128-row aligned groups waste no tile rows.
+ *   G == 0 is a no-op.  Requires G <= 1024, K % 128 == 0, stride_b >= (N-1)*ldb + K,
+ *   stride_sfb >= ceil(K/256)*ld_sfb, plus the dense FP8 requirements. */
+int m_grouped_gemm_fp8(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
+                       const void* B, int64_t ldb, int64_t stride_b,
+                       const int16_t* sfb, int64_t ld_sfb, int64_t stride_sfb,
+                       void* D, int64_t ldd, const int32_t* group_offsets, int32_t G,
+                       int64_t M_total, int64_t N, int64_t K, void* stream);
+
+/* Pack UE8M0 scales (device kernel on `stream`):
+ *   sf: uint8 [mn][ld_sf], K-blocks contiguous (kb of them per scale row)
+ *   -> packed: int16 [ceil(kb/2)][ld_packed], MN-major, as described above.
+ *   Requires ld_sf >= kb, ld_packed >= mn; device pointers. */
+int pack_ue8m0_scales(const uint8_t* sf, int64_t mn, int64_t kb, int64_t ld_sf,
+                      int16_t* packed, int64_t ld_packed, void* stream);
+
+/* Inverse of pack_ue8m0_scales (device kernel on `stream`). */
+int unpack_ue8m0_scales(const int16_t* packed, int64_t mn, int64_t kb, int64_t ld_packed,
+                        uint8_t* sf, int64_t ld_sf, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSG_H */

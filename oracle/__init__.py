@@ -63,6 +63,8 @@ def _load():
         lib.orc_ue8m0_to_f64.argtypes = [ctypes.c_uint8]
         lib.orc_f64_to_bf16_rne.restype = ctypes.c_uint16
         lib.orc_f64_to_bf16_rne.argtypes = [ctypes.c_double]
+        lib.orc_f64_to_bf16_rne_array.restype = None
+        lib.orc_f64_to_bf16_rne_array.argtypes = [_vp, _vp, ctypes.c_int64]
         lib.orc_scale_byte.restype = ctypes.c_uint8
         lib.orc_scale_byte.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
         lib.orc_pack_scales.restype = None
@@ -161,14 +163,10 @@ def ue8m0_table() -> np.ndarray:
 
 def bf16_rne(x) -> np.ndarray:
     """fp64 -> bf16 bits (uint16), round to nearest even, one rounding."""
-    lib = _load()
-    x = np.asarray(x, dtype=np.float64)
-    flat = x.ravel()
-    out = np.empty(flat.shape, dtype=np.uint16)
-    f = lib.orc_f64_to_bf16_rne
-    for i, v in enumerate(flat.tolist()):
-        out[i] = f(v)
-    return out.reshape(x.shape)
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().orc_f64_to_bf16_rne_array(_ptr(x), _ptr(out), x.size)
+    return out
 
 
 # ---------------------------------------------------------------------------

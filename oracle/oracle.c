@@ -134,6 +134,12 @@ uint16_t orc_f64_to_bf16_rne(double x) {
   return sign | (uint16_t)(bits >> 16);
 }
 
+/* Array form of orc_f64_to_bf16_rne. */
+void orc_f64_to_bf16_rne_array(const double* x, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i)
+    out[i] = orc_f64_to_bf16_rne(x[i]);
+}
+
 /* ----------------------------------------------------------------------------
  * Packed UE8M0 scales: the oracle's own pack and unpack
  * ------------------------------------------------------------------------- */

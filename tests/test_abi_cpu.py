@@ -1,0 +1,148 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports every
+function include/bsg.h declares, and rejects bad arguments with the documented
+status codes before it touches the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_precision_05_amd as bsg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "bsg.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_api():
+    names = _declared_functions()
+    for n in ("gemm_bf16", "gemm_fp8_blockscaled", "gemm_fp4_blockscaled", "m_grouped_gemm_fp8",
+              "pack_ue8m0_scales", "unpack_ue8m0_scales", "bsg_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = bsg.lib()
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    assert bsg.status_string(0) == "BSG_OK"
+    assert bsg.status_string(1) == "BSG_ERR_INVALID_ARG"
+    assert bsg.status_string(2) == "BSG_ERR_UNSUPPORTED_SHAPE"
+    assert bsg.status_string(3) == "BSG_ERR_MISALIGNED"
+    assert bsg.status_string(4) == "BSG_ERR_HIP"
+    assert bsg.status_string(99) == "BSG_ERR_UNKNOWN"
+
+
+# fake, never-dereferenced device addresses: validation fails before any HIP call
+P = 0x10000
+P2 = 0x20000
+
+
+def test_bf16_validation():
+    L = bsg.lib()
+    assert L.gemm_bf16(P, 64, P, 64, P, 64, -1, 8, 64, None) == bsg.BSG_ERR_INVALID_ARG
+    assert L.gemm_bf16(P, 64, P, 64, P, 64, 8, 8, 60, None) == bsg.BSG_ERR_UNSUPPORTED_SHAPE
+    assert L.gemm_bf16(0, 64, P, 64, P, 64, 8, 8, 64, None) == bsg.BSG_ERR_INVALID_ARG
+    assert L.gemm_bf16(P, 32, P, 64, P, 64, 8, 8, 64, None) == bsg.BSG_ERR_INVALID_ARG   # lda < K
+    assert L.gemm_bf16(P, 64, P, 64, P, 4, 8, 8, 64, None) == bsg.BSG_ERR_INVALID_ARG    # ldd < N
+    assert L.gemm_bf16(P + 2, 64, P, 64, P, 64, 8, 8, 64, None) == bsg.BSG_ERR_MISALIGNED
+    assert L.gemm_bf16(P, 68, P, 64, P, 64, 8, 8, 64, None) == bsg.BSG_ERR_MISALIGNED   # 136 B rows
+    assert L.gemm_bf16(P, 64, P, 64, P + 1, 64, 8, 8, 64, None) == bsg.BSG_ERR_MISALIGNED  # odd D
+    assert L.gemm_bf16(0, 0, 0, 0, 0, 64, 8, 8, 64, None) == bsg.BSG_ERR_INVALID_ARG  # null D
+    # empty problems are no-ops and need no pointers
+    assert L.gemm_bf16(0, 0, 0, 0, 0, 0, 0, 8, 64, None) == bsg.BSG_OK
+    assert L.gemm_bf16(0, 0, 0, 0, 0, 0, 8, 0, 64, None) == bsg.BSG_OK
+
+
+def test_fp8_validation():
+    L = bsg.lib()
+    f = L.gemm_fp8_blockscaled
+    ok_args = [P, 256, P2, 8, P, 256, P2, 2, P, 256, 8, 256, 256, None]
+    a = list(ok_args)
+    a[12] = 200            # K % 128
+    assert f(*a) == bsg.BSG_ERR_UNSUPPORTED_SHAPE
+    a = list(ok_args)
+    a[2] = 0               # null sfa
+    assert f(*a) == bsg.BSG_ERR_INVALID_ARG
+    a = list(ok_args)
+    a[3] = 4               # ld_sfa < M
+    assert f(*a) == bsg.BSG_ERR_INVALID_ARG
+    a = list(ok_args)
+    a[7] = 1               # ld_sfb < ceil(N/128) = 2
+    assert f(*a) == bsg.BSG_ERR_INVALID_ARG
+    a = list(ok_args)
+    a[2] = P2 + 1          # odd scale pointer
+    assert f(*a) == bsg.BSG_ERR_MISALIGNED
+    a = list(ok_args)
+    a[1] = 264             # lda not a multiple of 16 bytes
+    assert f(*a) == bsg.BSG_ERR_MISALIGNED
+    a = list(ok_args)
+    a[1] = 1 << 24         # rows too long for 32-bit tile offsets
+    assert f(*a) == bsg.BSG_ERR_UNSUPPORTED_SHAPE
+
+
+def test_fp4_validation():
+    L = bsg.lib()
+    f = L.gemm_fp4_blockscaled
+    ok_args = [P, 128, P2, 8, P, 128, P2, 256, P, 256, 8, 256, 256, None]
+    a = list(ok_args)
+    a[12] = 48             # K % 32
+    assert f(*a) == bsg.BSG_ERR_UNSUPPORTED_SHAPE
+    a = list(ok_args)
+    a[1] = 64              # lda (bytes) < K/2
+    assert f(*a) == bsg.BSG_ERR_INVALID_ARG
+    a = list(ok_args)
+    a[7] = 255             # ld_sfb < N
+    assert f(*a) == bsg.BSG_ERR_INVALID_ARG
+
+
+def test_grouped_validation():
+    L = bsg.lib()
+    f = L.m_grouped_gemm_fp8
+    ok = [P, 256, P2, 512, P, 256, 256 * 256, P2, 2, 4, P, 256, P2, 4, 512, 256, 256, None]
+    a = list(ok)
+    a[13] = 2000           # G too large
+    assert f(*a) == bsg.BSG_ERR_UNSUPPORTED_SHAPE
+    a = list(ok)
+    a[13] = -1
+    assert f(*a) == bsg.BSG_ERR_INVALID_ARG
+    a = list(ok)
+    a[12] = 0              # null offsets
+    assert f(*a) == bsg.BSG_ERR_INVALID_ARG
+    a = list(ok)
+    a[6] = 1000            # stride_b too small
+    assert f(*a) == bsg.BSG_ERR_INVALID_ARG
+    a = list(ok)
+    a[9] = 1               # stride_sfb too small
+    assert f(*a) == bsg.BSG_ERR_INVALID_ARG
+    a = list(ok)
+    a[16] = 100            # K % 128
+    assert f(*a) == bsg.BSG_ERR_UNSUPPORTED_SHAPE
+    a = list(ok)
+    a[13] = 0              # no experts: no-op
+    assert f(*a) == bsg.BSG_OK
+
+
+def test_pack_validation():
+    L = bsg.lib()
+    assert L.pack_ue8m0_scales(P, -1, 4, 4, P2, 8, None) == bsg.BSG_ERR_INVALID_ARG
+    assert L.pack_ue8m0_scales(P, 8, 4, 3, P2, 8, None) == bsg.BSG_ERR_INVALID_ARG   # ld_sf < kb
+    assert L.pack_ue8m0_scales(P, 8, 4, 4, P2, 7, None) == bsg.BSG_ERR_INVALID_ARG   # ld_packed < mn
+    assert L.pack_ue8m0_scales(P, 8, 4, 4, P2 + 1, 8, None) == bsg.BSG_ERR_MISALIGNED
+    assert L.pack_ue8m0_scales(0, 0, 4, 4, 0, 8, None) == bsg.BSG_OK
+    assert L.unpack_ue8m0_scales(P2, 8, 4, 7, P, 4, None) == bsg.BSG_ERR_INVALID_ARG
+    assert L.unpack_ue8m0_scales(0, 8, 4, 8, P, 4, None) == bsg.BSG_ERR_INVALID_ARG
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    a = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        bsg.gemm_bf16(a, a)

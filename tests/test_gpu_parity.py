@@ -1,0 +1,404 @@
+"""GPU parity: every entry point of the C ABI against the CPU oracle on the same
+seeded bytes.  Small shapes are compared in full; the 4096x7168x16384 and MoE
+workloads are compared on sampled rows and columns (every N tile, every expert
+class) in the launch configuration the benchmark times."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_precision_05_amd as bsg
+from block_scaled_precision_05_amd import workloads
+import oracle
+from parity import assert_parity, gpu_bits, bf16_bits_to_f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def _say(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+
+
+def _u16(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _u8(t):
+    return t.contiguous().view(torch.uint8).cpu().numpy()
+
+
+# ---------------------------------------------------------------------------
+# runners
+# ---------------------------------------------------------------------------
+
+def run_gpu(kind, t, K=None):
+    """t: device tensors with unpacked uint8 scales; packs them on the GPU."""
+    if kind == "bf16":
+        return bsg.gemm_bf16(t["A"], t["B"])
+    M, N = t["A"].shape[0], t["B"].shape[0]
+    if kind == "fp8":
+        K = t["A"].shape[1]
+        sfa = bsg.ensure_packed(t["sfa"], M, K // 128)
+        sfb = bsg.ensure_packed(t["sfb"], (N + 127) // 128, K // 128)
+        return bsg.gemm_fp8_blockscaled(t["A"], sfa, t["B"], sfb)
+    K = K if K is not None else 2 * t["A"].shape[1]
+    sfa = bsg.ensure_packed(t["sfa"], M, K // 32)
+    sfb = bsg.ensure_packed(t["sfb"], N, K // 32)
+    return bsg.gemm_fp4_blockscaled(t["A"], sfa, t["B"], sfb, K=K)
+
+
+def run_oracle(kind, h, K, rows=None, cols=None):
+    """h: host numpy arrays (A, sfa u8, B, sfb u8).  Returns (ref, na, nb)."""
+    if kind == "bf16":
+        A, B = h["A"].view(np.uint16), h["B"].view(np.uint16)
+        ref = oracle.gemm_bf16(A, B, rows=rows, cols=cols)
+        na = oracle.row_norms("bf16", A, rows=rows)
+        nb = oracle.row_norms("bf16", B, rows=cols)
+        return ref, na, nb
+    sfa = oracle.pack_scales(h["sfa"])
+    sfb = oracle.pack_scales(h["sfb"])
+    if kind == "fp8":
+        ref = oracle.gemm_fp8(h["A"], sfa, h["B"], sfb, rows=rows, cols=cols)
+        na = oracle.row_norms("e4m3", h["A"], sfa, rows=rows)
+        nb = oracle.row_norms("e4m3", h["B"], sfb, rows=cols, gran_mn=128)
+    else:
+        ref = oracle.gemm_fp4(h["A"], sfa, h["B"], sfb, K, rows=rows, cols=cols)
+        na = oracle.row_norms("e2m1", h["A"], sfa, K=K, rows=rows)
+        nb = oracle.row_norms("e2m1", h["B"], sfb, K=K, rows=cols)
+    return ref, na, nb
+
+
+def host(t):
+    out = {}
+    for k, v in t.items():
+        if v.dtype == torch.bfloat16:
+            out[k] = v.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        else:
+            out[k] = v.contiguous().view(torch.uint8).cpu().numpy() if v.element_size() == 1 \
+                else v.cpu().numpy()
+    return out
+
+
+def dense_full(kind, M, N, K, seed):
+    w = workloads.dense(kind, M, N, K, seed, device="cpu")
+    t = {k: v.to(DEV) for k, v in w.tensors.items()}
+    D = run_gpu(kind, t, K=K)
+    torch.cuda.synchronize()
+    ref, na, nb = run_oracle(kind, host(w.tensors), K)
+    return assert_parity(gpu_bits(D), ref, na, nb, what=f"{kind} {M}x{N}x{K} seed {seed}")
+
+
+# ---------------------------------------------------------------------------
+# scale packing
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mn,kb,ldp", [(1, 1, 1), (5, 3, 5), (1024, 32, 1024), (300, 57, 320),
+                                       (7168, 512, 7168)])
+def test_pack_unpack_bit_exact(mn, kb, ldp):
+    _say(f"pack mn={mn} kb={kb} ld={ldp}")
+    g = torch.Generator().manual_seed(mn * 7 + kb)
+    sf = torch.randint(0, 256, (mn, kb), generator=g, dtype=torch.int32).to(torch.uint8)
+    p = bsg.pack_ue8m0_scales(sf.to(DEV), ld_packed=ldp)
+    torch.cuda.synchronize()
+    want = oracle.pack_scales(sf.numpy(), ld_packed=ldp)
+    got = p.cpu().numpy()
+    assert np.array_equal(got[:, :mn], want[:, :mn])
+    back = bsg.unpack_ue8m0_scales(p, mn, kb)
+    assert np.array_equal(back.cpu().numpy(), sf.numpy())
+
+
+def test_ensure_packed_reuses_or_converts():
+    sf = torch.randint(0, 256, (64, 6), dtype=torch.int32).to(torch.uint8).to(DEV)
+    p = bsg.ensure_packed(sf, 64, 6)
+    assert p.dtype == torch.int16 and tuple(p.shape) == (3, 64)
+    assert bsg.ensure_packed(p, 64, 6) is p
+    e8 = sf.view(torch.float8_e8m0fnu)
+    assert torch.equal(bsg.ensure_packed(e8, 64, 6), p)
+    with pytest.raises(TypeError):
+        bsg.ensure_packed(sf.float(), 64, 6)
+
+
+# ---------------------------------------------------------------------------
+# dense parity
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8", "fp4"])
+def test_dense_small(kind):
+    _say(f"dense small {kind}")
+    dense_full(kind, 256, 256, 512, 1001)
+
+
+@pytest.mark.parametrize("kind,M,N,K", [
+    ("bf16", 300, 520, 200), ("bf16", 1, 1, 8), ("bf16", 513, 257, 1032),
+    ("fp8", 300, 520, 384), ("fp8", 1, 129, 128), ("fp8", 777, 300, 1152),
+    ("fp4", 300, 520, 224), ("fp4", 3, 5, 32), ("fp4", 600, 270, 1056),
+])
+def test_dense_ragged(kind, M, N, K):
+    _say(f"dense ragged {kind} {M}x{N}x{K}")
+    dense_full(kind, M, N, K, 2000 + M)
+
+
+def test_fp8_mid_workload():
+    """FP8 1024x2048x4096 with 1x128 / 128x128 scales, compared in full."""
+    _say("fp8 1024x2048x4096")
+    w = workloads.make("fp8_mid", device="cpu")
+    t = {k: v.to(DEV) for k, v in w.tensors.items()}
+    D = run_gpu("fp8", t)
+    torch.cuda.synchronize()
+    ref, na, nb = run_oracle("fp8", host(w.tensors), w.K)
+    assert_parity(gpu_bits(D), ref, na, nb, what="fp8_mid full")
+
+
+def test_bf16_small_workload():
+    _say("bf16 256x256x512")
+    w = workloads.make("bf16_small", device="cpu")
+    t = {k: v.to(DEV) for k, v in w.tensors.items()}
+    D = run_gpu("bf16", t)
+    torch.cuda.synchronize()
+    ref, na, nb = run_oracle("bf16", host(w.tensors), w.K)
+    assert_parity(gpu_bits(D), ref, na, nb, what="bf16_small full")
+
+
+LARGE = {"bf16": "bf16_large", "fp8": "fp8_large", "fp4": "fp4_large"}
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8", "fp4"])
+def test_large_workload_sampled(kind):
+    """4096x7168x16384: sampled rows x all columns and sampled columns x all rows."""
+    name = LARGE[kind]
+    _say(f"large {name}: generating on the GPU")
+    w = workloads.make(name, device=DEV)
+    D = run_gpu(kind, w.tensors, K=w.K)
+    torch.cuda.synchronize()
+    _say(f"large {name}: GPU done, oracle on samples")
+    g = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, 2047, 4095],
+                                     g.integers(0, w.M, 4)]))
+    cols = np.unique(np.concatenate([[0, 1, 127, 128, 223, 224, 255, 256, 3583, 7167],
+                                     g.integers(0, w.N, 2)]))
+    h = host(w.tensors)
+    ref, na, nb = run_oracle(kind, h, w.K, rows=rows)
+    Dh = gpu_bits(D)
+    assert_parity(Dh[rows], ref, na, nb, what=f"{name} rows {len(rows)} x all cols")
+    ref, na, nb = run_oracle(kind, h, w.K, cols=cols)
+    assert_parity(Dh[:, cols], ref, na, nb, what=f"{name} all rows x cols {len(cols)}")
+
+
+# ---------------------------------------------------------------------------
+# structured cases with exactly known results (bit-exact)
+# ---------------------------------------------------------------------------
+
+def test_fp8_identity_gives_dequant_b_bit_exact():
+    K = 512
+    g = torch.Generator().manual_seed(11)
+    B = torch.randint(0, 256, (300, K), generator=g, dtype=torch.int32).to(torch.uint8)
+    B[(B & 0x7F) == 0x7F] = 0x38
+    sfb = torch.randint(120, 135, (3, K // 128), generator=g, dtype=torch.int32).to(torch.uint8)
+    A = torch.zeros(K, K, dtype=torch.uint8)
+    A[torch.arange(K), torch.arange(K)] = 0x38
+    sfa = torch.full((K, K // 128), 127, dtype=torch.uint8)
+    t = {"A": A.to(DEV), "sfa": sfa.to(DEV), "B": B.to(DEV), "sfb": sfb.to(DEV)}
+    D = run_gpu("fp8", t)
+    ref = oracle.gemm_fp8(A.numpy(), oracle.pack_scales(sfa.numpy()), B.numpy(),
+                          oracle.pack_scales(sfb.numpy()))
+    got, want = gpu_bits(D), oracle.bf16_rne(ref)
+    nz = (want & 0x7FFF) != 0
+    assert np.array_equal(got[nz], want[nz]) and np.all((got[~nz] & 0x7FFF) == 0)
+
+
+def test_fp4_identity_gives_dequant_b_bit_exact():
+    K = 256
+    g = torch.Generator().manual_seed(12)
+    B = torch.randint(0, 256, (200, K // 2), generator=g, dtype=torch.int32).to(torch.uint8)
+    sfb = torch.randint(118, 136, (200, K // 32), generator=g, dtype=torch.int32).to(torch.uint8)
+    codes = torch.zeros(K, K, dtype=torch.uint8)
+    codes[torch.arange(K), torch.arange(K)] = 0x2
+    A = (codes[:, 0::2] | (codes[:, 1::2] << 4)).contiguous()
+    sfa = torch.full((K, K // 32), 127, dtype=torch.uint8)
+    t = {"A": A.to(DEV), "sfa": sfa.to(DEV), "B": B.to(DEV), "sfb": sfb.to(DEV)}
+    D = run_gpu("fp4", t, K=K)
+    ref = oracle.gemm_fp4(A.numpy(), oracle.pack_scales(sfa.numpy()), B.numpy(),
+                          oracle.pack_scales(sfb.numpy()), K)
+    got, want = gpu_bits(D), oracle.bf16_rne(ref)
+    nz = (want & 0x7FFF) != 0
+    assert np.array_equal(got[nz], want[nz]) and np.all((got[~nz] & 0x7FFF) == 0)
+
+
+@pytest.mark.parametrize("kind", ["fp8", "fp4"])
+def test_scale_only_closed_form_bit_exact(kind):
+    """Unit codes everywhere: D depends on the scales alone and is exact in fp32."""
+    M, N = 200, 300
+    K = 128 * 6 if kind == "fp8" else 32 * 14
+    g = torch.Generator().manual_seed(13)
+    if kind == "fp8":
+        A = torch.full((M, K), 0x38, dtype=torch.uint8)
+        B = torch.full((N, K), 0x38, dtype=torch.uint8)
+        sfa = torch.randint(120, 133, (M, K // 128), generator=g, dtype=torch.int32).to(torch.uint8)
+        sfb = torch.randint(120, 133, ((N + 127) // 128, K // 128), generator=g,
+                            dtype=torch.int32).to(torch.uint8)
+    else:
+        A = torch.full((M, K // 2), 0x22, dtype=torch.uint8)
+        B = torch.full((N, K // 2), 0x22, dtype=torch.uint8)
+        sfa = torch.randint(120, 133, (M, K // 32), generator=g, dtype=torch.int32).to(torch.uint8)
+        sfb = torch.randint(120, 133, (N, K // 32), generator=g, dtype=torch.int32).to(torch.uint8)
+    t = {"A": A.to(DEV), "sfa": sfa.to(DEV), "B": B.to(DEV), "sfb": sfb.to(DEV)}
+    D = run_gpu(kind, t, K=K)
+    ref, _, _ = run_oracle(kind, host({"A": A, "sfa": sfa, "B": B, "sfb": sfb}), K)
+    assert np.array_equal(gpu_bits(D), oracle.bf16_rne(ref))
+
+
+def test_all_ones_gives_K():
+    K = 4096
+    A = torch.ones(130, K, dtype=torch.bfloat16, device=DEV)
+    D = bsg.gemm_bf16(A, A[:70])
+    assert torch.all(D.float() == K)
+
+
+def test_k_zero_writes_zeros_and_empty_is_noop():
+    A = torch.zeros(10, 0, dtype=torch.bfloat16, device=DEV)
+    B = torch.zeros(20, 0, dtype=torch.bfloat16, device=DEV)
+    out = torch.full((10, 24), 3.0, dtype=torch.bfloat16, device=DEV)
+    bsg.gemm_bf16(A, B, out=out)
+    assert torch.all(out[:, :20] == 0) and torch.all(out[:, 20:] == 3.0)
+    E = torch.zeros(0, 64, dtype=torch.bfloat16, device=DEV)
+    assert bsg.gemm_bf16(E, torch.zeros(8, 64, dtype=torch.bfloat16, device=DEV)).shape == (0, 8)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8", "fp4"])
+def test_run_to_run_bitwise_deterministic(kind):
+    w = workloads.dense(kind, 1024, 1536, 2048, 99, device=DEV)
+    D1 = run_gpu(kind, w.tensors, K=w.K)
+    D2 = run_gpu(kind, w.tensors, K=w.K)
+    torch.cuda.synchronize()
+    assert torch.equal(D1.view(torch.int16), D2.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# grouped
+# ---------------------------------------------------------------------------
+
+def run_grouped(w, out=None):
+    t = w.tensors
+    K = w.K
+    sfa = bsg.ensure_packed(t["sfa"], t["A"].shape[0], K // 128)
+    sfb = torch.stack([bsg.ensure_packed(s, (w.N + 127) // 128, K // 128) for s in t["sfb"]])
+    return bsg.m_grouped_gemm_fp8(t["A"], sfa, t["B"], sfb, t["offsets"], out=out)
+
+
+def grouped_oracle(w, rows, experts_needed=None):
+    t = w.tensors
+    off = t["offsets"].cpu().numpy()
+    A = _u8(t["A"])
+    sfa = oracle.pack_scales(t["sfa"].cpu().numpy())
+    G = off.size - 1
+    # decode only the experts that own a sampled row (the rest are not read)
+    need = sorted({int(np.searchsorted(off, r, side="right") - 1) for r in rows
+                   if off[0] <= r < off[-1]})
+    Bsub = np.stack([_u8(t["B"][g]) for g in need]) if need else np.zeros((0, w.N, w.K), np.uint8)
+    sfbsub = np.stack([oracle.pack_scales(t["sfb"][g].cpu().numpy()) for g in need]) if need else \
+        np.zeros((0, 1, 1), np.int16)
+    sub_off = []
+    # remap rows of the needed experts onto a compact offset table
+    ref = np.full((len(rows), w.N), np.nan)
+    na = np.zeros(len(rows))
+    nb_by_g = {}
+    for i, r in enumerate(rows):
+        if not (off[0] <= r < off[-1]):
+            continue
+        g = int(np.searchsorted(off, r, side="right") - 1)
+        j = need.index(g)
+        one_off = np.array([0, 1], np.int32)
+        ref[i] = oracle.grouped_fp8(A[r:r + 1], oracle.pack_scales(t["sfa"][r:r + 1].cpu().numpy()),
+                                    Bsub[j:j + 1], sfbsub[j:j + 1], one_off)[0]
+        na[i] = oracle.row_norms("e4m3", A[r:r + 1],
+                                 oracle.pack_scales(t["sfa"][r:r + 1].cpu().numpy()))[0]
+        if g not in nb_by_g:
+            nb_by_g[g] = oracle.row_norms("e4m3", Bsub[j], sfbsub[j], gran_mn=128)
+    return ref, na, nb_by_g, off
+
+
+def check_grouped(w, D, rows, what):
+    ref, na, nb_by_g, off = grouped_oracle(w, rows)
+    Dh = gpu_bits(D)
+    for i, r in enumerate(rows):
+        if not (off[0] <= r < off[-1]):
+            continue
+        g = int(np.searchsorted(off, r, side="right") - 1)
+        assert_parity(Dh[r:r + 1], ref[i:i + 1], na[i:i + 1], nb_by_g[g],
+                      what=f"{what} row {r} expert {g}")
+
+
+def test_grouped_small_full():
+    w = workloads.grouped(5, 640, 512, seed=21, device=DEV, counts=[128, 0, 256, 128, 0])
+    D = run_grouped(w)
+    torch.cuda.synchronize()
+    rows = np.arange(w.tensors["A"].shape[0])
+    # full comparison through the oracle's own grouped path
+    t = w.tensors
+    ref = oracle.grouped_fp8(_u8(t["A"]), oracle.pack_scales(t["sfa"].cpu().numpy()),
+                             np.stack([_u8(b) for b in t["B"]]),
+                             np.stack([oracle.pack_scales(s.cpu().numpy()) for s in t["sfb"]]),
+                             t["offsets"].cpu().numpy(), rows=rows)
+    na = oracle.row_norms("e4m3", _u8(t["A"]), oracle.pack_scales(t["sfa"].cpu().numpy()))
+    off = t["offsets"].cpu().numpy()
+    Dh = gpu_bits(D)
+    for g in range(5):
+        lo, hi = off[g], off[g + 1]
+        if hi > lo:
+            nb = oracle.row_norms("e4m3", _u8(t["B"][g]), oracle.pack_scales(t["sfb"][g].cpu().numpy()),
+                                  gran_mn=128)
+            assert_parity(Dh[lo:hi], ref[lo:hi], na[lo:hi], nb, what=f"grouped small expert {g}")
+
+
+def test_grouped_unaligned_offsets_and_untouched_rows():
+    """Offsets need no alignment; rows outside [off[0], off[G]) are not written."""
+    G, N, K = 5, 256, 256
+    w = workloads.grouped(G, N, K, seed=22, device=DEV, counts=[100, 0, 37, 300, 1], align=1)
+    t = w.tensors
+    # shift every expert by 5 rows: rows 0..4 and the tail belong to no expert
+    Mt = t["A"].shape[0] + 9
+    A = torch.zeros(Mt, K, dtype=torch.uint8, device=DEV)
+    A[5:5 + t["A"].shape[0]] = t["A"]
+    sfa = torch.full((Mt, K // 128), 127, dtype=torch.uint8, device=DEV)
+    sfa[5:5 + t["A"].shape[0]] = t["sfa"]
+    off = (t["offsets"] + 5).to(torch.int32)
+    w.tensors.update(A=A, sfa=sfa, offsets=off)
+    out = torch.full((Mt, N), -7.0, dtype=torch.bfloat16, device=DEV)
+    run_grouped(w, out=out)
+    torch.cuda.synchronize()
+    o = off.cpu().numpy()
+    assert torch.all(out[:o[0]] == -7.0) and torch.all(out[o[-1]:] == -7.0)
+    rows = list(range(o[0], o[-1]))
+    check_grouped(w, out, rows[:: max(1, len(rows) // 60)] + [o[-1] - 1], "grouped unaligned")
+
+
+def test_grouped_single_expert_equals_dense():
+    K, N = 512, 384
+    w = workloads.grouped(1, N, K, seed=23, device=DEV, counts=[384])
+    D = run_grouped(w)
+    t = w.tensors
+    sfa = bsg.ensure_packed(t["sfa"], 384, K // 128)
+    sfb = bsg.ensure_packed(t["sfb"][0], 3, K // 128)
+    Dd = bsg.gemm_fp8_blockscaled(t["A"], sfa, t["B"][0], sfb)
+    torch.cuda.synchronize()
+    assert torch.equal(D.view(torch.int16), Dd.view(torch.int16))
+
+
+def test_grouped_moe_workload_sampled():
+    """256 experts, N=2048, K=7168, Zipf(1.1) routing padded to 128 rows."""
+    _say("moe_fp8: generating on the GPU")
+    w = workloads.make("moe_fp8", device=DEV)
+    D = run_grouped(w)
+    torch.cuda.synchronize()
+    _say("moe_fp8: GPU done, oracle on samples")
+    off = w.tensors["offsets"].cpu().numpy()
+    counts = w.tensors["counts"].cpu().numpy()
+    big = int(np.argmax(counts))
+    nz = np.nonzero(counts)[0]
+    small = int(nz[np.argmin(counts[nz])])
+    rows = [off[big], off[big] + 1, off[big + 1] - 1, off[small], off[small] + counts[small] - 1,
+            off[small + 1] - 1, off[0], off[-1] - 1]
+    g = np.random.default_rng(7)
+    rows += list(g.integers(off[0], off[-1], 6))
+    check_grouped(w, D, sorted(set(int(r) for r in rows)), "moe_fp8")
