@@ -1,0 +1,307 @@
+"""Benchmark of the block-scaled GEMM library on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--dtypes bf16,fp8,fp4,grouped]
+
+Workload: D = A * B^T at M=4096, N=7168, K=16384, the dense shape the pages time
+(431 TFLOPS BF16 on the other accelerator: "DeepSeek lanza kernels de DeepGEMM
+para Huawei Ascend 950", section "Que alcance tienen las pruebas de
+rendimiento"), in BF16, in FP8 e4m3 with 1x128 / 128x128 UE8M0 scales and in FP4
+e2m1 with 1x32 scales, plus the M-grouped FP8 MoE GEMM (256 experts, N=2048,
+K=7168, 16384 tokens routed top-6 with Zipf(1.1) popularity).  All inputs are
+seeded synthetic data generated straight into HBM before timing starts.
+
+One JSON line is printed.  `value` is the BF16 GEMM's whole-run throughput in
+TFLOPS (2*M*N*K per call, the pages' convention) over exactly `--steps` timed
+calls, bracketed by device synchronisation; every other dtype is timed the same
+way in the same run and reported under `per_dtype` with its fraction of the
+dtype's dense MFMA peak.  Each call is also bracketed by HIP events on the
+stream it is launched on; their mean is the launch duration behind `roofline`.
+A cold-L2 variant (a 512 MiB scratch write before each sample, more than the
+MALL plus every XCD's L2) is reported per dtype as `cold_l2_us`.
+
+`cpu_baseline` times the CPU oracle (plain C, fp64) on a bounded row sample of
+the BF16 workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "TFLOPS and % of MI355X dense MFMA peak, GEMM 4096×7168×16384 per dtype"
+
+# MI355X published dense MFMA peaks (TFLOP/s).
+PEAK = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0, "grouped": 5000.0}
+# The pages' own figure at this shape (other accelerator; context only).
+PAGES_BF16_TFLOPS = 431.0
+
+KERNEL_NAME = {
+    "bf16": "gemm_kernel<0, 256, 256, 2, 2, false>",
+    "fp8": "gemm_kernel<1, 256, 256, 2, 2, false>",
+    "fp4": "gemm_kernel<2, 256, 256, 2, 2, false>",
+    "grouped": "gemm_kernel<1, 128, 512, 1, 4, true>",
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_sources_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_scaled_precision_05_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kind: str, sha: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            tab = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = tab.get(kind)
+    if not ent or ent.get("src_sha") != sha:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def make_case(kind, dev):
+    """Returns (call, flops, min_bytes, meta) with every input resident on `dev`."""
+    import torch
+    import block_scaled_precision_05_amd as bsg
+    from block_scaled_precision_05_amd import workloads
+
+    name = {"bf16": "bf16_large", "fp8": "fp8_large", "fp4": "fp4_large",
+            "grouped": "moe_fp8"}[kind]
+    w = workloads.make(name, device=dev)
+    t = w.tensors
+    M, N, K = w.M, w.N, w.K
+    if kind == "bf16":
+        A, B = t["A"], t["B"]
+        D = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        call = lambda: bsg.gemm_bf16(A, B, out=D)
+        nbytes = 2 * (M * K + N * K + M * N)
+        meta = {}
+    elif kind == "fp8":
+        A, B, sfa_u8, sfb_u8 = t["A"], t["B"], t["sfa"], t["sfb"]
+        D = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        sfa = bsg.ensure_packed(sfa_u8, M, K // 128)
+        sfb = bsg.ensure_packed(sfb_u8, (N + 127) // 128, K // 128)
+
+        def call():
+            # reuse-or-convert on every call, as the pages' scale helper does
+            a = bsg.ensure_packed(sfa, M, K // 128)
+            b = bsg.ensure_packed(sfb, (N + 127) // 128, K // 128)
+            return bsg.gemm_fp8_blockscaled(A, a, B, b, out=D)
+        nbytes = M * K + N * K + 2 * M * N + 2 * (sfa.numel() + sfb.numel())
+        meta = {"scales": "sfa 1x128, sfb 128x128, UE8M0 e~U{-8..4}, packed int16 MN-major"}
+    elif kind == "fp4":
+        A, B, sfa_u8, sfb_u8 = t["A"], t["B"], t["sfa"], t["sfb"]
+        D = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        sfa = bsg.ensure_packed(sfa_u8, M, K // 32)
+        sfb = bsg.ensure_packed(sfb_u8, N, K // 32)
+
+        def call():
+            a = bsg.ensure_packed(sfa, M, K // 32)
+            b = bsg.ensure_packed(sfb, N, K // 32)
+            return bsg.gemm_fp4_blockscaled(A, a, B, b, K=K, out=D)
+        nbytes = (M * K + N * K) // 2 + 2 * M * N + 2 * (sfa.numel() + sfb.numel())
+        meta = {"scales": "1x32 UE8M0, OCP MX rule floor(log2 amax)-2"}
+    else:
+        A, sfa_u8, B, sfb_u8, off = t["A"], t["sfa"], t["B"], t["sfb"], t["offsets"]
+        G = B.shape[0]
+        D = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        sfa = bsg.ensure_packed(sfa_u8, M, K // 128)
+        sfb = torch.stack([bsg.ensure_packed(s, (N + 127) // 128, K // 128) for s in sfb_u8])
+        call = lambda: bsg.m_grouped_gemm_fp8(A, sfa, B, sfb, off, out=D)
+        nbytes = M * K + B.numel() + 2 * M * N + 2 * (sfa.numel() + sfb.numel())
+        meta = {"experts": G, "m_total": M, "useful_rows": w.meta["useful_rows"],
+                "routing": w.meta["routing"],
+                "executed_tflop": 2.0 * M * N * K / 1e12}
+    flops = w.flops
+    meta.update({"M": M, "N": N, "K": K})
+    return call, flops, nbytes, meta
+
+
+def time_case(kind, steps, warmup, dev, cold_samples):
+    import torch
+    call, flops, nbytes, meta = make_case(kind, dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        call()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) * 1e3 for s, e in ev]          # microseconds
+    res = {"wall_s": wall, "per_launch_us": per, "flops": flops, "min_bytes": nbytes,
+           "meta": meta}
+    if cold_samples > 0:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold = []
+        for _ in range(cold_samples):
+            scratch.fill_(1)
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            call()
+            e.record(stream)
+            e.synchronize()
+            cold.append(s.elapsed_time(e) * 1e3)
+        res["cold_us"] = cold
+        del scratch
+    return res
+
+
+def summarize(kind, r, steps):
+    per = sorted(r["per_launch_us"])
+    mean_us = statistics.fmean(per)
+    med = statistics.median(per)
+    out = {
+        "tflops": r["flops"] * steps / r["wall_s"] / 1e12,
+        "wall_ms_per_call": r["wall_s"] * 1e3 / steps,
+        "tflops_median_launch": r["flops"] / (med * 1e-6) / 1e12,
+        "frac_of_peak": r["flops"] * steps / r["wall_s"] / 1e12 / PEAK[kind],
+        "peak_tflops": PEAK[kind],
+        "launch_us_mean": mean_us,
+        "launch_us_median": med,
+        "launch_us_min": per[0],
+        "launch_us_p90": per[min(len(per) - 1, int(0.9 * len(per)))],
+        "tflop_per_call": r["flops"] / 1e12,
+        "min_hbm_mb": r["min_bytes"] / 1e6,
+    }
+    if "cold_us" in r:
+        c = sorted(r["cold_us"])
+        out["cold_l2_us_median"] = statistics.median(c)
+        out["cold_l2_tflops"] = r["flops"] / (statistics.median(c) * 1e-6) / 1e12
+    out.update(r["meta"])
+    return out
+
+
+def cpu_baseline(budget_s: float):
+    """Times the CPU oracle on rows of the BF16 4096x7168x16384 workload: chunks
+    of 128 rows (all 7168 columns each) until `budget_s` seconds have passed."""
+    import numpy as np
+    import torch
+    import oracle
+    from block_scaled_precision_05_amd import workloads
+
+    w = workloads.make("bf16_large", device="cpu")
+    A = w.tensors["A"].view(torch.int16).numpy().view(np.uint16)
+    B = w.tensors["B"].view(torch.int16).numpy().view(np.uint16)
+    done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s and done < w.M:
+        rows = np.arange(done, min(done + 128, w.M))
+        oracle.gemm_bf16(A, B, rows=rows)
+        done += rows.size
+    dt = time.perf_counter() - t0
+    flops = 2.0 * done * w.N * w.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"BF16 4096x7168x16384, rows 0..{done - 1} x all 7168 columns "
+                      f"({done} of 4096 rows, {dt:.1f} s, in chunks of 128 rows)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--dtypes", default="bf16,fp8,fp4,grouped")
+    ap.add_argument("--cold-samples", type=int, default=10)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle time for cpu_baseline (0 disables it)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this library has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_scaled_precision_05_amd as bsg
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    bsg.lib()   # fails loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    kinds = [k.strip() for k in args.dtypes.split(",") if k.strip()]
+    if "bf16" not in kinds:
+        kinds = ["bf16"] + kinds
+    sha = kernel_sources_sha()
+
+    per = {}
+    for kind in kinds:
+        log(f"{kind}: generating inputs and timing {args.warmup}+{args.steps} calls")
+        r = time_case(kind, args.steps, args.warmup, dev, args.cold_samples)
+        per[kind] = summarize(kind, r, args.steps)
+        log(f"{kind}: {per[kind]['tflops']:.1f} TFLOPS "
+            f"({100 * per[kind]['frac_of_peak']:.1f}% of peak), "
+            f"{per[kind]['launch_us_mean']:.1f} us per launch")
+        torch.cuda.empty_cache()
+
+    b = per["bf16"]
+    roof = {
+        "kernel": KERNEL_NAME["bf16"],
+        "bound": "mfma",
+        "achieved": b["tflop_per_call"] / (b["launch_us_mean"] * 1e-6),
+        "peak": PEAK["bf16"],
+        "unit": "TFLOP/s",
+    }
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = load_traffic("bf16", sha)
+    roof["src_sha"] = sha
+
+    cpu = None
+    if args.cpu_budget > 0:
+        log(f"cpu_baseline: oracle for ~{args.cpu_budget:.0f} s")
+        cpu = cpu_baseline(args.cpu_budget)
+
+    steps = args.steps
+    line = {
+        "metric": METRIC,
+        "value": b["tflops"],
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": b["wall_ms_per_call"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": b["tflops"] / PAGES_BF16_TFLOPS,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gemm_bf16 D=A*B^T M=4096 N=7168 K=16384, bf16 N(0,1) inputs, "
+                               "fp32 accumulate, bf16 out",
+                   "M": 4096, "N": 7168, "K": 16384, "parallelism": "single GPU"},
+        "frac_of_peak": b["frac_of_peak"],
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "per_dtype": per,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
