@@ -50,11 +50,16 @@ __global__ void unpack_kernel(const int16_t* __restrict__ packed, int64_t mn, in
 // Tile configurations.
 // ---------------------------------------------------------------------------
 // Dense: 256x256 workgroup tile, 2x2 waves of 128x128 (16 fragments of 32x32 per
-// wave, 256 fp32 accumulators per lane).  Two 64 KiB LDS stages.
-#define BSG_DENSE_CFG 256, 256, 2, 2
+// wave, 256 fp32 accumulators per lane).  The copy into LDS is bound by how many
+// requests a CU keeps in flight, so full 128-byte lines per row (two 64 KiB
+// stages) beat a deeper ring of half lines for BF16 and FP8; FP4, with four times
+// the MFMA rate per byte, prefers the deeper ring of four 32 KiB stages.
+#define BSG_BF16_CFG 256, 256, 2, 2, 128, 2
+#define BSG_FP8_CFG 256, 256, 2, 2, 128, 2
+#define BSG_FP4_CFG 256, 256, 2, 2, 64, 4
 // Grouped: 128-row tiles so 128-aligned experts waste no rows; 1x4 waves of
-// 128x128 over a 512-wide N tile.  Two 80 KiB LDS stages.
-#define BSG_GROUPED_CFG 128, 512, 1, 4
+// 128x128 over a 512-wide N tile; two 80 KiB stages (the whole LDS).
+#define BSG_GROUPED_CFG 128, 512, 1, 4, 128, 2
 
 static int g_num_cus[64];
 
@@ -70,12 +75,13 @@ static int num_cus() {
   return g_num_cus[dev];
 }
 
-template <int KIND, int BM, int BN, int WM, int WN, bool GROUPED>
+template <int KIND, int BM, int BN, int WM, int WN, int SB, int NS, bool GROUPED>
 static int launch(GemmArgs a, hipStream_t stream) {
-  using T = GemmTile<KIND, BM, BN, WM, WN, GROUPED>;
+  using T = GemmTile<KIND, BM, BN, WM, WN, SB, NS>;
   a.d_vec = (((uintptr_t)a.D & 7) == 0 && (a.ldd % 4) == 0) ? 1 : 0;
   a.tiles_m = (a.M + BM - 1) / BM;
   a.tiles_n = (a.N + BN - 1) / BN;
+  a.nk = (a.k_bytes + SB - 1) / SB;
   int grid;
   if (GROUPED) {
     grid = num_cus();
@@ -84,7 +90,8 @@ static int launch(GemmArgs a, hipStream_t stream) {
     grid = (int)(tiles < num_cus() ? tiles : num_cus());
   }
   (void)hipGetLastError();
-  hipLaunchKernelGGL((gemm_kernel<KIND, BM, BN, WM, WN, GROUPED>), dim3(grid), dim3(T::NT), 0, stream, a);
+  hipLaunchKernelGGL((gemm_kernel<KIND, BM, BN, WM, WN, SB, NS, GROUPED>), dim3(grid), dim3(T::NT), 0,
+                     stream, a);
   return hipGetLastError() == hipSuccess ? BSG_OK : BSG_ERR_HIP;
 }
 
@@ -148,8 +155,7 @@ int gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, void* D, i
   a.N = (int32_t)N;
   a.K = (int32_t)K;
   a.k_bytes = (int32_t)(2 * K);
-  a.nk = (int32_t)((2 * K + 127) / 128);
-  return launch<KIND_BF16, BSG_DENSE_CFG, false>(a, (hipStream_t)stream);
+  return launch<KIND_BF16, BSG_BF16_CFG, false>(a, (hipStream_t)stream);
 }
 
 static int check_scales(const int16_t* sfa, int64_t ld_sfa, int64_t rows_a, const int16_t* sfb,
@@ -183,10 +189,9 @@ int gemm_fp8_blockscaled(const void* A, int64_t lda, const int16_t* sfa, int64_t
   a.N = (int32_t)N;
   a.K = (int32_t)K;
   a.k_bytes = (int32_t)K;
-  a.nk = (int32_t)(K / 128);
   a.kp_count = (int32_t)((K / 128 + 1) / 2);
   a.sfb_rows = (int32_t)((N + 127) / 128);
-  return launch<KIND_FP8, BSG_DENSE_CFG, false>(a, (hipStream_t)stream);
+  return launch<KIND_FP8, BSG_FP8_CFG, false>(a, (hipStream_t)stream);
 }
 
 int gemm_fp4_blockscaled(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
@@ -211,10 +216,9 @@ int gemm_fp4_blockscaled(const void* A, int64_t lda, const int16_t* sfa, int64_t
   a.N = (int32_t)N;
   a.K = (int32_t)K;
   a.k_bytes = (int32_t)(K / 2);
-  a.nk = (int32_t)((K / 2 + 127) / 128);
   a.kp_count = (int32_t)((K / 32 + 1) / 2);
   a.sfb_rows = (int32_t)N;
-  return launch<KIND_FP4, BSG_DENSE_CFG, false>(a, (hipStream_t)stream);
+  return launch<KIND_FP4, BSG_FP4_CFG, false>(a, (hipStream_t)stream);
 }
 
 int m_grouped_gemm_fp8(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
@@ -251,7 +255,6 @@ int m_grouped_gemm_fp8(const void* A, int64_t lda, const int16_t* sfa, int64_t l
   a.N = (int32_t)N;
   a.K = (int32_t)K;
   a.k_bytes = (int32_t)K;
-  a.nk = (int32_t)(K / 128);
   a.kp_count = (int32_t)kp;
   a.sfb_rows = (int32_t)((N + 127) / 128);
   a.G = G;

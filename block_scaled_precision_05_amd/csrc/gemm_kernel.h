@@ -3,25 +3,38 @@
 //
 // Data path of one workgroup (WM x WN waves, one wave per SIMD):
 //   HBM/L2 --buffer_load ... lds (16 B per lane, no VGPR round trip)--> LDS
-//   LDS (two stages of 128 bytes of K per tile row, XOR-swizzled) --ds_read_b128--> VGPRs
+//   LDS (a ring of NS stages of SB bytes of K per tile row, XOR-swizzled) --ds_read_b128--> VGPRs
 //   VGPRs --v_mfma_f32_32x32x16_bf16 / v_mfma_scale_f32_32x32x64_f8f6f4--> fp32 accumulators
 //   accumulators --v_cvt to bf16 (round to nearest even)--> D
-// The global loads of stage k+1 are in flight while stage k is multiplied.  This
-// is the MI355X counterpart of the staged, double-buffered operand pipeline the
-// pages describe for the other accelerator ("DeepGEMM-Ascend cobre quantas
-// operacoes no Ascend 950?", sections "O que muda de fato entre CUDA e o Huawei
-// Ascend?" and "Reuso de operandos e pipelining na pratica").
+//
+// Software pipeline.  A stage is 128 bytes of K for every row of the tile, split
+// into J k-steps of one MFMA per (A fragment, B fragment) pair.  Fragments are
+// double-buffered in registers: the LDS reads of k-step j+1 are interleaved with
+// the MFMAs of k-step j.  The single workgroup barrier of a stage sits before its
+// last k-step, whose fragments are already in registers, so the matrix cores keep
+// working while the waves meet; right after it the copy of stage s+2 into the LDS
+// buffer just released is issued, together with the first fragment reads of stage
+// s+1.  Each copy therefore has one full stage of MFMA time to land.  This is the
+// MI355X counterpart of the staged, double-buffered operand pipeline with ready
+// signals that the pages describe for the other accelerator ("DeepGEMM-Ascend
+// cobre quantas operacoes no Ascend 950?", sections "O que muda de fato entre CUDA
+// e o Huawei Ascend?" and "Reuso de operandos e pipelining na pratica").
 //
 // Scale handling (FP8 and FP4): the UE8M0 bytes go straight into the scaled
 // MFMA's per-lane scale operand, so promotion by 2^(e-127) happens inside the
 // matrix core and is exact.  FP8 uses one byte per (row, 128-K block): the stage
 // is exactly one K-block, so every MFMA of a stage sees a row-uniform scale.
 // FP4 uses one byte per (row, 32-K block): each lane's 16-byte operand is
-// exactly one K-block and carries that block's byte.
+// exactly one K-block and carries that block's byte.  Scale words are loaded
+// from global memory two stages ahead, together with the tile copy, and are only
+// decoded after the barrier that waits for that copy, so they never add a wait.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
+#include <utility>
 
 namespace bsg {
 
@@ -71,33 +84,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            kRsrcWord3);
 }
 
-// LDS position of 16-byte chunk c (0..7) of tile row r: rows are 128 bytes; the
-// chunk is XOR-swizzled with (r/2)%8 so that 16 lanes reading one logical chunk
-// of 16 consecutive rows hit 16 distinct (bank-half, chunk) pairs of the 64-bank
-// LDS (conflict-free ds_read_b128).
-__device__ __forceinline__ uint32_t lds_off(int r, int c) {
-  return (uint32_t)(r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
-}
-
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   __bf16 a = (__bf16)lo;   // v_cvt_pk_bf16_f32: round to nearest even
   __bf16 b = (__bf16)hi;
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// FP4 scaled MFMA whose scale byte (K-block s of the lane's scale word) is picked
-// by the instruction's op_sel immediate.
-__device__ __forceinline__ f32x16_t mfma_fp4_sel(int s, i32x8_t b, i32x8_t a, f32x16_t c,
-                                                 uint32_t sb, uint32_t sa) {
-  switch (s) {
-    case 0: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 4, 4, 0, (int)sb, 0, (int)sa);
-    case 1: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 4, 4, 1, (int)sb, 1, (int)sa);
-    case 2: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 4, 4, 2, (int)sb, 2, (int)sa);
-    default: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 4, 4, 3, (int)sb, 3, (int)sa);
-  }
+// Scaled MFMA (32x32x64, fp32 accumulate).  FMT 0 = e4m3, 4 = e2m1; the scale byte
+// used is byte SEL of each lane's scale word (the instruction's op_sel immediate).
+template <int FMT, int SEL>
+__device__ __forceinline__ f32x16_t mfma_scaled(i32x8_t b, i32x8_t a, f32x16_t c, uint32_t sb,
+                                                uint32_t sa) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, FMT, FMT, SEL, (int)sb, SEL,
+                                                         (int)sa);
 }
 
-template <int KIND, int BM, int BN, int WM, int WN, bool GROUPED>
+// Compile-time shape of one kernel instance.
+//   BM x BN   workgroup tile, WM x WN waves (one per SIMD), each wave TM x TN made
+//             of 32x32 MFMA fragments (FM x FN of them);
+//   SB        bytes of K per tile row per stage (64 or 128): 16-byte chunks NC;
+//   NS        LDS stages in the ring; the copy of a stage is issued NS-1 stages
+//             before its data is read.
+template <int KIND, int BM, int BN, int WM, int WN, int SB, int NS>
 struct GemmTile {
   static constexpr int NW = WM * WN;
   static constexpr int NT = NW * 64;
@@ -105,13 +113,37 @@ struct GemmTile {
   static constexpr int TN = BN / WN;     // rows of B per wave
   static constexpr int FM = TM / 32;     // 32x32 fragments per wave along M
   static constexpr int FN = TN / 32;
-  static constexpr int STAGE_BYTES = (BM + BN) * 128;
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
-  static constexpr int A_LOADS = BM / 8 / NW;   // buffer_load_lds x4 per wave per stage
-  static constexpr int B_LOADS = BN / 8 / NW;
+  static constexpr int NC = SB / 16;     // 16-byte chunks per row per stage
+  static constexpr int RPS = 16 / NC;    // consecutive rows sharing one swizzle value
+  // k-steps per stage and 16-byte LDS reads per fragment per k-step:
+  //   BF16 32x32x16 (16 bytes per lane), FP8 32x32x64 (32 bytes), FP4 32x32x64 (16 bytes)
+  static constexpr int J = KIND == KIND_FP8 ? NC / 4 : NC / 2;
+  static constexpr int RPF = KIND == KIND_FP8 ? 2 : 1;
+  static constexpr int STAGE_BYTES = (BM + BN) * SB;
+  static constexpr int LDS_BYTES = NS * STAGE_BYTES;
+  static constexpr int ROWS_PER_COPY = 1024 / SB;          // rows of one 1 KiB wave copy
+  static constexpr int A_LOADS = BM / ROWS_PER_COPY / NW;  // wave copies per stage
+  static constexpr int B_LOADS = BN / ROWS_PER_COPY / NW;
+  static constexpr int N_DMA = A_LOADS + B_LOADS;
+  // packed scale words per lane per fragment per stage: FP8 one (the K-block's
+  // pair), FP4 NC/4 (lane group lg takes NC/2 K-blocks of 32)
+  static constexpr int SW = KIND == KIND_BF16 ? 0 : (KIND == KIND_FP8 ? 1 : NC / 4);
+  static constexpr int NSC = (FM + (KIND == KIND_FP8 ? 1 : FN)) * SW;
+  static constexpr int VMEM_PER_STAGE = N_DMA + NSC;
+  static_assert(SB == 64 || SB == 128, "a stage is 64 or 128 bytes of K per row");
+  static_assert(NS >= 2 && NS <= 8, "ring of 2..8 stages");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be made of 32x32 fragments");
-  static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "rows must split evenly over waves");
-  static_assert(LDS_BYTES <= 163840, "two stages must fit in LDS");
+  static_assert((BM / ROWS_PER_COPY) % NW == 0 && (BN / ROWS_PER_COPY) % NW == 0,
+                "rows must split evenly over waves");
+  static_assert(LDS_BYTES <= 163840, "the ring must fit in LDS");
+  static_assert((NS - 1) * N_DMA <= 63, "outstanding copies must fit the vmcnt counter");
+  static_assert((NS * J) % 2 == 0, "a round of the ring must hold an even number of k-steps");
+  // LDS position of 16-byte chunk c of tile row r: the chunk is XOR-swizzled with
+  // (r / RPS) % NC so that the 16 lanes of one ds_read_b128 phase, reading one
+  // logical chunk of 16 consecutive rows, cover all 64 banks exactly once.
+  static __device__ __forceinline__ uint32_t lds_off(int r, int c) {
+    return (uint32_t)(r * SB + ((c ^ ((r / RPS) % NC)) << 4));
+  }
 };
 
 // Wave-wide inclusive prefix sum of one int per lane.
@@ -202,10 +234,53 @@ __device__ __forceinline__ void raster(int p, int tiles_m, int tiles_n, int& tm,
   tn = r / gm;
 }
 
-template <int KIND, int BM, int BN, int WM, int WN, bool GROUPED>
+// Interleaves, inside one scheduling region, each MFMA with the next LDS read and
+// the next global load, front-loading the loads so their latency hides behind the
+// remaining MFMAs.
+template <int NMFMA, int NDS, int NVMEM, int I>
+__device__ __forceinline__ void interleave_one() {
+  constexpr int ds_per = (NDS + NMFMA - 1) / NMFMA;
+  constexpr int vm_per = (NVMEM + NMFMA - 1) / NMFMA;
+  constexpr int ds_n = I * ds_per < NDS ? ((NDS - I * ds_per) < ds_per ? NDS - I * ds_per : ds_per) : 0;
+  constexpr int vm_n = I * vm_per < NVMEM ? ((NVMEM - I * vm_per) < vm_per ? NVMEM - I * vm_per : vm_per) : 0;
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                        // MFMA
+  if constexpr (ds_n > 0) __builtin_amdgcn_sched_group_barrier(0x100, ds_n, 0);  // DS read
+  if constexpr (vm_n > 0) __builtin_amdgcn_sched_group_barrier(0x020, vm_n, 0);  // VMEM read
+}
+
+template <int NMFMA, int NDS, int NVMEM>
+__device__ __forceinline__ void interleave() {
+  [&]<int... is>(std::integer_sequence<int, is...>) {
+    (interleave_one<NMFMA, NDS, NVMEM, is>(), ...);
+  }(std::make_integer_sequence<int, NMFMA>{});
+}
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most `vm` vector memory
+// loads are outstanding and every LDS access has completed.
+template <int VM>
+__device__ __forceinline__ void wait_vm_lds() {
+  static_assert(VM >= 0 && VM <= 63, "vmcnt is 6 bits");
+  constexpr int imm = (VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14);
+  __builtin_amdgcn_s_waitcnt(imm);
+}
+
+// Workgroup barrier of the LDS ring.  The caller waits for exactly the copies and
+// LDS reads it needs first (wait_vm_lds); a __syncthreads() would also wait for
+// every copy still in flight, which would empty the ring at each stage.  The
+// signal fences keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void ring_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <int KIND, int BM, int BN, int WM, int WN, int SB, int NS, bool GROUPED>
 __global__ __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(const GemmArgs args) {
-  using T = GemmTile<KIND, BM, BN, WM, WN, GROUPED>;
+  using T = GemmTile<KIND, BM, BN, WM, WN, SB, NS>;
+  constexpr int FM = T::FM, FN = T::FN, J = T::J, RPF = T::RPF, NC = T::NC, SW = T::SW;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
 
   const int tid = threadIdx.x;
@@ -213,6 +288,9 @@ void gemm_kernel(const GemmArgs args) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31, lg = lane >> 5;
+  const int nk = args.nk;
+  const int nk_pad = (nk + NS - 1) / NS * NS;   // whole rounds of the ring; the extra
+                                                // stages multiply zeros
 
   int total_tiles;
   GroupCursor cur{0, 0};
@@ -221,6 +299,34 @@ void gemm_kernel(const GemmArgs args) {
   } else {
     total_tiles = args.tiles_m * args.tiles_n;
   }
+
+  // Per-lane LDS byte offsets of this lane's fragment reads for k-step j (fragment
+  // f adds 32*f rows; the swizzle depends only on l32 since 32 rows is a whole
+  // number of swizzle periods).
+  //   BF16: lane group lg reads chunk 2j + lg (8 bf16 = K 16j + 8lg .. +7).
+  //   FP8:  chunks 4j + 2lg and 4j + 2lg + 1 (32 e4m3 values).
+  //   FP4:  chunk (NC/2)*lg + j (32 e2m1 values = one 32-wide K-block).
+  const int a_row0 = wm * T::TM + l32;
+  const int b_row0 = wn * T::TN + l32;
+  uint32_t a_rd[J][RPF], b_rd[J][RPF];
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int h = 0; h < RPF; ++h) {
+      const int c = KIND == KIND_BF16 ? 2 * j + lg
+                                      : (KIND == KIND_FP8 ? 4 * j + 2 * lg + h : (NC / 2) * lg + j);
+      a_rd[j][h] = T::lds_off(a_row0, c);
+      b_rd[j][h] = (uint32_t)(BM * SB) + T::lds_off(b_row0, c);
+    }
+
+  // Copy lanes: lane t of a wave copy covering rows r0 .. r0 + 1024/SB - 1 writes
+  // LDS bytes r0*SB + 16t, i.e. row r0 + t/NC, physical chunk t%NC, which holds
+  // logical chunk (t%NC) ^ swizzle(row).  Copy q of wave w starts at row
+  // r0 = (q*NW + w) * 1024/SB, and r0 / RPS = 4*(q*NW + w), so the swizzle of a
+  // copy row is (4w + (t/NC)/RPS) % NC whatever q is.
+  static_assert((4 * T::NW) % NC == 0, "copy swizzle must not depend on the copy index");
+  const int cp_row = lane / NC;
+  const int cp_c16 = 16 * ((lane % NC) ^ ((4 * wave + cp_row / T::RPS) % NC));
 
   for (int i = blockIdx.x; i < total_tiles; i += gridDim.x) {
     const int p = xcd_remap(i, total_tiles);
@@ -241,6 +347,9 @@ void gemm_kernel(const GemmArgs args) {
       m_end = m0 + BM < args.M ? m0 + BM : args.M;
       n0 = tn * BN;
     }
+    m0 = __builtin_amdgcn_readfirstlane(m0);
+    m_end = __builtin_amdgcn_readfirstlane(m_end);
+    n0 = __builtin_amdgcn_readfirstlane(n0);
     const int n_end = n0 + BN < args.N ? n0 + BN : args.N;
     const int rows_a = m_end - m0, rows_b = n_end - n0;
 
@@ -250,201 +359,230 @@ void gemm_kernel(const GemmArgs args) {
         make_rsrc(args.A + (int64_t)m0 * args.lda, (uint32_t)((rows_a - 1) * args.lda + args.k_bytes));
     const __amdgpu_buffer_rsrc_t rb =
         make_rsrc(Bbase + (int64_t)n0 * args.ldb, (uint32_t)((rows_b - 1) * args.ldb + args.k_bytes));
+    uint32_t a_vbase = (uint32_t)((T::ROWS_PER_COPY * wave + cp_row) * args.lda) + cp_c16;
+    uint32_t b_vbase = (uint32_t)((T::ROWS_PER_COPY * wave + cp_row) * args.ldb) + cp_c16;
+    const uint32_t a_qstep = (uint32_t)(T::ROWS_PER_COPY * T::NW * args.lda);
+    const uint32_t b_qstep = (uint32_t)(T::ROWS_PER_COPY * T::NW * args.ldb);
+    // Opaque per tile: otherwise the compiler hoists every copy offset of the
+    // prologue out of the tile loop and spills them all.
+    asm volatile("" : "+v"(a_vbase), "+v"(b_vbase));
 
-    // Per-lane load offsets for the global->LDS copies: lane t of a wave-load
-    // covering rows r0..r0+7 writes LDS bytes r0*128 + 16t, i.e. row r0 + t/8,
-    // physical chunk t%8, which holds logical chunk (t%8) ^ ((row/2)%8).
-    uint32_t a_voff[T::A_LOADS], b_voff[T::B_LOADS];
-    int a_chunk[T::A_LOADS], b_chunk[T::B_LOADS];
-#pragma unroll
-    for (int q = 0; q < T::A_LOADS; ++q) {
-      const int r = 8 * (q * T::NW + wave) + (lane >> 3);
-      const int c = (lane & 7) ^ ((r >> 1) & 7);
-      a_chunk[q] = c;
-      a_voff[q] = (uint32_t)(r * args.lda) + (uint32_t)(c * 16);
-    }
-#pragma unroll
-    for (int q = 0; q < T::B_LOADS; ++q) {
-      const int r = 8 * (q * T::NW + wave) + (lane >> 3);
-      const int c = (lane & 7) ^ ((r >> 1) & 7);
-      b_chunk[q] = c;
-      b_voff[q] = (uint32_t)(r * args.ldb) + (uint32_t)(c * 16);
-    }
-
+    // Copies stage kt into LDS buffer `buf`; a stage past the end copies nothing
+    // (every lane's offset is out of range, so no memory is read).
     auto issue_stage = [&](int kt, int buf) {
       uint8_t* sA = smem + buf * T::STAGE_BYTES;
-      uint8_t* sB = sA + BM * 128;
-      const int kb = kt * 128;
+      uint8_t* sB = sA + BM * SB;
+      const int kb = kt * SB;
+      const int k_lim = kt < nk ? args.k_bytes : 0;
+      // past the K extent the offset gets bit 31, which no record count reaches
+      const uint32_t oob = kb + cp_c16 < k_lim ? 0u : kOOB;
 #pragma unroll
       for (int q = 0; q < T::A_LOADS; ++q) {
-        const uint32_t off = (kb + a_chunk[q] * 16 < args.k_bytes) ? a_voff[q] + kb : kOOB;
+        const uint32_t off = (a_vbase + q * a_qstep + kb) | oob;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ra, (__attribute__((address_space(3))) void*)(sA + 8 * (q * T::NW + wave) * 128), 16, off,
-            0, 0, 0);
+            ra, (__attribute__((address_space(3))) void*)(sA + T::ROWS_PER_COPY * (q * T::NW + wave) * SB),
+            16, off, 0, 0, 0);
       }
 #pragma unroll
       for (int q = 0; q < T::B_LOADS; ++q) {
-        const uint32_t off = (kb + b_chunk[q] * 16 < args.k_bytes) ? b_voff[q] + kb : kOOB;
+        const uint32_t off = (b_vbase + q * b_qstep + kb) | oob;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rb, (__attribute__((address_space(3))) void*)(sB + 8 * (q * T::NW + wave) * 128), 16, off,
-            0, 0, 0);
+            rb, (__attribute__((address_space(3))) void*)(sB + T::ROWS_PER_COPY * (q * T::NW + wave) * SB),
+            16, off, 0, 0, 0);
       }
     };
 
-    // Scale rows this lane feeds to the MFMAs (clamped into the arrays; rows past
-    // the end only meet zero operands).
-    int sa_row[T::FM], sb_row[T::FN];
+    // Scale loads.  Each lane reads the packed words of the rows it feeds to the
+    // MFMAs: A row m0 + wm*TM + 32f + l32 (f < FM); for FP4 B row n likewise; for
+    // FP8 the one 128-row block of B this wave's TN <= 128 rows fall in.  Fragment
+    // f's word sits 64f bytes after fragment 0's.  Rows past M or N read some
+    // other finite word or zero (out of range): they only meet zero operands and
+    // their outputs are never stored.
+    static_assert(KIND != KIND_FP8 || T::TN <= 128, "one FP8 B scale block per wave");
+    constexpr int NSB = KIND == KIND_FP8 ? 1 : FN;   // B scale words per lane per packed row
+    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(
+        args.sfa, (uint32_t)(2 * ((int64_t)(args.kp_count - 1) * args.ld_sfa + args.M)));
+    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(
+        sfb, (uint32_t)(2 * ((int64_t)(args.kp_count - 1) * args.ld_sfb + args.sfb_rows)));
+    uint32_t sa_voff = 2u * (uint32_t)(m0 + wm * T::TM + l32);
+    asm volatile("" : "+v"(sa_voff));
+    uint32_t sb_voff = KIND == KIND_FP8 ? 2u * (uint32_t)((n0 + wn * T::TN) / 128)
+                                        : 2u * (uint32_t)(n0 + wn * T::TN + l32);
+    asm volatile("" : "+v"(sb_voff));
+    // Raw scale words of stage kt (packed int16, not decoded yet).
+    //   FP8: K-block kt*SB/128, held in packed row kb/2, byte kb%2.
+    //   FP4: lane group lg needs K-blocks kt*NC + (NC/2)*lg + j (j < NC/2), the
+    //        packed rows kt*NC/2 + (NC/4)*lg + w for w < NC/4.
+    auto load_scales = [&](int kt, uint16_t (&ra_)[FM][SW > 0 ? SW : 1],
+                           uint16_t (&rb_)[NSB][SW > 0 ? SW : 1]) {
+      if constexpr (KIND != KIND_BF16) {
 #pragma unroll
-    for (int f = 0; f < T::FM; ++f) {
-      int m = m0 + wm * T::TM + 32 * f + l32;
-      sa_row[f] = m < args.M ? m : args.M - 1;
-    }
+        for (int w = 0; w < SW; ++w) {
+          int kp = KIND == KIND_FP8 ? (kt * SB / 128) >> 1 : kt * (NC / 2) + (NC / 4) * lg + w;
+          kp = kp < args.kp_count ? kp : args.kp_count - 1;
+          const uint32_t va = sa_voff + 2u * (uint32_t)(kp * args.ld_sfa);
+          const uint32_t vb = sb_voff + 2u * (uint32_t)(kp * args.ld_sfb);
 #pragma unroll
-    for (int f = 0; f < T::FN; ++f) {
-      int n = n0 + wn * T::TN + 32 * f + l32;
-      n = n < args.N ? n : args.N - 1;
-      sb_row[f] = KIND == KIND_FP8 ? n / 128 : n;
-    }
-    // FP8: one byte per stage (K-block kt).  FP4: four bytes per stage for lane
-    // group lg (K-blocks 8kt + 4lg + s, s = 0..3), assembled from two packed words.
-    auto load_scales = [&](int kt, uint32_t* va, uint32_t* vb) {
+          for (int f = 0; f < FM; ++f)
+            ra_[f][w] = __builtin_amdgcn_raw_buffer_load_b16(rsa, va + 64 * f, 0, 0);
+#pragma unroll
+          for (int f = 0; f < NSB; ++f)
+            rb_[f][w] = __builtin_amdgcn_raw_buffer_load_b16(rsb, vb + 64 * f, 0, 0);
+        }
+      }
+    };
+    // Decoded per-lane scale operand of stage kt.  FP8: the K-block's byte in
+    // bits 0..7.  FP4: k-step j's byte in byte j.  (The raw words stay 16-bit
+    // until here, so nothing touches a load's result before the barrier that
+    // waits for it.)
+    auto decode_scales = [&](int kt, const uint16_t (&ra_)[FM][SW > 0 ? SW : 1],
+                             const uint16_t (&rb_)[NSB][SW > 0 ? SW : 1], uint32_t (&sa)[FM],
+                             uint32_t (&sb)[FN]) {
       if constexpr (KIND == KIND_FP8) {
-        const int64_t kp = kt >> 1;
-        const int sh = (kt & 1) * 8;
+        const int sh = ((kt * SB / 128) & 1) * 8;
 #pragma unroll
-        for (int f = 0; f < T::FM; ++f)
-          va[f] = ((uint32_t)(uint16_t)args.sfa[kp * args.ld_sfa + sa_row[f]] >> sh) & 0xFF;
+        for (int f = 0; f < FM; ++f) sa[f] = ((uint32_t)ra_[f][0] >> sh) & 0xFF;
 #pragma unroll
-        for (int f = 0; f < T::FN; ++f)
-          vb[f] = ((uint32_t)(uint16_t)sfb[kp * args.ld_sfb + sb_row[f]] >> sh) & 0xFF;
+        for (int f = 0; f < FN; ++f) sb[f] = ((uint32_t)rb_[0][0] >> sh) & 0xFF;
       } else if constexpr (KIND == KIND_FP4) {
-        int kp0 = 4 * kt + 2 * lg, kp1 = kp0 + 1;
-        kp0 = kp0 < args.kp_count ? kp0 : args.kp_count - 1;
-        kp1 = kp1 < args.kp_count ? kp1 : args.kp_count - 1;
 #pragma unroll
-        for (int f = 0; f < T::FM; ++f)
-          va[f] = (uint32_t)(uint16_t)args.sfa[(int64_t)kp0 * args.ld_sfa + sa_row[f]] |
-                  ((uint32_t)(uint16_t)args.sfa[(int64_t)kp1 * args.ld_sfa + sa_row[f]] << 16);
+        for (int f = 0; f < FM; ++f)
+          sa[f] = SW == 2 ? ((uint32_t)ra_[f][0] | ((uint32_t)ra_[f][SW - 1] << 16)) : (uint32_t)ra_[f][0];
 #pragma unroll
-        for (int f = 0; f < T::FN; ++f)
-          vb[f] = (uint32_t)(uint16_t)sfb[(int64_t)kp0 * args.ld_sfb + sb_row[f]] |
-                  ((uint32_t)(uint16_t)sfb[(int64_t)kp1 * args.ld_sfb + sb_row[f]] << 16);
+        for (int f = 0; f < FN; ++f)
+          sb[f] = SW == 2 ? ((uint32_t)rb_[f][0] | ((uint32_t)rb_[f][SW - 1] << 16)) : (uint32_t)rb_[f][0];
       }
     };
 
-    f32x16_t acc[T::FM][T::FN];
+    // Fragment registers, double-buffered across k-steps.
+    typedef typename std::conditional<KIND == KIND_BF16, bf16x8_t, i32x8_t>::type frag_t;
+    frag_t fa[2][FM], fb[2][FN];
+    auto read_frags = [&](int buf, int j, frag_t (&xa)[FM], frag_t (&xb)[FN]) {
+      const uint8_t* base = smem + buf * T::STAGE_BYTES;
 #pragma unroll
-    for (int a = 0; a < T::FM; ++a)
+      for (int f = 0; f < FM; ++f) {
+        const uint8_t* p0 = base + a_rd[j][0] + 32 * SB * f;
+        if constexpr (KIND == KIND_BF16) {
+          xa[f] = *(const bf16x8_t*)p0;
+        } else if constexpr (KIND == KIND_FP8) {
+          const i32x4_t lo = *(const i32x4_t*)p0;
+          const i32x4_t hi = *(const i32x4_t*)(base + a_rd[j][RPF - 1] + 32 * SB * f);
+          xa[f] = (i32x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        } else {
+          const i32x4_t v = *(const i32x4_t*)p0;
+          xa[f] = (i32x8_t){v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+        }
+      }
 #pragma unroll
-      for (int b = 0; b < T::FN; ++b)
+      for (int f = 0; f < FN; ++f) {
+        const uint8_t* p0 = base + b_rd[j][0] + 32 * SB * f;
+        if constexpr (KIND == KIND_BF16) {
+          xb[f] = *(const bf16x8_t*)p0;
+        } else if constexpr (KIND == KIND_FP8) {
+          const i32x4_t lo = *(const i32x4_t*)p0;
+          const i32x4_t hi = *(const i32x4_t*)(base + b_rd[j][RPF - 1] + 32 * SB * f);
+          xb[f] = (i32x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        } else {
+          const i32x4_t v = *(const i32x4_t*)p0;
+          xb[f] = (i32x8_t){v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+        }
+      }
+    };
+
+    f32x16_t acc[FM][FN];
+#pragma unroll
+    for (int a = 0; a < FM; ++a)
+#pragma unroll
+      for (int b = 0; b < FN; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-    uint32_t sa_cur[T::FM], sb_cur[T::FN], sa_nxt[T::FM], sb_nxt[T::FN];
-    if (args.nk > 0) {
-      issue_stage(0, 0);
-      load_scales(0, sa_cur, sb_cur);
-    }
+    // One k-step's MFMAs: acc += A_frag x B_frag for every fragment pair.
+    auto mfmas = [&](auto jc, const frag_t (&xa)[FM], const frag_t (&xb)[FN], const uint32_t (&sa)[FM],
+                     const uint32_t (&sb)[FN]) {
+      constexpr int j = decltype(jc)::value;
+#pragma unroll
+      for (int a = 0; a < FM; ++a)
+#pragma unroll
+        for (int b = 0; b < FN; ++b) {
+          if constexpr (KIND == KIND_BF16)
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb[b], xa[a], acc[a][b], 0, 0, 0);
+          else if constexpr (KIND == KIND_FP8)
+            acc[a][b] = mfma_scaled<0, 0>(xb[b], xa[a], acc[a][b], sb[b], sa[a]);
+          else
+            acc[a][b] = mfma_scaled<4, j>(xb[b], xa[a], acc[a][b], sb[b], sa[a]);
+        }
+    };
+
+    // Raw scale words, one register set per ring slot (indexed by the stage's
+    // buffer, a compile-time value in the unrolled loop below).
+    uint16_t rs_a[NS][FM][SW > 0 ? SW : 1] = {}, rs_b[NS][NSB][SW > 0 ? SW : 1] = {};
+    uint32_t sa_cur[FM] = {}, sb_cur[FN] = {};
+
+    // Prologue: the previous tile's LDS reads are over once every wave is here;
+    // then stages 0 .. NS-1 are put in flight and stage 0 is waited for.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    [&]<int... bs>(std::integer_sequence<int, bs...>) {
+      ((load_scales(bs < nk ? bs : 0, rs_a[bs], rs_b[bs]), issue_stage(bs, bs)), ...);
+    }(std::make_integer_sequence<int, NS>{});
+    wait_vm_lds<(NS - 1) * T::N_DMA>();
+    ring_barrier();
+    decode_scales(0, rs_a[0], rs_b[0], sa_cur, sb_cur);
+    read_frags(0, 0, fa[0], fb[0]);
 
-    const int a_row0 = wm * T::TM + l32;   // first tile row of this lane's A fragments
-    const int b_row0 = wn * T::TN + l32;
-
-    for (int kt = 0; kt < args.nk; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < args.nk) {
-        issue_stage(kt + 1, buf ^ 1);
-        load_scales(kt + 1, sa_nxt, sb_nxt);
-      }
-      const uint8_t* sA = smem + buf * T::STAGE_BYTES;
-      const uint8_t* sB = sA + BM * 128;
-
-      if constexpr (KIND == KIND_BF16) {
-        // 4 k-steps of 16; lane group lg takes chunk 2s + lg.
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          bf16x8_t fa[T::FM], fb[T::FN];
-#pragma unroll
-          for (int f = 0; f < T::FM; ++f)
-            fa[f] = *(const bf16x8_t*)(sA + lds_off(a_row0 + 32 * f, 2 * s + lg));
-#pragma unroll
-          for (int f = 0; f < T::FN; ++f)
-            fb[f] = *(const bf16x8_t*)(sB + lds_off(b_row0 + 32 * f, 2 * s + lg));
-#pragma unroll
-          for (int a = 0; a < T::FM; ++a)
-#pragma unroll
-            for (int b = 0; b < T::FN; ++b)
-              acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[b], fa[a], acc[a][b], 0, 0, 0);
+    // One stage.  Every stage runs the same code: after the last real one, the
+    // barrier, the copies (all out of range, so no memory traffic), the extra
+    // MFMAs on zero operands and the next-stage reads are dead work, which keeps
+    // the loop free of branches around the MFMAs.
+    auto stage = [&](auto bufc, int s) {
+      constexpr int buf = decltype(bufc)::value;
+      constexpr int nbuf = (buf + 1) % NS;
+      auto body = [&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        // fragment register set of this k-step: k-steps alternate sets across
+        // stage boundaries too (a round of NS stages has an even number of them)
+        constexpr int cu = (buf * J + j) & 1, nx = cu ^ 1;
+        if constexpr (j + 1 < J) {
+          read_frags(buf, j + 1, fa[nx], fb[nx]);
+          mfmas(jc, fa[cu], fb[cu], sa_cur, sb_cur);
+          interleave<FM * FN, (FM + FN) * RPF, 0>();
+          __builtin_amdgcn_sched_barrier(0);
+        } else {
+          // Stage s+1 has landed once at most NS-2 stages of this wave's copies
+          // are outstanding and every wave has passed the barrier; every wave has
+          // also finished reading buffer `buf`, which now takes stage s+NS.
+          wait_vm_lds<(NS - 2) * T::N_DMA>();
+          ring_barrier();
+          load_scales(s + NS < nk ? s + NS : 0, rs_a[buf], rs_b[buf]);
+          issue_stage(s + NS, buf);
+          read_frags(nbuf, 0, fa[nx], fb[nx]);
+          mfmas(jc, fa[cu], fb[cu], sa_cur, sb_cur);
+          interleave<FM * FN, (FM + FN) * RPF, T::VMEM_PER_STAGE>();
+          __builtin_amdgcn_sched_barrier(0);
+          decode_scales(s + 1, rs_a[nbuf], rs_b[nbuf], sa_cur, sb_cur);
         }
-      } else if constexpr (KIND == KIND_FP8) {
-        // 2 k-steps of 64; lane group lg takes chunks 4s + 2lg and 4s + 2lg + 1.
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          i32x8_t fa[T::FM], fb[T::FN];
-#pragma unroll
-          for (int f = 0; f < T::FM; ++f) {
-            const i32x4_t lo = *(const i32x4_t*)(sA + lds_off(a_row0 + 32 * f, 4 * s + 2 * lg));
-            const i32x4_t hi = *(const i32x4_t*)(sA + lds_off(a_row0 + 32 * f, 4 * s + 2 * lg + 1));
-            fa[f] = (i32x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          }
-#pragma unroll
-          for (int f = 0; f < T::FN; ++f) {
-            const i32x4_t lo = *(const i32x4_t*)(sB + lds_off(b_row0 + 32 * f, 4 * s + 2 * lg));
-            const i32x4_t hi = *(const i32x4_t*)(sB + lds_off(b_row0 + 32 * f, 4 * s + 2 * lg + 1));
-            fb[f] = (i32x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          }
-#pragma unroll
-          for (int a = 0; a < T::FM; ++a)
-#pragma unroll
-            for (int b = 0; b < T::FN; ++b)
-              acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  fb[b], fa[a], acc[a][b], 0, 0, 0, (int)sb_cur[b], 0, (int)sa_cur[a]);
-        }
-      } else {
-        // FP4: 4 k-steps of 64; lane group lg takes chunk 4lg + s = K-block 8kt + 4lg + s,
-        // whose scale is byte s of the lane's assembled scale word.
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          i32x8_t fa[T::FM], fb[T::FN];
-#pragma unroll
-          for (int f = 0; f < T::FM; ++f) {
-            const i32x4_t v = *(const i32x4_t*)(sA + lds_off(a_row0 + 32 * f, 4 * lg + s));
-            fa[f] = (i32x8_t){v[0], v[1], v[2], v[3], 0, 0, 0, 0};
-          }
-#pragma unroll
-          for (int f = 0; f < T::FN; ++f) {
-            const i32x4_t v = *(const i32x4_t*)(sB + lds_off(b_row0 + 32 * f, 4 * lg + s));
-            fb[f] = (i32x8_t){v[0], v[1], v[2], v[3], 0, 0, 0, 0};
-          }
-#pragma unroll
-          for (int a = 0; a < T::FM; ++a)
-#pragma unroll
-            for (int b = 0; b < T::FN; ++b)
-              acc[a][b] = mfma_fp4_sel(s, fb[b], fa[a], acc[a][b], sb_cur[b], sa_cur[a]);
-        }
-      }
-
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if constexpr (KIND != KIND_BF16) {
-#pragma unroll
-        for (int f = 0; f < T::FM; ++f) sa_cur[f] = sa_nxt[f];
-#pragma unroll
-        for (int f = 0; f < T::FN; ++f) sb_cur[f] = sb_nxt[f];
-      }
+      };
+      [&]<int... js>(std::integer_sequence<int, js...>) {
+        (body(std::integral_constant<int, js>{}), ...);
+      }(std::make_integer_sequence<int, J>{});
+    };
+    for (int s = 0; s < nk_pad; s += NS) {
+      [&]<int... bs>(std::integer_sequence<int, bs...>) {
+        (stage(std::integral_constant<int, bs>{}, s + bs), ...);
+      }(std::make_integer_sequence<int, NS>{});
     }
 
     // Epilogue.  MFMA operands were (B fragment, A fragment), so accumulator
     // register r of lane l holds D[m][n] with m = l%32 and
     // n = 8*(r/4) + 4*(l/32) + r%4: four consecutive columns per register quad.
 #pragma unroll
-    for (int a = 0; a < T::FM; ++a) {
+    for (int a = 0; a < FM; ++a) {
       const int m = m0 + wm * T::TM + 32 * a + l32;
       if (m >= m_end) continue;
       uint16_t* drow = args.D + (int64_t)m * args.ldd;
 #pragma unroll
-      for (int b = 0; b < T::FN; ++b) {
+      for (int b = 0; b < FN; ++b) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int n = n0 + wn * T::TN + 32 * b + 8 * q + 4 * lg;
