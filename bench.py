@@ -232,6 +232,9 @@ def main():
     ap.add_argument("--cold-samples", type=int, default=10)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle time for cpu_baseline (0 disables it)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 512 MiB device copy three times (the reference "
+                         "dispatch that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -246,6 +249,13 @@ def main():
         sys.exit(1)
     bsg.lib()   # fails loudly if the HIP library is missing
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        src = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     kinds = [k.strip() for k in args.dtypes.split(",") if k.strip()]
     if "bf16" not in kinds:
         kinds = ["bf16"] + kinds
