@@ -44,10 +44,10 @@ PEAK = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0, "grouped": 5000.0}
 PAGES_BF16_TFLOPS = 431.0
 
 KERNEL_NAME = {
-    "bf16": "gemm_kernel<0, 256, 256, 2, 2, 128, 2, false>",
-    "fp8": "gemm_kernel<1, 256, 256, 2, 2, 128, 2, false>",
-    "fp4": "gemm_kernel<2, 256, 256, 2, 2, 64, 4, false>",
-    "grouped": "gemm_kernel<1, 128, 512, 1, 4, 128, 2, true>",
+    "bf16": "gemm_kernel<0, 256, 256, 2, 2, 64, 5, 1, false>",
+    "fp8": "gemm_kernel<1, 256, 256, 2, 2, 64, 5, 1, false>",
+    "fp4": "gemm_kernel<2, 256, 256, 2, 2, 64, 5, 1, false>",
+    "grouped": "gemm_kernel<1, 128, 512, 1, 4, 128, 2, 0, true>",
 }
 
 

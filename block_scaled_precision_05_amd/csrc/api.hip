@@ -54,12 +54,12 @@ __global__ void unpack_kernel(const int16_t* __restrict__ packed, int64_t mn, in
 // requests a CU keeps in flight, so full 128-byte lines per row (two 64 KiB
 // stages) beat a deeper ring of half lines for BF16 and FP8; FP4, with four times
 // the MFMA rate per byte, prefers the deeper ring of four 32 KiB stages.
-#define BSG_BF16_CFG 256, 256, 2, 2, 128, 2
-#define BSG_FP8_CFG 256, 256, 2, 2, 128, 2
-#define BSG_FP4_CFG 256, 256, 2, 2, 64, 4
+#define BSG_BF16_CFG 256, 256, 2, 2, 64, 5, 1
+#define BSG_FP8_CFG 256, 256, 2, 2, 64, 5, 1
+#define BSG_FP4_CFG 256, 256, 2, 2, 64, 5, 1
 // Grouped: 128-row tiles so 128-aligned experts waste no rows; 1x4 waves of
 // 128x128 over a 512-wide N tile; two 80 KiB stages (the whole LDS).
-#define BSG_GROUPED_CFG 128, 512, 1, 4, 128, 2
+#define BSG_GROUPED_CFG 128, 512, 1, 4, 128, 2, 0
 
 static int g_num_cus[64];
 
@@ -75,9 +75,9 @@ static int num_cus() {
   return g_num_cus[dev];
 }
 
-template <int KIND, int BM, int BN, int WM, int WN, int SB, int NS, bool GROUPED>
+template <int KIND, int BM, int BN, int WM, int WN, int SB, int NS, int PR, bool GROUPED>
 static int launch(GemmArgs a, hipStream_t stream) {
-  using T = GemmTile<KIND, BM, BN, WM, WN, SB, NS>;
+  using T = GemmTile<KIND, BM, BN, WM, WN, SB, NS, PR>;
   a.d_vec = (((uintptr_t)a.D & 7) == 0 && (a.ldd % 4) == 0) ? 1 : 0;
   a.tiles_m = (a.M + BM - 1) / BM;
   a.tiles_n = (a.N + BN - 1) / BN;
@@ -90,7 +90,7 @@ static int launch(GemmArgs a, hipStream_t stream) {
     grid = (int)(tiles < num_cus() ? tiles : num_cus());
   }
   (void)hipGetLastError();
-  hipLaunchKernelGGL((gemm_kernel<KIND, BM, BN, WM, WN, SB, NS, GROUPED>), dim3(grid), dim3(T::NT), 0,
+  hipLaunchKernelGGL((gemm_kernel<KIND, BM, BN, WM, WN, SB, NS, PR, GROUPED>), dim3(grid), dim3(T::NT), 0,
                      stream, a);
   return hipGetLastError() == hipSuccess ? BSG_OK : BSG_ERR_HIP;
 }

@@ -103,9 +103,17 @@ __device__ __forceinline__ f32x16_t mfma_scaled(i32x8_t b, i32x8_t a, f32x16_t c
 //   BM x BN   workgroup tile, WM x WN waves (one per SIMD), each wave TM x TN made
 //             of 32x32 MFMA fragments (FM x FN of them);
 //   SB        bytes of K per tile row per stage (64 or 128): 16-byte chunks NC;
-//   NS        LDS stages in the ring; the copy of a stage is issued NS-1 stages
-//             before its data is read.
-template <int KIND, int BM, int BN, int WM, int WN, int SB, int NS>
+//   NS        LDS stages in the ring;
+//   PR        0: the copy of stage s+NS is issued at the barrier of stage s, into
+//             the buffer stage s just released (NS-1 stages ahead);
+//             1 (64-byte stages only): stages are copied in pairs, the two 64-byte
+//             halves of every 128-byte line back to back, so each line costs the
+//             memory system one request.  A pair (t, t+1) starts at the barrier of
+//             stage t-NS+1, which frees the buffers of stages t-NS and t-NS+1, and
+//             its copies are spread over the next 2J k-steps (one chunk per
+//             k-step): a copy instruction waits in the address unit, and in-order
+//             issue makes the MFMAs behind it wait too, so copies must trickle.
+template <int KIND, int BM, int BN, int WM, int WN, int SB, int NS, int PR>
 struct GemmTile {
   static constexpr int NW = WM * WN;
   static constexpr int NT = NW * 64;
@@ -137,7 +145,70 @@ struct GemmTile {
                 "rows must split evenly over waves");
   static_assert(LDS_BYTES <= 163840, "the ring must fit in LDS");
   static_assert((NS - 1) * N_DMA <= 63, "outstanding copies must fit the vmcnt counter");
-  static_assert((NS * J) % 2 == 0, "a round of the ring must hold an even number of k-steps");
+  static_assert(PR == 0 || SB == 64, "paired copies fetch the two halves of 128-byte lines");
+  static_assert(PR == 0 || NS >= 3, "a pair needs two free buffers besides the one in use");
+  // stages per unrolled round: buffer index and pair phase are compile-time
+  static constexpr int U = PR ? (NS % 2 ? 2 * NS : NS) : NS;
+  static_assert((U * J) % 2 == 0, "a round of the ring must hold an even number of k-steps");
+  static constexpr int pmod(int x, int m) { return ((x % m) + m) % m; }
+  // Paired issue: chunks per pair, copies of each of the two stages per chunk,
+  // and the parity of the stages whose barrier starts a pair.
+  static constexpr int CH = 2 * J;
+  static constexpr int QPC = N_DMA / CH;
+  static_assert(PR == 0 || N_DMA % CH == 0, "a pair's copies must split into whole chunks");
+  static constexpr int P0 = (NS - 1) % 2;
+  // chunk due at (global) k-step g, and the stage whose barrier started its pair
+  static constexpr int chunk_at(int g) { return pmod(g - (P0 * J + J - 1), 2 * J); }
+  static constexpr int pair_start(int g) { return (g - chunk_at(g) - (J - 1)) / J; }
+  static constexpr int chunk_vmem(int g) { return 2 * QPC + (chunk_at(g) < 2 ? NSC : 0); }
+  // Copies of one wave issued after the last copy of stage st, counted at the
+  // moment the barrier of stage s waits (s = -1: the prologue's wait for stage
+  // 0).  Replays the kernel's issue order: every chunk due at a k-step g < 0 is
+  // issued by the prologue, the rest at their k-steps, the barrier k-step's chunk
+  // after its wait.  Non-paired: stage s+NS is issued whole at the barrier of s.
+  static constexpr int copies_after(int s, int st) {
+    int issued = 0, last = -1;
+    if (!PR) {
+      for (int t = 0; t < NS; ++t)
+        for (int q = 0; q < N_DMA; ++q) { if (t == st) last = issued; ++issued; }
+      for (int b = 0; b <= s; ++b) {
+        if (b == s) return issued - 1 - last;
+        for (int q = 0; q < N_DMA; ++q) { if (b + NS == st) last = issued; ++issued; }
+      }
+      return issued - 1 - last;
+    }
+    auto chunk = [&](int g) {
+      const int c = chunk_at(g), t = pair_start(g) + NS - 1;
+      if (t < 0) return;
+      for (int q = c * QPC; q < (c + 1) * QPC; ++q) {
+        if (t == st) last = issued;
+        ++issued;
+        if (t + 1 == st) last = issued;
+        ++issued;
+      }
+    };
+    for (int g = -(NS + 2) * J; g < 0; ++g) chunk(g);
+    if (s < 0) return issued - 1 - last;
+    for (int g = 0;; ++g) {
+      if (g % J == J - 1 && g / J == s) return issued - 1 - last;
+      chunk(g);
+    }
+  }
+  // vmcnt for the barrier of stage s (position si in the round): safe for every
+  // round (the first round may differ from the steady state)
+  static constexpr int wait_at(int si) {
+    const int a = copies_after(si, si + 1), b = copies_after(si + U, si + U + 1),
+              c = copies_after(si + 2 * U, si + 2 * U + 1);
+    const int m = a < b ? a : b;
+    return m < c ? m : c;
+  }
+  static constexpr bool steady(int si) {
+    return copies_after(si + U, si + U + 1) == copies_after(si + 2 * U, si + 2 * U + 1);
+  }
+  static constexpr int wait_prologue() { return copies_after(-1, 0); }
+  static_assert(wait_at(0) >= 0 && wait_at(0) <= 63 && wait_at(1) >= 0 && wait_at(1) <= 63 &&
+                    wait_prologue() >= 0 && wait_prologue() <= 63,
+                "vmcnt is 6 bits");
   // LDS position of 16-byte chunk c of tile row r: the chunk is XOR-swizzled with
   // (r / RPS) % NC so that the 16 lanes of one ds_read_b128 phase, reading one
   // logical chunk of 16 consecutive rows, cover all 64 banks exactly once.
@@ -240,9 +311,9 @@ __device__ __forceinline__ void raster(int p, int tiles_m, int tiles_n, int& tm,
 template <int NMFMA, int NDS, int NVMEM, int I>
 __device__ __forceinline__ void interleave_one() {
   constexpr int ds_per = (NDS + NMFMA - 1) / NMFMA;
-  constexpr int vm_per = (NVMEM + NMFMA - 1) / NMFMA;
   constexpr int ds_n = I * ds_per < NDS ? ((NDS - I * ds_per) < ds_per ? NDS - I * ds_per : ds_per) : 0;
-  constexpr int vm_n = I * vm_per < NVMEM ? ((NVMEM - I * vm_per) < vm_per ? NVMEM - I * vm_per : vm_per) : 0;
+  // global loads spread evenly over the MFMAs (front-loaded LDS reads)
+  constexpr int vm_n = (I + 1) * NVMEM / NMFMA - I * NVMEM / NMFMA;
   __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                        // MFMA
   if constexpr (ds_n > 0) __builtin_amdgcn_sched_group_barrier(0x100, ds_n, 0);  // DS read
   if constexpr (vm_n > 0) __builtin_amdgcn_sched_group_barrier(0x020, vm_n, 0);  // VMEM read
@@ -276,10 +347,10 @@ __device__ __forceinline__ void ring_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int KIND, int BM, int BN, int WM, int WN, int SB, int NS, bool GROUPED>
+template <int KIND, int BM, int BN, int WM, int WN, int SB, int NS, int PR, bool GROUPED>
 __global__ __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(const GemmArgs args) {
-  using T = GemmTile<KIND, BM, BN, WM, WN, SB, NS>;
+  using T = GemmTile<KIND, BM, BN, WM, WN, SB, NS, PR>;
   constexpr int FM = T::FM, FN = T::FN, J = T::J, RPF = T::RPF, NC = T::NC, SW = T::SW;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
 
@@ -289,8 +360,8 @@ void gemm_kernel(const GemmArgs args) {
   const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31, lg = lane >> 5;
   const int nk = args.nk;
-  const int nk_pad = (nk + NS - 1) / NS * NS;   // whole rounds of the ring; the extra
-                                                // stages multiply zeros
+  const int nk_pad = (nk + T::U - 1) / T::U * T::U;   // whole rounds of the ring; the
+                                                       // extra stages multiply zeros
 
   int total_tiles;
   GroupCursor cur{0, 0};
@@ -367,28 +438,40 @@ void gemm_kernel(const GemmArgs args) {
     // prologue out of the tile loop and spills them all.
     asm volatile("" : "+v"(a_vbase), "+v"(b_vbase));
 
-    // Copies stage kt into LDS buffer `buf`; a stage past the end copies nothing
-    // (every lane's offset is out of range, so no memory is read).
-    auto issue_stage = [&](int kt, int buf) {
+    // Copy q of stage kt into LDS buffer `buf` (A copies first, then B); a stage
+    // past the end copies nothing (every lane's offset is out of range, so no
+    // memory is read).
+    auto copy_one = [&](int kt, int buf, int q) {
       uint8_t* sA = smem + buf * T::STAGE_BYTES;
       uint8_t* sB = sA + BM * SB;
       const int kb = kt * SB;
       const int k_lim = kt < nk ? args.k_bytes : 0;
       // past the K extent the offset gets bit 31, which no record count reaches
       const uint32_t oob = kb + cp_c16 < k_lim ? 0u : kOOB;
-#pragma unroll
-      for (int q = 0; q < T::A_LOADS; ++q) {
+      if (q < T::A_LOADS) {
         const uint32_t off = (a_vbase + q * a_qstep + kb) | oob;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             ra, (__attribute__((address_space(3))) void*)(sA + T::ROWS_PER_COPY * (q * T::NW + wave) * SB),
             16, off, 0, 0, 0);
-      }
-#pragma unroll
-      for (int q = 0; q < T::B_LOADS; ++q) {
-        const uint32_t off = (b_vbase + q * b_qstep + kb) | oob;
+      } else {
+        const int qb = q - T::A_LOADS;
+        const uint32_t off = (b_vbase + qb * b_qstep + kb) | oob;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rb, (__attribute__((address_space(3))) void*)(sB + T::ROWS_PER_COPY * (q * T::NW + wave) * SB),
+            rb, (__attribute__((address_space(3))) void*)(sB + T::ROWS_PER_COPY * (qb * T::NW + wave) * SB),
             16, off, 0, 0, 0);
+      }
+    };
+    auto issue_stage = [&](int kt, int buf) {
+#pragma unroll
+      for (int q = 0; q < T::N_DMA; ++q) copy_one(kt, buf, q);
+    };
+    // Chunk c of pair (kt, kt+1): copies c*QPC .. (c+1)*QPC-1 of both stages, the
+    // two halves of every line back to back.
+    auto issue_chunk = [&](int kt, int buf0, int buf1, int c) {
+#pragma unroll
+      for (int q = 0; q < T::QPC; ++q) {
+        copy_one(kt, buf0, c * T::QPC + q);
+        copy_one(kt + 1, buf1, c * T::QPC + q);
       }
     };
 
@@ -520,13 +603,35 @@ void gemm_kernel(const GemmArgs args) {
     uint32_t sa_cur[FM] = {}, sb_cur[FN] = {};
 
     // Prologue: the previous tile's LDS reads are over once every wave is here;
-    // then stages 0 .. NS-1 are put in flight and stage 0 is waited for.
+    // then stages 0 .. T0-1 are put in flight and stage 0 is waited for.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    [&]<int... bs>(std::integer_sequence<int, bs...>) {
-      ((load_scales(bs < nk ? bs : 0, rs_a[bs], rs_b[bs]), issue_stage(bs, bs)), ...);
-    }(std::make_integer_sequence<int, NS>{});
-    wait_vm_lds<(NS - 1) * T::N_DMA>();
+    // Paired copies due at a k-step g: chunk chunk_at(g) of the pair started at
+    // the barrier of stage pair_start(g); chunk 0 also loads the first stage's
+    // scale words, chunk 1 the second's.
+    auto pair_chunk = [&](auto gc, int round) {
+      constexpr int g = decltype(gc)::value;
+      constexpr int c = T::chunk_at(g), tl = T::pair_start(g) + NS - 1;
+      constexpr int b0 = T::pmod(tl, NS), b1 = T::pmod(tl + 1, NS);
+      const int t = round + tl;
+      if constexpr (c == 0) load_scales(t < nk ? t : 0, rs_a[b0], rs_b[b0]);
+      if constexpr (c == 1) load_scales(t + 1 < nk ? t + 1 : 0, rs_a[b1], rs_b[b1]);
+      issue_chunk(t, b0, b1, c);
+    };
+    if constexpr (PR) {
+      // every chunk due before k-step 0 (pairs with a first stage t >= 0)
+      [&]<int... gs>(std::integer_sequence<int, gs...>) {
+        ((T::pair_start(gs - (NS + 2) * J) + NS - 1 >= 0
+              ? pair_chunk(std::integral_constant<int, gs - (NS + 2) * J>{}, 0)
+              : void()),
+         ...);
+      }(std::make_integer_sequence<int, (NS + 2) * J>{});
+    } else {
+      [&]<int... bs>(std::integer_sequence<int, bs...>) {
+        ((load_scales(bs < nk ? bs : 0, rs_a[bs], rs_b[bs]), issue_stage(bs, bs)), ...);
+      }(std::make_integer_sequence<int, NS>{});
+    }
+    wait_vm_lds<T::wait_prologue()>();
     ring_barrier();
     decode_scales(0, rs_a[0], rs_b[0], sa_cur, sb_cur);
     read_frags(0, 0, fa[0], fb[0]);
@@ -535,30 +640,41 @@ void gemm_kernel(const GemmArgs args) {
     // barrier, the copies (all out of range, so no memory traffic), the extra
     // MFMAs on zero operands and the next-stage reads are dead work, which keeps
     // the loop free of branches around the MFMAs.
-    auto stage = [&](auto bufc, int s) {
-      constexpr int buf = decltype(bufc)::value;
+    auto stage = [&](auto ic, int s) {
+      constexpr int si = decltype(ic)::value;   // position of the stage in the round
+      constexpr int buf = si % NS;
       constexpr int nbuf = (buf + 1) % NS;
+      static_assert(!PR || T::steady(si), "the copy schedule must repeat every round");
+      const int round = s - si;
       auto body = [&](auto jc) {
         constexpr int j = decltype(jc)::value;
+        constexpr int g = si * J + j;             // k-step index within the round
+        constexpr int nvm = PR ? T::chunk_vmem(g) : (j + 1 < J ? 0 : T::VMEM_PER_STAGE);
         // fragment register set of this k-step: k-steps alternate sets across
-        // stage boundaries too (a round of NS stages has an even number of them)
-        constexpr int cu = (buf * J + j) & 1, nx = cu ^ 1;
+        // stage boundaries too (a round has an even number of them)
+        constexpr int cu = (si * J + j) & 1, nx = cu ^ 1;
         if constexpr (j + 1 < J) {
           read_frags(buf, j + 1, fa[nx], fb[nx]);
+          if constexpr (PR) pair_chunk(std::integral_constant<int, g>{}, round);
           mfmas(jc, fa[cu], fb[cu], sa_cur, sb_cur);
-          interleave<FM * FN, (FM + FN) * RPF, 0>();
+          interleave<FM * FN, (FM + FN) * RPF, nvm>();
           __builtin_amdgcn_sched_barrier(0);
         } else {
-          // Stage s+1 has landed once at most NS-2 stages of this wave's copies
+          // Stage s+1 has landed once no more than wait_at() of this wave's copies
           // are outstanding and every wave has passed the barrier; every wave has
-          // also finished reading buffer `buf`, which now takes stage s+NS.
-          wait_vm_lds<(NS - 2) * T::N_DMA>();
+          // also finished reading buffer `buf` (copies issued from here on go to
+          // the buffers of stages already consumed).
+          wait_vm_lds<T::wait_at(si)>();
           ring_barrier();
-          load_scales(s + NS < nk ? s + NS : 0, rs_a[buf], rs_b[buf]);
-          issue_stage(s + NS, buf);
+          if constexpr (PR) {
+            pair_chunk(std::integral_constant<int, g>{}, round);
+          } else {
+            load_scales(s + NS < nk ? s + NS : 0, rs_a[buf], rs_b[buf]);
+            issue_stage(s + NS, buf);
+          }
           read_frags(nbuf, 0, fa[nx], fb[nx]);
           mfmas(jc, fa[cu], fb[cu], sa_cur, sb_cur);
-          interleave<FM * FN, (FM + FN) * RPF, T::VMEM_PER_STAGE>();
+          interleave<FM * FN, (FM + FN) * RPF, nvm>();
           __builtin_amdgcn_sched_barrier(0);
           decode_scales(s + 1, rs_a[nbuf], rs_b[nbuf], sa_cur, sb_cur);
         }
@@ -567,10 +683,10 @@ void gemm_kernel(const GemmArgs args) {
         (body(std::integral_constant<int, js>{}), ...);
       }(std::make_integer_sequence<int, J>{});
     };
-    for (int s = 0; s < nk_pad; s += NS) {
-      [&]<int... bs>(std::integer_sequence<int, bs...>) {
-        (stage(std::integral_constant<int, bs>{}, s + bs), ...);
-      }(std::make_integer_sequence<int, NS>{});
+    for (int s = 0; s < nk_pad; s += T::U) {
+      [&]<int... is>(std::integer_sequence<int, is...>) {
+        (stage(std::integral_constant<int, is>{}, s + is), ...);
+      }(std::make_integer_sequence<int, T::U>{});
     }
 
     // Epilogue.  MFMA operands were (B fragment, A fragment), so accumulator
