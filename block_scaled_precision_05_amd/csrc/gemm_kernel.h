@@ -160,7 +160,13 @@ struct GemmTile {
   // chunk due at (global) k-step g, and the stage whose barrier started its pair
   static constexpr int chunk_at(int g) { return pmod(g - (P0 * J + J - 1), 2 * J); }
   static constexpr int pair_start(int g) { return (g - chunk_at(g) - (J - 1)) / J; }
-  static constexpr int chunk_vmem(int g) { return 2 * QPC + (chunk_at(g) < 2 ? NSC : 0); }
+  // FP8 with paired 64-byte stages: both stages of a pair lie in one 128-wide
+  // K-block, so the pair loads its scale words once (chunk 0) and both stages
+  // decode them from the first stage's register set.
+  static constexpr bool SHARED_SCALES = PR && KIND == KIND_FP8;
+  static constexpr int chunk_vmem(int g) {
+    return 2 * QPC + (chunk_at(g) == 0 || (chunk_at(g) == 1 && !SHARED_SCALES) ? NSC : 0);
+  }
   // Copies of one wave issued after the last copy of stage st, counted at the
   // moment the barrier of stage s waits (s = -1: the prologue's wait for stage
   // 0).  Replays the kernel's issue order: every chunk due at a k-step g < 0 is
@@ -615,7 +621,7 @@ void gemm_kernel(const GemmArgs args) {
       constexpr int b0 = T::pmod(tl, NS), b1 = T::pmod(tl + 1, NS);
       const int t = round + tl;
       if constexpr (c == 0) load_scales(t < nk ? t : 0, rs_a[b0], rs_b[b0]);
-      if constexpr (c == 1) load_scales(t + 1 < nk ? t + 1 : 0, rs_a[b1], rs_b[b1]);
+      if constexpr (c == 1 && !T::SHARED_SCALES) load_scales(t + 1 < nk ? t + 1 : 0, rs_a[b1], rs_b[b1]);
       issue_chunk(t, b0, b1, c);
     };
     if constexpr (PR) {
@@ -676,7 +682,9 @@ void gemm_kernel(const GemmArgs args) {
           mfmas(jc, fa[cu], fb[cu], sa_cur, sb_cur);
           interleave<FM * FN, (FM + FN) * RPF, nvm>();
           __builtin_amdgcn_sched_barrier(0);
-          decode_scales(s + 1, rs_a[nbuf], rs_b[nbuf], sa_cur, sb_cur);
+          // (shared scales: stage s+1 reads the set of its pair's first stage)
+          constexpr int sbuf = T::SHARED_SCALES ? T::pmod(((si + 1) & ~1), NS) : nbuf;
+          decode_scales(s + 1, rs_a[sbuf], rs_b[sbuf], sa_cur, sb_cur);
         }
       };
       [&]<int... js>(std::integer_sequence<int, js...>) {
