@@ -50,16 +50,18 @@ __global__ void unpack_kernel(const int16_t* __restrict__ packed, int64_t mn, in
 // Tile configurations.
 // ---------------------------------------------------------------------------
 // Dense: 256x256 workgroup tile, 2x2 waves of 128x128 (16 fragments of 32x32 per
-// wave, 256 fp32 accumulators per lane).  The copy into LDS is bound by how many
-// requests a CU keeps in flight, so full 128-byte lines per row (two 64 KiB
-// stages) beat a deeper ring of half lines for BF16 and FP8; FP4, with four times
-// the MFMA rate per byte, prefers the deeper ring of four 32 KiB stages.
+// wave, 256 fp32 accumulators per lane), a ring of five 64-byte stages (32 KiB
+// each) copied in pairs.  The copies are limited by the requests a CU keeps in
+// flight and by the issue cost of the copy instructions (spread over the MFMAs);
+// the MFMAs by the chip's power limit.  256x224 tiles (exactly two per CU at
+// 4096x7168) measured no faster: with the chip power-bound, the CUs left idle in
+// the last wave of 256x256 tiles let the others clock higher.
 #define BSG_BF16_CFG 256, 256, 2, 2, 64, 5, 1
 #define BSG_FP8_CFG 256, 256, 2, 2, 64, 5, 1
 #define BSG_FP4_CFG 256, 256, 2, 2, 64, 5, 1
 // Grouped: 128-row tiles so 128-aligned experts waste no rows; 1x4 waves of
-// 128x128 over a 512-wide N tile; two 80 KiB stages (the whole LDS).
-#define BSG_GROUPED_CFG 128, 512, 1, 4, 128, 2, 0
+// 128x128 over a 512-wide N tile; a ring of four 40 KiB stages (the whole LDS).
+#define BSG_GROUPED_CFG 128, 512, 1, 4, 64, 4, 1
 
 static int g_num_cus[64];
 

@@ -7,18 +7,22 @@
 //   VGPRs --v_mfma_f32_32x32x16_bf16 / v_mfma_scale_f32_32x32x64_f8f6f4--> fp32 accumulators
 //   accumulators --v_cvt to bf16 (round to nearest even)--> D
 //
-// Software pipeline.  A stage is 128 bytes of K for every row of the tile, split
-// into J k-steps of one MFMA per (A fragment, B fragment) pair.  Fragments are
-// double-buffered in registers: the LDS reads of k-step j+1 are interleaved with
-// the MFMAs of k-step j.  The single workgroup barrier of a stage sits before its
-// last k-step, whose fragments are already in registers, so the matrix cores keep
-// working while the waves meet; right after it the copy of stage s+2 into the LDS
-// buffer just released is issued, together with the first fragment reads of stage
-// s+1.  Each copy therefore has one full stage of MFMA time to land.  This is the
-// MI355X counterpart of the staged, double-buffered operand pipeline with ready
-// signals that the pages describe for the other accelerator ("DeepGEMM-Ascend
-// cobre quantas operacoes no Ascend 950?", sections "O que muda de fato entre CUDA
-// e o Huawei Ascend?" and "Reuso de operandos e pipelining na pratica").
+// Software pipeline.  A stage is SB bytes of K for every row of the tile, split
+// into J k-steps of one MFMA per (A fragment, B fragment) pair; the LDS holds a
+// ring of NS stages.  Fragments are double-buffered in registers: the LDS reads
+// of k-step j+1 are interleaved with the MFMAs of k-step j.  The single
+// workgroup barrier of a stage sits before its last k-step, whose fragments are
+// already in registers, so the matrix cores keep working while the waves meet;
+// it waits (explicit vmcnt) only for the copies of the next stage, never for the
+// whole ring.  Copies into the buffers that barrier released start right after
+// it and trickle out between the MFMAs of the following k-steps, so NS-1 or
+// NS-2 stages of MFMA time cover each copy.  With 64-byte stages the copies go
+// in pairs of stages, so the two halves of each 128-byte line are requested back
+// to back.  This is the MI355X counterpart of the staged, multi-buffered operand
+// pipeline with ready signals that the pages describe for the other accelerator
+// ("DeepGEMM-Ascend cobre quantas operacoes no Ascend 950?", sections "O que
+// muda de fato entre CUDA e o Huawei Ascend?" and "Reuso de operandos e
+// pipelining na pratica").
 //
 // Scale handling (FP8 and FP4): the UE8M0 bytes go straight into the scaled
 // MFMA's per-lane scale operand, so promotion by 2^(e-127) happens inside the
@@ -26,7 +30,7 @@
 // is exactly one K-block, so every MFMA of a stage sees a row-uniform scale.
 // FP4 uses one byte per (row, 32-K block): each lane's 16-byte operand is
 // exactly one K-block and carries that block's byte.  Scale words are loaded
-// from global memory two stages ahead, together with the tile copy, and are only
+// from global memory together with the tile copy of their stage, and are only
 // decoded after the barrier that waits for that copy, so they never add a wait.
 #pragma once
 
@@ -65,7 +69,7 @@ struct GemmArgs {
   int32_t N;
   int32_t K;                // logical K (elements)
   int32_t k_bytes;          // bytes of K per row
-  int32_t nk;               // K stages (128 bytes of K each)
+  int32_t nk;               // K stages (SB bytes of K each)
   int32_t kp_count;         // rows of the packed scale arrays, ceil(Kb/2)
   int32_t sfb_rows;         // scale rows of B (ceil(N/128) for FP8, N for FP4)
   int32_t tiles_m;          // dense: M tiles
@@ -128,21 +132,31 @@ struct GemmTile {
   static constexpr int J = KIND == KIND_FP8 ? NC / 4 : NC / 2;
   static constexpr int RPF = KIND == KIND_FP8 ? 2 : 1;
   static constexpr int STAGE_BYTES = (BM + BN) * SB;
-  static constexpr int LDS_BYTES = NS * STAGE_BYTES;
   static constexpr int ROWS_PER_COPY = 1024 / SB;          // rows of one 1 KiB wave copy
-  static constexpr int A_LOADS = BM / ROWS_PER_COPY / NW;  // wave copies per stage
-  static constexpr int B_LOADS = BN / ROWS_PER_COPY / NW;
+  static constexpr int A_COPIES = BM / ROWS_PER_COPY;      // 1 KiB copies per stage
+  static constexpr int B_COPIES = BN / ROWS_PER_COPY;
+  static constexpr int A_LOADS = (A_COPIES + NW - 1) / NW; // copies per wave per stage
+  static constexpr int B_LOADS = (B_COPIES + NW - 1) / NW;
   static constexpr int N_DMA = A_LOADS + B_LOADS;
+  // When the copies do not split evenly over the waves, the short waves issue an
+  // out-of-range copy into a spare 1 KiB of LDS instead, so every wave issues the
+  // same number of copies and the vmcnt arithmetic holds for all of them.
+  static constexpr bool DUMMY = A_LOADS * NW != A_COPIES || B_LOADS * NW != B_COPIES;
+  static constexpr int LDS_BYTES = NS * STAGE_BYTES + (DUMMY ? 1024 : 0);
+  // FP8 B scales: one 128-row block per wave when the wave's TN rows stay inside
+  // one block, else one word per 32-row fragment.
+  static constexpr bool ONE_B_SCALE = TN <= 128 && 128 % TN == 0 && BN % 128 == 0;
+  static constexpr int NSB = KIND == KIND_FP8 ? (ONE_B_SCALE ? 1 : FN) : FN;
   // packed scale words per lane per fragment per stage: FP8 one (the K-block's
   // pair), FP4 NC/4 (lane group lg takes NC/2 K-blocks of 32)
   static constexpr int SW = KIND == KIND_BF16 ? 0 : (KIND == KIND_FP8 ? 1 : NC / 4);
-  static constexpr int NSC = (FM + (KIND == KIND_FP8 ? 1 : FN)) * SW;
+  static constexpr int NSC = (FM + NSB) * SW;
   static constexpr int VMEM_PER_STAGE = N_DMA + NSC;
   static_assert(SB == 64 || SB == 128, "a stage is 64 or 128 bytes of K per row");
   static_assert(NS >= 2 && NS <= 8, "ring of 2..8 stages");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be made of 32x32 fragments");
-  static_assert((BM / ROWS_PER_COPY) % NW == 0 && (BN / ROWS_PER_COPY) % NW == 0,
-                "rows must split evenly over waves");
+  static_assert(BM % ROWS_PER_COPY == 0 && BN % ROWS_PER_COPY == 0,
+                "tile rows must be whole copies");
   static_assert(LDS_BYTES <= 163840, "the ring must fit in LDS");
   static_assert((NS - 1) * N_DMA <= 63, "outstanding copies must fit the vmcnt counter");
   static_assert(PR == 0 || SB == 64, "paired copies fetch the two halves of 128-byte lines");
@@ -454,16 +468,21 @@ void gemm_kernel(const GemmArgs args) {
       const int k_lim = kt < nk ? args.k_bytes : 0;
       // past the K extent the offset gets bit 31, which no record count reaches
       const uint32_t oob = kb + cp_c16 < k_lim ? 0u : kOOB;
+      uint8_t* const spare = smem + NS * T::STAGE_BYTES;
       if (q < T::A_LOADS) {
-        const uint32_t off = (a_vbase + q * a_qstep + kb) | oob;
+        const int ci = q * T::NW + wave;
+        const bool dummy = T::DUMMY && ci >= T::A_COPIES;
+        const uint32_t off = (a_vbase + q * a_qstep + kb) | oob | (dummy ? kOOB : 0u);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ra, (__attribute__((address_space(3))) void*)(sA + T::ROWS_PER_COPY * (q * T::NW + wave) * SB),
+            ra, (__attribute__((address_space(3))) void*)(dummy ? spare : sA + T::ROWS_PER_COPY * ci * SB),
             16, off, 0, 0, 0);
       } else {
         const int qb = q - T::A_LOADS;
-        const uint32_t off = (b_vbase + qb * b_qstep + kb) | oob;
+        const int ci = qb * T::NW + wave;
+        const bool dummy = T::DUMMY && ci >= T::B_COPIES;
+        const uint32_t off = (b_vbase + qb * b_qstep + kb) | oob | (dummy ? kOOB : 0u);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rb, (__attribute__((address_space(3))) void*)(sB + T::ROWS_PER_COPY * (qb * T::NW + wave) * SB),
+            rb, (__attribute__((address_space(3))) void*)(dummy ? spare : sB + T::ROWS_PER_COPY * ci * SB),
             16, off, 0, 0, 0);
       }
     };
@@ -482,13 +501,13 @@ void gemm_kernel(const GemmArgs args) {
     };
 
     // Scale loads.  Each lane reads the packed words of the rows it feeds to the
-    // MFMAs: A row m0 + wm*TM + 32f + l32 (f < FM); for FP4 B row n likewise; for
-    // FP8 the one 128-row block of B this wave's TN <= 128 rows fall in.  Fragment
-    // f's word sits 64f bytes after fragment 0's.  Rows past M or N read some
-    // other finite word or zero (out of range): they only meet zero operands and
-    // their outputs are never stored.
-    static_assert(KIND != KIND_FP8 || T::TN <= 128, "one FP8 B scale block per wave");
-    constexpr int NSB = KIND == KIND_FP8 ? 1 : FN;   // B scale words per lane per packed row
+    // MFMAs: A row m0 + wm*TM + 32f + l32 (f < FM), whose word sits 64f bytes after
+    // fragment 0's; for FP4 B row n likewise; for FP8 the 128-row block of B that
+    // holds the wave's rows (one block) or fragment f's 32 rows.  Rows past M or N
+    // read some other finite word or zero (out of range): they only meet zero
+    // operands and their outputs are never stored.
+    constexpr int NSB = T::NSB;   // B scale words per lane per packed row
+    const int nrow0 = n0 + wn * T::TN;   // first B row of this wave (uniform)
     const __amdgpu_buffer_rsrc_t rsa = make_rsrc(
         args.sfa, (uint32_t)(2 * ((int64_t)(args.kp_count - 1) * args.ld_sfa + args.M)));
     const __amdgpu_buffer_rsrc_t rsb = make_rsrc(
@@ -515,8 +534,13 @@ void gemm_kernel(const GemmArgs args) {
           for (int f = 0; f < FM; ++f)
             ra_[f][w] = __builtin_amdgcn_raw_buffer_load_b16(rsa, va + 64 * f, 0, 0);
 #pragma unroll
-          for (int f = 0; f < NSB; ++f)
-            rb_[f][w] = __builtin_amdgcn_raw_buffer_load_b16(rsb, vb + 64 * f, 0, 0);
+          for (int f = 0; f < NSB; ++f) {
+            if constexpr (KIND == KIND_FP8 && !T::ONE_B_SCALE)
+              rb_[f][w] = __builtin_amdgcn_raw_buffer_load_b16(
+                  rsb, 2u * (uint32_t)(((nrow0 + 32 * f) >> 7) + kp * args.ld_sfb), 0, 0);
+            else
+              rb_[f][w] = __builtin_amdgcn_raw_buffer_load_b16(rsb, vb + 64 * f, 0, 0);
+          }
         }
       }
     };
@@ -532,7 +556,7 @@ void gemm_kernel(const GemmArgs args) {
 #pragma unroll
         for (int f = 0; f < FM; ++f) sa[f] = ((uint32_t)ra_[f][0] >> sh) & 0xFF;
 #pragma unroll
-        for (int f = 0; f < FN; ++f) sb[f] = ((uint32_t)rb_[0][0] >> sh) & 0xFF;
+        for (int f = 0; f < FN; ++f) sb[f] = ((uint32_t)rb_[T::ONE_B_SCALE ? 0 : f][0] >> sh) & 0xFF;
       } else if constexpr (KIND == KIND_FP4) {
 #pragma unroll
         for (int f = 0; f < FM; ++f)
