@@ -18,6 +18,8 @@ para calculo e comunicacao de IA", section "Resultados de kernel e comunicacao")
   fp8_large     FP8 4096x7168x16384, scales as fp8_mid
   moe_fp8       M-grouped FP8: 256 experts, N=2048, K=7168, Zipf(1.1) routing
   fp4_large     FP4 4096x7168x16384, 1x32 UE8M0 scales on both operands
+  act_large     bf16 activations 4096x16384 (A of the dense shape), to be quantised
+  act_moe       bf16 activations 16384x7168 (the MoE tokens), to be quantised
 
 Value recipes:
   * FP8: for every scale entry an exponent e ~ U{-8..4}; a value is
@@ -30,6 +32,9 @@ Value recipes:
     over 256 experts with popularity p_r ~ r^-1.1 (rank r = 1..256), ranks mapped
     to expert ids by a seeded permutation; every count is padded up to a multiple
     of 128.  Padding rows hold zero codes and scale byte 127.
+  * Activations (bf16, input of the per-token quantiser): x ~ N(0,1) times a
+    per-row power of two 2^U{-6..6}; one column in 64 (a seeded choice) is an
+    outlier channel scaled by 32; the last ``zero_rows`` rows are zero.
 """
 from __future__ import annotations
 
@@ -103,6 +108,19 @@ def fp4_operand(rows: int, K: int, g: torch.Generator, device):
     return packed.contiguous(), sf
 
 
+def activations(rows: int, K: int, seed: int, device="cpu", zero_rows: int = 0) -> torch.Tensor:
+    """bf16 [rows][K] activations (recipe in the module docstring)."""
+    g = _gen(device, seed)
+    x = torch.randn(rows, K, generator=g, device=device, dtype=torch.float32)
+    e = torch.randint(-6, 7, (rows, 1), generator=g, device=device, dtype=torch.int32)
+    x = x * torch.exp2(e.to(torch.float32))
+    hot = torch.rand(K, generator=g, device=device) < (1.0 / 64)
+    x[:, hot] *= 32.0
+    if zero_rows:
+        x[rows - zero_rows:] = 0
+    return x.to(torch.bfloat16)
+
+
 def moe_counts(g: torch.Generator, device, tokens: int = 16384, topk: int = 6,
                experts: int = 256, zipf: float = 1.1):
     """Per-expert routed row counts (int64 [experts])."""
@@ -151,6 +169,8 @@ SHAPES = {
     "moe_fp8": ("grouped_fp8", None, 2048, 7168, 1004),
     "fp4_large": ("fp4", 4096, 7168, 16384, 1005),
     "fp8_large": ("fp8", 4096, 7168, 16384, 1006),
+    "act_large": ("act", 4096, None, 16384, 1007),
+    "act_moe": ("act", 16384, None, 7168, 1008),
 }
 
 
@@ -216,6 +236,10 @@ def make(name: str, device="cpu", seed: int | None = None) -> Workload:
     seed = default_seed if seed is None else seed
     if kind == "grouped_fp8":
         w = grouped(256, N, K, seed, device=device, name=name)
+    elif kind == "act":
+        w = Workload(name, "act", M, 0, K)
+        w.tensors["X"] = activations(M, K, seed, device=device)
+        w.meta["seed"] = seed
     else:
         w = dense(kind, M, N, K, seed, device=device, name=name)
     w.name = name

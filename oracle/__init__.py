@@ -11,8 +11,13 @@ in plain k order.  This module only marshals numpy arrays into it and builds it
 with gcc.  ``oracle.exact`` holds an independent exact-rational brute force for
 tiny shapes.
 
-Parity status of each function (what pins it is in ``tests/test_oracle_pins.py``):
-  decoders, bf16 rounding, pack/unpack, dense BF16/FP8/FP4, grouped FP8: pinned.
+``oracle.quantize`` (numpy, fp64) holds the per-token quantiser: bf16 rows to
+e4m3 or e2m1 codes with UE8M0 block scales.
+
+Parity status of each function (what pins it is in ``tests/test_oracle_pins.py``
+and ``tests/test_quantize_pins.py``):
+  decoders, bf16 rounding, pack/unpack, dense BF16/FP8/FP4, grouped FP8,
+  per-token quantisation: pinned.
 """
 from __future__ import annotations
 
