@@ -1,6 +1,7 @@
 """Benchmark of the block-scaled GEMM library on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--dtypes bf16,fp8,fp4,grouped]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--dtypes bf16,fp8,fp4,grouped,quant_fp8,quant_fp4,quant_fp8_moe]
 
 Workload: D = A * B^T at M=4096, N=7168, K=16384, the dense shape the pages time
 (431 TFLOPS BF16 on the other accelerator: "DeepSeek lanza kernels de DeepGEMM
@@ -18,6 +19,11 @@ dtype's dense MFMA peak.  Each call is also bracketed by HIP events on the
 stream it is launched on; their mean is the launch duration behind `roofline`.
 A cold-L2 variant (a 512 MiB scratch write before each sample, more than the
 MALL plus every XCD's L2) is reported per dtype as `cold_l2_us`.
+
+The per-token quantisers (bf16 activations -> FP8 1x128 or FP4 1x32 codes with
+packed UE8M0 scales) are timed the same way on the dense shape's A (4096x16384)
+and on the MoE tokens (16384x7168), reported in GB/s of algorithmic traffic
+against the 8 TB/s HBM peak.
 
 `cpu_baseline` times the CPU oracle (plain C, fp64) on a bounded row sample of
 the BF16 workload on this host's cores.
@@ -41,6 +47,9 @@ METRIC = "TFLOPS and % of MI355X dense MFMA peak, GEMM 4096×7168×16384 per dty
 
 # MI355X published dense MFMA peaks (TFLOP/s).
 PEAK = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0, "grouped": 5000.0}
+# MI355X published HBM3E bandwidth (GB/s): the bound of the quantisers.
+HBM_PEAK_GBS = 8000.0
+QUANT_KINDS = ("quant_fp8", "quant_fp4", "quant_fp8_moe")
 # The pages' own figure at this shape (other accelerator; context only).
 PAGES_BF16_TFLOPS = 431.0
 
@@ -49,6 +58,9 @@ KERNEL_NAME = {
     "fp8": "gemm_kernel<1, 256, 256, 2, 2, 64, 5, 1, false>",
     "fp4": "gemm_kernel<2, 256, 256, 2, 2, 64, 5, 1, false>",
     "grouped": "gemm_kernel<1, 128, 512, 1, 4, 64, 4, 1, true>",
+    "quant_fp8": "quant_kernel<0, 0>",
+    "quant_fp4": "quant_kernel<1, 0>",
+    "quant_fp8_moe": "quant_kernel<0, 0>",
 }
 
 
@@ -56,12 +68,21 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_sources_sha() -> str:
-    """Hash of the kernel sources with comments and blank space removed, so that
-    counters stay attached to the code they were taken on across comment edits."""
+# Kernel sources behind each measured kind: a change to any of them detaches the
+# committed rocprofv3 counters from the kernel.
+SOURCES = {
+    "gemm": ("gemm_kernel.h", "api.hip"),
+    "quant": ("quant.hip",),
+}
+
+
+def kernel_sources_sha(group: str = "gemm") -> str:
+    """Hash of one group's kernel sources with comments and blank space removed,
+    so that counters stay attached to the code they were taken on across comment
+    edits."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_scaled_precision_05_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in SOURCES[group]:
         with open(os.path.join(csrc, name)) as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -93,10 +114,24 @@ def make_case(kind, dev):
     from block_scaled_precision_05_amd import workloads
 
     name = {"bf16": "bf16_large", "fp8": "fp8_large", "fp4": "fp4_large",
-            "grouped": "moe_fp8"}[kind]
+            "grouped": "moe_fp8", "quant_fp8": "act_large", "quant_fp4": "act_large",
+            "quant_fp8_moe": "act_moe"}[kind]
     w = workloads.make(name, device=dev)
     t = w.tensors
     M, N, K = w.M, w.N, w.K
+    if kind in QUANT_KINDS:
+        X = t["X"]
+        fp4 = kind == "quant_fp4"
+        gk = 32 if fp4 else 128
+        Q = torch.empty(M, K // 2 if fp4 else K, dtype=torch.uint8, device=dev)
+        S = torch.empty((K // gk + 1) // 2, M, dtype=torch.int16, device=dev)
+        fn = bsg.quantize_fp4_per_token if fp4 else bsg.quantize_fp8_per_token
+        call = lambda: fn(X, rule="ceil", out=Q, sf_out=S)
+        nbytes = 2 * M * K + Q.numel() + 2 * S.numel()
+        meta = {"scales": f"1x{gk} UE8M0, rule ceil, packed int16 MN-major",
+                "bytes_per_call": nbytes}
+        meta.update({"M": M, "K": K})
+        return call, 0.0, nbytes, meta
     if kind == "bf16":
         A, B = t["A"], t["B"]
         D = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
@@ -184,6 +219,25 @@ def summarize(kind, r, steps):
     per = sorted(r["per_launch_us"])
     mean_us = statistics.fmean(per)
     med = statistics.median(per)
+    if kind in QUANT_KINDS:
+        gbs = r["min_bytes"] * steps / r["wall_s"] / 1e9
+        out = {
+            "gb_per_s": gbs,
+            "wall_us_per_call": r["wall_s"] * 1e6 / steps,
+            "frac_of_hbm_peak": gbs / HBM_PEAK_GBS,
+            "hbm_peak_gb_per_s": HBM_PEAK_GBS,
+            "launch_us_mean": mean_us,
+            "launch_us_median": med,
+            "launch_us_min": per[0],
+            "gb_per_s_mean_launch": r["min_bytes"] / (mean_us * 1e-6) / 1e9,
+            "kernel": KERNEL_NAME[kind],
+        }
+        if "cold_us" in r:
+            c = statistics.median(sorted(r["cold_us"]))
+            out["cold_l2_us_median"] = c
+            out["cold_l2_gb_per_s"] = r["min_bytes"] / (c * 1e-6) / 1e9
+        out.update(r["meta"])
+        return out
     out = {
         "tflops": r["flops"] * steps / r["wall_s"] / 1e12,
         "wall_ms_per_call": r["wall_s"] * 1e3 / steps,
@@ -235,7 +289,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--dtypes", default="bf16,fp8,fp4,grouped")
+    ap.add_argument("--dtypes", default="bf16,fp8,fp4,grouped,quant_fp8,quant_fp4,quant_fp8_moe")
     ap.add_argument("--cold-samples", type=int, default=10)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle time for cpu_baseline (0 disables it)")
@@ -273,9 +327,14 @@ def main():
         log(f"{kind}: generating inputs and timing {args.warmup}+{args.steps} calls")
         r = time_case(kind, args.steps, args.warmup, dev, args.cold_samples)
         per[kind] = summarize(kind, r, args.steps)
-        log(f"{kind}: {per[kind]['tflops']:.1f} TFLOPS "
-            f"({100 * per[kind]['frac_of_peak']:.1f}% of peak), "
-            f"{per[kind]['launch_us_mean']:.1f} us per launch")
+        if kind in QUANT_KINDS:
+            log(f"{kind}: {per[kind]['gb_per_s']:.0f} GB/s "
+                f"({100 * per[kind]['frac_of_hbm_peak']:.1f}% of HBM peak), "
+                f"{per[kind]['launch_us_mean']:.1f} us per launch")
+        else:
+            log(f"{kind}: {per[kind]['tflops']:.1f} TFLOPS "
+                f"({100 * per[kind]['frac_of_peak']:.1f}% of peak), "
+                f"{per[kind]['launch_us_mean']:.1f} us per launch")
         torch.cuda.empty_cache()
 
     b = per["bf16"]

@@ -12,6 +12,8 @@ if ``libbsg.so`` is missing or cannot be loaded, every call raises.
     P = pack_ue8m0_scales(sf)                   # uint8 [mn, kb] -> int16 [ceil(kb/2), mn]
     sf = unpack_ue8m0_scales(P, mn, kb)
     P = ensure_packed(sf, mn, kb)               # reuse if already packed, else pack
+    Q, P = quantize_fp8_per_token(X)            # bf16 [M,K] -> e4m3 + packed 1x128 scales
+    Q, P = quantize_fp4_per_token(X)            # bf16 [M,K] -> e2m1 (2/byte) + packed 1x32 scales
 """
 from __future__ import annotations
 
@@ -30,6 +32,8 @@ BSG_ERR_UNSUPPORTED_SHAPE = 2
 BSG_ERR_MISALIGNED = 3
 BSG_ERR_HIP = 4
 
+SCALE_RULES = {"ceil": 0, "ocp_mx": 1}
+
 _lock = threading.Lock()
 _lib = None
 
@@ -47,6 +51,8 @@ EXPORTS = {
                            _vp, _i32, _i64, _i64, _i64, _vp],
     "pack_ue8m0_scales": [_vp, _i64, _i64, _i64, _vp, _i64, _vp],
     "unpack_ue8m0_scales": [_vp, _i64, _i64, _i64, _vp, _i64, _vp],
+    "quantize_fp8_per_token": [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i32, _vp],
+    "quantize_fp4_per_token": [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i32, _vp],
 }
 
 
@@ -254,3 +260,36 @@ def ensure_packed(sf: torch.Tensor, mn: int, kb: int, stream=None) -> torch.Tens
     raise TypeError(
         f"scales must be packed int16 [{(kb + 1) // 2}, >={mn}] or UE8M0 bytes [{mn}, {kb}]; "
         f"got {sf.dtype} {tuple(sf.shape)}")
+
+
+def _quantize(fn: str, X, rule, q_cols, gk, out, sf_out, ld_sf, stream):
+    _dev(X, out, sf_out)
+    if X.dtype != torch.bfloat16:
+        raise TypeError("X must be bfloat16")
+    if rule not in SCALE_RULES:
+        raise ValueError(f"rule must be one of {sorted(SCALE_RULES)}")
+    M, K = X.shape
+    kp = (K // gk + 1) // 2
+    ld = M if ld_sf is None else int(ld_sf)
+    Q = torch.empty((M, q_cols(K)), dtype=torch.uint8, device=X.device) if out is None \
+        else _bytes_u8(out)
+    P = torch.empty((kp, ld), dtype=torch.int16, device=X.device) if sf_out is None else sf_out
+    _check(fn, getattr(lib(), fn)(_ptr(X), _mat(X, "X"), _ptr(Q), _mat(Q, "out"), _ptr(P),
+                                  _packed(P, "sf_out"), M, K, SCALE_RULES[rule], _stream(stream)))
+    return Q, P
+
+
+def quantize_fp8_per_token(X, rule: str = "ceil", out=None, sf_out=None, ld_sf=None, stream=None):
+    """bf16 [M, K] -> (e4m3 codes uint8 [M, K], packed int16 scales [ceil(K/256), ld_sf])
+    with one UE8M0 scale per row per 128-wide K-block; ``rule`` is "ceil" (no
+    clipping) or "ocp_mx".  The scales are ready to pass as ``sfa``."""
+    return _quantize("quantize_fp8_per_token", X, rule, lambda K: K, 128, out, sf_out, ld_sf,
+                     stream)
+
+
+def quantize_fp4_per_token(X, rule: str = "ceil", out=None, sf_out=None, ld_sf=None, stream=None):
+    """bf16 [M, K] -> (e2m1 codes uint8 [M, K/2], even K index in the low nibble;
+    packed int16 scales [ceil(K/64), ld_sf]), one UE8M0 scale per row per 32-wide
+    K-block."""
+    return _quantize("quantize_fp4_per_token", X, rule, lambda K: K // 2, 32, out, sf_out, ld_sf,
+                     stream)

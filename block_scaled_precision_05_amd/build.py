@@ -1,4 +1,4 @@
-"""Builds libbsg.so (the C-ABI GEMM library) for gfx950 with hipcc, in-tree."""
+"""Builds libbsg.so (the C-ABI GEMM and quantisation library) for gfx950 with hipcc, in-tree."""
 from __future__ import annotations
 
 import os
@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libbsg.so")
-SOURCES = [os.path.join(HERE, "csrc", "api.hip")]
+SOURCES = [os.path.join(HERE, "csrc", "api.hip"), os.path.join(HERE, "csrc", "quant.hip")]
 HEADERS = [os.path.join(HERE, "csrc", "gemm_kernel.h"), os.path.join(ROOT, "include", "bsg.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -61,6 +61,12 @@ enum bsg_status {
   BSG_ERR_HIP = 4,               /* the HIP runtime reported an error at launch */
 };
 
+/* Scale rules of the per-token quantisers (below). */
+enum bsg_scale_rule {
+  BSG_SCALE_CEIL = 0,   /* smallest power of two that holds the block's amax: nothing clips */
+  BSG_SCALE_OCP_MX = 1, /* OCP Microscaling: 2^(floor(log2 amax) - emax), larger values saturate */
+};
+
 /* Human-readable name of a status code (static storage). */
 const char* bsg_status_string(int status);
 
@@ -129,6 +135,39 @@ int pack_ue8m0_scales(const uint8_t* sf, int64_t mn, int64_t kb, int64_t ld_sf,
 /* Inverse of pack_ue8m0_scales (device kernel on `stream`). */
 int unpack_ue8m0_scales(const int16_t* packed, int64_t mn, int64_t kb, int64_t ld_packed,
                         uint8_t* sf, int64_t ld_sf, void* stream);
+
+/* Per-token quantisation of bf16 rows into the operand formats above, with the
+ * scales written straight into the packed int16, MN-major layout (device kernel
+ * on `stream`).  The pages say operands carry UE8M0 scales that the accelerator
+ * wants packed in pairs along K, MN-major, and that converting them on each call
+ * costs time ("DeepGEMM-Ascend cobre quantas operacoes no Ascend 950?", section
+ * "Fatores de escala FP8 e o formato UE8M0 no Ascend"); producing that layout
+ * here leaves no conversion for the GEMM call.  The scale rule and the rounding
+ * are readings (the pages do not give them):
+ *   per block of GK elements of a row (GK = 128 for FP8, 32 for FP4), with amax
+ *   its largest magnitude and qmax the format's largest finite value (448, 6):
+ *     rule BSG_SCALE_CEIL  : e = smallest integer with amax <= qmax * 2^e;
+ *     rule BSG_SCALE_OCP_MX: e = floor(log2 amax) - emax (emax 8 for e4m3, 2 for
+ *                            e2m1); magnitudes above qmax * 2^e saturate;
+ *     scale byte = clamp(e + 127, 0, 254); an all-zero block gets byte 0;
+ *     code = x / 2^e rounded to the nearest grid value, ties to the even code,
+ *            saturating at qmax, with x's sign bit (so -0 gives the -0 code).
+ *   X: bf16 [M][ldx], finite values (NaN or infinity give unspecified codes).
+ *   Q: FP8: e4m3 [M][ldq] bytes, ldq >= K;  FP4: e2m1 [M][ldq] bytes, ldq >= K/2,
+ *      two values per byte, the even K index in the low nibble.
+ *   sf: packed int16 [ceil(Kb/2)][ld_sf], ld_sf >= M, Kb = K/GK; element (kp, m)
+ *       holds the bytes of blocks 2kp (low) and 2kp+1 (high, 0x7F when Kb is
+ *       odd).  This is exactly the sfa operand of gemm_fp8_blockscaled /
+ *       gemm_fp4_blockscaled (and of m_grouped_gemm_fp8 for FP8).
+ *   Requires K % GK == 0, K / 512 < 65536; X 16-byte aligned with ldx % 8 == 0;
+ *   Q 8-byte (FP8) or 4-byte (FP4) aligned with ldq a multiple of that; sf 2-byte
+ *   aligned.  M == 0 or K == 0 is a no-op.  Columns of Q beyond K and of sf beyond
+ *   M are not written. */
+int quantize_fp8_per_token(const void* X, int64_t ldx, void* Q, int64_t ldq, int16_t* sf,
+                           int64_t ld_sf, int64_t M, int64_t K, int32_t rule, void* stream);
+
+int quantize_fp4_per_token(const void* X, int64_t ldx, void* Q, int64_t ldq, int16_t* sf,
+                           int64_t ld_sf, int64_t M, int64_t K, int32_t rule, void* stream);
 
 #ifdef __cplusplus
 }

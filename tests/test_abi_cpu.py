@@ -21,7 +21,8 @@ def _declared_functions():
 def test_header_declares_the_api():
     names = _declared_functions()
     for n in ("gemm_bf16", "gemm_fp8_blockscaled", "gemm_fp4_blockscaled", "m_grouped_gemm_fp8",
-              "pack_ue8m0_scales", "unpack_ue8m0_scales", "bsg_status_string"):
+              "pack_ue8m0_scales", "unpack_ue8m0_scales", "bsg_status_string",
+              "quantize_fp8_per_token", "quantize_fp4_per_token"):
         assert n in names
 
 
@@ -139,6 +140,39 @@ def test_pack_validation():
     assert L.pack_ue8m0_scales(0, 0, 4, 4, 0, 8, None) == bsg.BSG_OK
     assert L.unpack_ue8m0_scales(P2, 8, 4, 7, P, 4, None) == bsg.BSG_ERR_INVALID_ARG
     assert L.unpack_ue8m0_scales(0, 8, 4, 8, P, 4, None) == bsg.BSG_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name,gk,qalign", [("quantize_fp8_per_token", 128, 8),
+                                            ("quantize_fp4_per_token", 32, 4)])
+def test_quantize_validation(name, gk, qalign):
+    f = getattr(bsg.lib(), name)
+    K = 4 * gk
+    qcols = K if gk == 128 else K // 2
+    ok = [P, K, P2, qcols, P2 + 0x8000, 64, 64, K, 0, None]
+    # X, ldx, Q, ldq, sf, ld_sf, M, K, rule, stream
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a6=-1) == bsg.BSG_ERR_INVALID_ARG
+    assert call(a8=2) == bsg.BSG_ERR_INVALID_ARG            # unknown rule
+    assert call(a7=K + 16) == bsg.BSG_ERR_UNSUPPORTED_SHAPE  # K % gk
+    assert call(a0=0) == bsg.BSG_ERR_INVALID_ARG
+    assert call(a2=0) == bsg.BSG_ERR_INVALID_ARG
+    assert call(a4=0) == bsg.BSG_ERR_INVALID_ARG
+    assert call(a1=K - 8) == bsg.BSG_ERR_INVALID_ARG         # ldx < K
+    assert call(a3=qcols - qalign) == bsg.BSG_ERR_INVALID_ARG  # ldq too small
+    assert call(a5=63) == bsg.BSG_ERR_INVALID_ARG            # ld_sf < M
+    assert call(a0=P + 8) == bsg.BSG_ERR_MISALIGNED
+    assert call(a1=K + 4) == bsg.BSG_ERR_MISALIGNED          # ldx % 8
+    assert call(a2=P2 + qalign // 2) == bsg.BSG_ERR_MISALIGNED
+    assert call(a3=qcols + qalign // 2) == bsg.BSG_ERR_MISALIGNED
+    assert call(a4=P2 + 0x8001) == bsg.BSG_ERR_MISALIGNED
+    assert call(a7=512 * 65536) == bsg.BSG_ERR_UNSUPPORTED_SHAPE
+    # empty problems are no-ops and need no pointers
+    assert f(0, 0, 0, 0, 0, 0, 0, K, 0, None) == bsg.BSG_OK
+    assert f(0, 0, 0, 0, 0, 0, 8, 0, 1, None) == bsg.BSG_OK
 
 
 def test_binding_refuses_cpu_tensors():
