@@ -27,10 +27,19 @@ Every step below is done in fp64, where all of them are exact (bf16 values,
 powers of two and their products are dyadic rationals well inside fp64's range)
 except the rounding decision itself, which compares exact distances.
 
+SwiGLU (for the MoE FFN core): y = silu(gate) * up with silu(g) = g / (1 + e^-g),
+evaluated in fp64, then quantised as above.  The pages list SwiGLU between the two
+grouped GEMMs of the fused MoE benchmark ("DeepGEMM-Ascend cobre quantas
+operacoes no Ascend 950?" third page, "Kernels de computacao: DeepGEMM-Ascend
+versus DeepGEMM", section "Execucao de MoE: MegaMoE e distribuicao de
+especialistas") without defining it; the textbook SwiGLU, with the gate in the
+first half of the up-projection's columns, is the reading taken here.
+
 Parity status: pinned (tests/test_quantize_pins.py: hand-worked fixtures,
 exhaustive-search brute force in exact rationals, torch's own e4m3 cast for
 in-range values, exact reconstruction of representable blocks, scale shift
-invariance).
+invariance; SwiGLU against torch's silu in fp64, the identity
+silu(g) - silu(-g) = g, and its reduction to the quantiser where sigmoid is 1).
 """
 from __future__ import annotations
 
@@ -111,34 +120,65 @@ def round_to_grid(v: np.ndarray, fmt: str) -> np.ndarray:
     return code.astype(np.uint8)
 
 
-def quantize_rows(x_bits: np.ndarray, fmt: str, rule: str = "ceil"):
-    """bf16 bits uint16 [M][K] -> (codes, sf) with
+def quantize_values(x: np.ndarray, fmt: str, rule: str = "ceil"):
+    """fp64 values [M][K] -> (codes, sf) with
          e4m3: codes uint8 [M][K];
          e2m1: codes uint8 [M][K/2], even k in the low nibble;
-       sf: UE8M0 bytes uint8 [M][K / block], one per block of the row."""
+       sf: UE8M0 bytes uint8 [M][K / block], one per block of the row.
+    A code's sign bit is the value's sign bit (np.signbit: -0.0 counts)."""
     if fmt not in FORMATS:
         raise ValueError(f"unknown format {fmt!r}")
     if rule not in RULES:
         raise ValueError(f"unknown scale rule {rule!r}")
     gk, _, _ = FORMATS[fmt]
-    x_bits = np.asarray(x_bits, dtype=np.uint16)
-    M, K = x_bits.shape
+    x = np.asarray(x, dtype=np.float64)
+    M, K = x.shape
     if K % gk:
         raise ValueError(f"K={K} is not a multiple of the block size {gk}")
     kb = K // gk
-    x = bf16_bits_to_f64(x_bits)
     amax = np.abs(x).reshape(M, kb, gk).max(axis=2) if K else np.zeros((M, 0))
     sf = scale_bytes(amax, fmt, rule)
     e = sf.astype(np.int64) - 127
     v = np.ldexp(x, -np.repeat(e, gk, axis=1))                # exact
     mag = round_to_grid(v, fmt)
-    sign = (x_bits >> 15).astype(np.uint8)
+    sign = np.signbit(x).astype(np.uint8)
     if fmt == "e4m3":
         codes = mag | (sign << 7)
     else:
         nib = mag | (sign << 3)
         codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
     return codes.astype(np.uint8), sf
+
+
+def quantize_rows(x_bits: np.ndarray, fmt: str, rule: str = "ceil"):
+    """bf16 bits uint16 [M][K] -> (codes, sf), as quantize_values on the decoded
+    rows (bf16 -> fp64 is exact and keeps the sign of zero)."""
+    return quantize_values(bf16_bits_to_f64(np.asarray(x_bits, dtype=np.uint16)), fmt, rule)
+
+
+def silu(g: np.ndarray) -> np.ndarray:
+    """SiLU (swish) g * sigmoid(g) = g / (1 + e^-g), fp64.  For g below about -709
+    e^-g overflows to inf and the quotient is a signed zero, the limit."""
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def swiglu(h_bits: np.ndarray, inter: int) -> np.ndarray:
+    """SwiGLU of an up-projection output: bf16 bits [M][2*inter] holding the gate
+    in columns [0, inter) and the up projection in [inter, 2*inter); returns
+    y = silu(gate) * up in fp64 [M][inter]."""
+    h = bf16_bits_to_f64(np.asarray(h_bits, dtype=np.uint16))
+    if h.shape[1] < 2 * inter:
+        raise ValueError("h has fewer than 2*inter columns")
+    return silu(h[:, :inter]) * h[:, inter:2 * inter]
+
+
+def swiglu_quantize(h_bits: np.ndarray, inter: int, fmt: str = "e4m3", rule: str = "ceil"):
+    """(codes, sf, y): the per-token quantisation of swiglu(h_bits, inter), and y."""
+    y = swiglu(h_bits, inter)
+    codes, sf = quantize_values(y, fmt, rule)
+    return codes, sf, y
 
 
 def quantize_rows_packed(x_bits: np.ndarray, fmt: str, rule: str = "ceil",

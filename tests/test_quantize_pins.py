@@ -222,3 +222,72 @@ def test_rejects_ragged_k(oq):
         oq.quantize_rows(np.zeros((2, 100), np.uint16), "e4m3", "ceil")
     with pytest.raises(ValueError):
         oq.quantize_rows(np.zeros((2, 48), np.uint16), "e2m1", "ceil")
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU
+# ---------------------------------------------------------------------------
+
+def test_silu_matches_torch(oq):
+    g = np.concatenate([np.linspace(-60, 60, 20001), [0.0, -0.0, 1e-30, -1e-30]])
+    ref = torch.nn.functional.silu(torch.from_numpy(g)).numpy()
+    got = oq.silu(g)
+    assert np.allclose(got, ref, rtol=4 * 2.0 ** -52, atol=1e-300)
+    assert oq.silu(np.array([-1000.0]))[0] == 0.0        # limit, no NaN
+
+
+def test_silu_odd_part_identity(oq):
+    g = np.random.default_rng(1).standard_normal(10000) * 8
+    assert np.allclose(oq.silu(g) - oq.silu(-g), g, rtol=8 * 2.0 ** -52, atol=0)
+
+
+def test_swiglu_reduces_to_quantiser_where_sigmoid_is_one(oq):
+    """gate = 64 makes sigmoid exactly 1 in fp64, so y = 64 * up exactly, and the
+    result must equal the (pinned) quantiser on 64 * up.  This also fixes which
+    half of the row is the gate."""
+    from block_scaled_precision_05_amd import workloads
+    inter = 256
+    up = workloads.activations(8, inter, seed=9)
+    gate = torch.full((8, inter), 64.0, dtype=torch.bfloat16)
+    h = _bf16_bits(torch.cat([gate, up], dim=1))
+    codes, sf, y = oq.swiglu_quantize(h, inter, "e4m3", "ceil")
+    assert np.array_equal(y, 64.0 * exact.dequant_bf16(_bf16_bits(up)))
+    c2, s2 = oq.quantize_values(64.0 * exact.dequant_bf16(_bf16_bits(up)), "e4m3", "ceil")
+    assert np.array_equal(codes, c2) and np.array_equal(sf, s2)
+    hs = _bf16_bits(torch.cat([up, gate], dim=1))          # halves swapped: differs
+    c3, _, _ = oq.swiglu_quantize(hs, inter, "e4m3", "ceil")
+    assert not np.array_equal(c3, codes)
+
+
+def test_quant_check_accepts_exact_and_rejects_planted_mistakes(oq):
+    """The tolerant comparator used for fp32-computed inputs: it accepts the
+    oracle's own codes, accepts a flip at an exact rounding midpoint, and
+    rejects a wrong code, a wrong sign and a wrong scale away from boundaries."""
+    import quant_check
+    from block_scaled_precision_05_amd import workloads
+    h = _bf16_bits(workloads.activations(16, 512, seed=3))
+    codes, sf, y = oq.swiglu_quantize(h, 256, "e4m3", "ceil")
+    quant_check.check_quantized(codes, sf, y, "e4m3")
+    # a value exactly at a midpoint: both neighbours are acceptable
+    y2 = y.copy()
+    e = int(sf[0, 0]) - 127
+    y2[0, 5] = np.ldexp(1.0625, e)            # midpoint of 1.0 and 1.125 at this scale
+    c2, s2 = oq.quantize_values(y2, "e4m3", "ceil")
+    c2b = c2.copy()
+    c2b[0, 5] = (c2[0, 5] & 0x80) | 0x39      # the odd neighbour
+    quant_check.check_quantized(c2b, s2, y2, "e4m3")
+    # planted mistakes
+    i, k = 3, 17
+    far = codes.copy()
+    far[i, k] = (far[i, k] & 0x80) | ((far[i, k] & 0x7F) + 2)
+    with pytest.raises(AssertionError):
+        quant_check.check_quantized(far, sf, y, "e4m3")
+    flip = codes.copy()
+    flip[i, k] ^= 0x80
+    if y[i, k] != 0:
+        with pytest.raises(AssertionError):
+            quant_check.check_quantized(flip, sf, y, "e4m3")
+    sfb = sf.copy()
+    sfb[2, 1] += 1
+    with pytest.raises(AssertionError):
+        quant_check.check_quantized(codes, sfb, y, "e4m3")
