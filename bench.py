@@ -1,7 +1,7 @@
 """Benchmark of the block-scaled GEMM library on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--dtypes bf16,fp8,fp4,grouped,quant_fp8,quant_fp4,quant_fp8_moe]
+                    [--dtypes bf16,fp8,fp4,grouped,quant_fp8,quant_fp4,quant_fp8_moe,moe_ffn]
 
 Workload: D = A * B^T at M=4096, N=7168, K=16384, the dense shape the pages time
 (431 TFLOPS BF16 on the other accelerator: "DeepSeek lanza kernels de DeepGEMM
@@ -25,6 +25,11 @@ packed UE8M0 scales) are timed the same way on the dense shape's A (4096x16384)
 and on the MoE tokens (16384x7168), reported in GB/s of algorithmic traffic
 against the 8 TB/s HBM peak.
 
+The MoE FFN core (grouped up-projection, SwiGLU + FP8 requantisation, grouped
+down-projection) runs on one GPU's share of the pages' fused MoE case: 48 of 384
+experts (EP8) plus the shared expert, 16384 tokens top-6, hidden 7168,
+intermediate 2048; TFLOPS count useful (unpadded) rows.
+
 `cpu_baseline` times the CPU oracle (plain C, fp64) on a bounded row sample of
 the BF16 workload on this host's cores.
 """
@@ -46,7 +51,7 @@ if ROOT not in sys.path:
 METRIC = "TFLOPS and % of MI355X dense MFMA peak, GEMM 4096×7168×16384 per dtype"
 
 # MI355X published dense MFMA peaks (TFLOP/s).
-PEAK = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0, "grouped": 5000.0}
+PEAK = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0, "grouped": 5000.0, "moe_ffn": 5000.0}
 # MI355X published HBM3E bandwidth (GB/s): the bound of the quantisers.
 HBM_PEAK_GBS = 8000.0
 QUANT_KINDS = ("quant_fp8", "quant_fp4", "quant_fp8_moe")
@@ -61,6 +66,7 @@ KERNEL_NAME = {
     "quant_fp8": "quant_kernel<0, 0, 32, 2, 0>",
     "quant_fp4": "quant_kernel<1, 0, 32, 2, 0>",
     "quant_fp8_moe": "quant_kernel<0, 0, 32, 2, 0>",
+    "moe_ffn": "gemm_kernel<1, 128, 512, 1, 4, 64, 4, 1, true> x2 + swiglu_quant_kernel<0>",
 }
 
 
@@ -115,7 +121,7 @@ def make_case(kind, dev):
 
     name = {"bf16": "bf16_large", "fp8": "fp8_large", "fp4": "fp4_large",
             "grouped": "moe_fp8", "quant_fp8": "act_large", "quant_fp4": "act_large",
-            "quant_fp8_moe": "act_moe"}[kind]
+            "quant_fp8_moe": "act_moe", "moe_ffn": "moe_ffn"}[kind]
     w = workloads.make(name, device=dev)
     t = w.tensors
     M, N, K = w.M, w.N, w.K
@@ -143,6 +149,29 @@ def make_case(kind, dev):
                 "bytes_per_call": nbytes}
         meta.update({"M": M, "K": K})
         return call, 0.0, nbytes, meta
+    if kind == "moe_ffn":
+        G, two_i, hidden = t["W13"].shape
+        inter = two_i // 2
+        sfa = bsg.ensure_packed(t["sfa"], M, hidden // 128)
+        sfw13 = torch.stack([bsg.ensure_packed(x, (two_i + 127) // 128, hidden // 128)
+                             for x in t["sfw13"]])
+        sfw2 = torch.stack([bsg.ensure_packed(x, (hidden + 127) // 128, inter // 128)
+                            for x in t["sfw2"]])
+        ws = (torch.empty(M, two_i, dtype=torch.bfloat16, device=dev),
+              torch.empty(M, inter, dtype=torch.uint8, device=dev),
+              torch.empty((inter // 128 + 1) // 2, M, dtype=torch.int16, device=dev))
+        D = torch.empty(M, hidden, dtype=torch.bfloat16, device=dev)
+        A, W13, W2, off = t["A"], t["W13"], t["W2"], t["offsets"]
+        call = lambda: bsg.moe_ffn_fp8(A, sfa, W13, sfw13, W2, sfw2, off, out=D, workspace=ws)
+        nbytes = (A.numel() + W13.numel() + W2.numel() + 2 * M * hidden
+                  + 2 * (M * two_i) * 2 + M * inter * 2)
+        meta = {"experts": G, "hidden": hidden, "inter": inter, "m_total": M,
+                "useful_rows": w.meta["useful_rows"], "routing": w.meta["routing"],
+                "executed_tflop": 2.0 * M * (two_i * hidden + hidden * inter) / 1e12,
+                "steps": "grouped up-projection, SwiGLU + FP8 1x128 requantisation, "
+                         "grouped down-projection"}
+        meta.update({"M": M, "N": hidden, "K": hidden})
+        return call, w.flops, nbytes, meta
     if kind == "bf16":
         A, B = t["A"], t["B"]
         D = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
@@ -300,7 +329,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--dtypes", default="bf16,fp8,fp4,grouped,quant_fp8,quant_fp4,quant_fp8_moe")
+    ap.add_argument("--dtypes",
+                    default="bf16,fp8,fp4,grouped,quant_fp8,quant_fp4,quant_fp8_moe,moe_ffn")
     ap.add_argument("--cold-samples", type=int, default=10)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle time for cpu_baseline (0 disables it)")

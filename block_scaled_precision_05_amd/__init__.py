@@ -14,6 +14,8 @@ if ``libbsg.so`` is missing or cannot be loaded, every call raises.
     P = ensure_packed(sf, mn, kb)               # reuse if already packed, else pack
     Q, P = quantize_fp8_per_token(X)            # bf16 [M,K] -> e4m3 + packed 1x128 scales
     Q, P = quantize_fp4_per_token(X)            # bf16 [M,K] -> e2m1 (2/byte) + packed 1x32 scales
+    Q, P = swiglu_quantize_fp8(H, inter)        # silu(H[:, :I]) * H[:, I:2I] -> e4m3 + scales
+    D = moe_ffn_fp8(A, sfa, W13, sfw13, W2, sfw2, offsets)   # grouped up, SwiGLU, grouped down
 """
 from __future__ import annotations
 
@@ -53,6 +55,12 @@ EXPORTS = {
     "unpack_ue8m0_scales": [_vp, _i64, _i64, _i64, _vp, _i64, _vp],
     "quantize_fp8_per_token": [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i32, _vp],
     "quantize_fp4_per_token": [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i32, _vp],
+    "swiglu_quantize_fp8": [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i32, _vp],
+    "moe_ffn_fp8": [_vp, _i64, _vp, _i64,
+                    _vp, _i64, _i64, _vp, _i64, _i64,
+                    _vp, _i64, _i64, _vp, _i64, _i64,
+                    _vp, _i32, _i64, _i64, _i64,
+                    _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i32, _vp],
 }
 
 
@@ -293,3 +301,63 @@ def quantize_fp4_per_token(X, rule: str = "ceil", out=None, sf_out=None, ld_sf=N
     K-block."""
     return _quantize("quantize_fp4_per_token", X, rule, lambda K: K // 2, 32, out, sf_out, ld_sf,
                      stream)
+
+
+def swiglu_quantize_fp8(H, inter: int, rule: str = "ceil", out=None, sf_out=None, ld_sf=None,
+                        stream=None):
+    """bf16 H [M, >=2*inter] (gate in columns [0, inter), up in [inter, 2*inter)) ->
+    (e4m3 codes uint8 [M, inter], packed int16 scales [ceil(inter/256), ld_sf]) of
+    y = silu(gate) * up, one UE8M0 scale per row per 128 columns."""
+    _dev(H, out, sf_out)
+    if H.dtype != torch.bfloat16:
+        raise TypeError("H must be bfloat16")
+    if rule not in SCALE_RULES:
+        raise ValueError(f"rule must be one of {sorted(SCALE_RULES)}")
+    M = H.shape[0]
+    kp = (inter // 128 + 1) // 2
+    ld = M if ld_sf is None else int(ld_sf)
+    Q = torch.empty((M, inter), dtype=torch.uint8, device=H.device) if out is None \
+        else _bytes_u8(out)
+    P = torch.empty((kp, ld), dtype=torch.int16, device=H.device) if sf_out is None else sf_out
+    _check("swiglu_quantize_fp8", lib().swiglu_quantize_fp8(
+        _ptr(H), _mat(H, "H"), _ptr(Q), _mat(Q, "out"), _ptr(P), _packed(P, "sf_out"), M, inter,
+        SCALE_RULES[rule], _stream(stream)))
+    return Q, P
+
+
+def moe_ffn_fp8(A, sfa, W13, sfw13, W2, sfw2, offsets, rule: str = "ceil", out=None,
+                workspace=None, stream=None):
+    """MoE FFN core: grouped up-projection (W13 [G, 2*inter, hidden]), SwiGLU + FP8
+    requantisation, grouped down-projection (W2 [G, hidden, inter]); A e4m3
+    [M_total, hidden] with packed scales; offsets int32 [G+1] on the GPU.  Returns
+    D bf16 [M_total, hidden].  ``workspace`` may pass (H, Y, sfy) buffers; they are
+    allocated here otherwise."""
+    _dev(A, sfa, W13, sfw13, W2, sfw2, offsets, out)
+    A, W13, W2 = _bytes_u8(A), _bytes_u8(W13), _bytes_u8(W2)
+    if W13.dim() != 3 or W2.dim() != 3 or sfw13.dim() != 3 or sfw2.dim() != 3:
+        raise ValueError("W13, W2 and their scales must be [G, rows, cols]")
+    if offsets.dtype != torch.int32 or offsets.dim() != 1 or not offsets.is_contiguous():
+        raise TypeError("offsets must be a contiguous int32 vector")
+    G, two_i, hidden = W13.shape
+    inter = two_i // 2
+    if W2.shape[0] != G or W2.shape[1] != hidden or W2.shape[2] != inter or two_i != 2 * inter:
+        raise ValueError("W2 must be [G, hidden, inter] for W13 [G, 2*inter, hidden]")
+    M = A.shape[0]
+    if workspace is None:
+        H = torch.empty((M, 2 * inter), dtype=torch.bfloat16, device=A.device)
+        Y = torch.empty((M, inter), dtype=torch.uint8, device=A.device)
+        sfy = torch.empty(((inter // 128 + 1) // 2, M), dtype=torch.int16, device=A.device)
+    else:
+        H, Y, sfy = workspace
+    D = _out(out, M, hidden, A.device)
+    for t, n in ((W13, "W13"), (W2, "W2"), (sfw13, "sfw13"), (sfw2, "sfw2")):
+        if t.stride(2) != 1:
+            raise ValueError(f"{n} must be contiguous along its last dimension")
+    _check("moe_ffn_fp8", lib().moe_ffn_fp8(
+        _ptr(A), _mat(A, "A"), _ptr(sfa), _packed(sfa, "sfa"),
+        _ptr(W13), W13.stride(1), W13.stride(0), _ptr(sfw13), sfw13.stride(1), sfw13.stride(0),
+        _ptr(W2), W2.stride(1), W2.stride(0), _ptr(sfw2), sfw2.stride(1), sfw2.stride(0),
+        _ptr(offsets), G, M, hidden, inter,
+        _ptr(H), _mat(H, "H"), _ptr(Y), _mat(_bytes_u8(Y), "Y"), _ptr(sfy), _packed(sfy, "sfy"),
+        _ptr(D), _mat(D, "out"), SCALE_RULES[rule], _stream(stream)))
+    return D

@@ -8,6 +8,7 @@
 
 #include "../../include/bsg.h"
 #include "gemm_kernel.h"
+#include "internal.h"
 
 namespace bsg {
 
@@ -125,6 +126,34 @@ static int check_dense(const void* A, int64_t lda, const void* B, int64_t ldb, c
   return BSG_OK;
 }
 
+static int check_scales(const int16_t* sfa, int64_t ld_sfa, int64_t rows_a, const int16_t* sfb,
+                        int64_t ld_sfb, int64_t rows_b, int64_t K) {
+  if (K == 0) return BSG_OK;
+  if (!sfa || !sfb) return BSG_ERR_INVALID_ARG;
+  if (ld_sfa < rows_a || ld_sfb < rows_b) return BSG_ERR_INVALID_ARG;
+  if (((uintptr_t)sfa & 1) || ((uintptr_t)sfb & 1)) return BSG_ERR_MISALIGNED;
+  return BSG_OK;
+}
+
+int grouped_fp8_check(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
+                      const void* B, int64_t ldb, int64_t stride_b, const int16_t* sfb,
+                      int64_t ld_sfb, int64_t stride_sfb, const void* D, int64_t ldd,
+                      const int32_t* group_offsets, int32_t G, int64_t M_total, int64_t N,
+                      int64_t K) {
+  if (G < 0 || G > 1024) return G < 0 ? BSG_ERR_INVALID_ARG : BSG_ERR_UNSUPPORTED_SHAPE;
+  int st = check_dense(A, lda, B, ldb, D, ldd, M_total, N, K, 128, K, 1);
+  if (st != BSG_OK || M_total == 0 || N == 0 || G == 0) return st;
+  if (!group_offsets) return BSG_ERR_INVALID_ARG;
+  st = check_scales(sfa, ld_sfa, M_total, sfb, ld_sfb, (N + 127) / 128, K);
+  if (st != BSG_OK) return st;
+  const int64_t kp = (K / 128 + 1) / 2;
+  if (G > 1 && (stride_b < (N - 1) * ldb + K || (K > 0 && stride_sfb < kp * ld_sfb)))
+    return BSG_ERR_INVALID_ARG;
+  if (stride_b < 0 || stride_sfb < 0) return BSG_ERR_INVALID_ARG;
+  if (stride_b % 16) return BSG_ERR_MISALIGNED;
+  return BSG_OK;
+}
+
 }  // namespace bsg
 
 using namespace bsg;
@@ -158,15 +187,6 @@ int gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, void* D, i
   a.K = (int32_t)K;
   a.k_bytes = (int32_t)(2 * K);
   return launch<KIND_BF16, BSG_BF16_CFG, false>(a, (hipStream_t)stream);
-}
-
-static int check_scales(const int16_t* sfa, int64_t ld_sfa, int64_t rows_a, const int16_t* sfb,
-                        int64_t ld_sfb, int64_t rows_b, int64_t K) {
-  if (K == 0) return BSG_OK;
-  if (!sfa || !sfb) return BSG_ERR_INVALID_ARG;
-  if (ld_sfa < rows_a || ld_sfb < rows_b) return BSG_ERR_INVALID_ARG;
-  if (((uintptr_t)sfa & 1) || ((uintptr_t)sfb & 1)) return BSG_ERR_MISALIGNED;
-  return BSG_OK;
 }
 
 int gemm_fp8_blockscaled(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
@@ -228,17 +248,10 @@ int m_grouped_gemm_fp8(const void* A, int64_t lda, const int16_t* sfa, int64_t l
                        const int16_t* sfb, int64_t ld_sfb, int64_t stride_sfb,
                        void* D, int64_t ldd, const int32_t* group_offsets, int32_t G,
                        int64_t M_total, int64_t N, int64_t K, void* stream) {
-  if (G < 0 || G > 1024) return G < 0 ? BSG_ERR_INVALID_ARG : BSG_ERR_UNSUPPORTED_SHAPE;
-  int st = check_dense(A, lda, B, ldb, D, ldd, M_total, N, K, 128, K, 1);
+  const int st = grouped_fp8_check(A, lda, sfa, ld_sfa, B, ldb, stride_b, sfb, ld_sfb, stride_sfb, D,
+                                   ldd, group_offsets, G, M_total, N, K);
   if (st != BSG_OK || M_total == 0 || N == 0 || G == 0) return st;
-  if (!group_offsets) return BSG_ERR_INVALID_ARG;
-  st = check_scales(sfa, ld_sfa, M_total, sfb, ld_sfb, (N + 127) / 128, K);
-  if (st != BSG_OK) return st;
   const int64_t kp = (K / 128 + 1) / 2;
-  if (G > 1 && (stride_b < (N - 1) * ldb + K || (K > 0 && stride_sfb < kp * ld_sfb)))
-    return BSG_ERR_INVALID_ARG;
-  if (stride_b < 0 || stride_sfb < 0) return BSG_ERR_INVALID_ARG;
-  if (stride_b % 16) return BSG_ERR_MISALIGNED;
   GemmArgs a = {};
   a.A = (const uint8_t*)A;
   a.B = (const uint8_t*)B;

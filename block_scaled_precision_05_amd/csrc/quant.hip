@@ -30,6 +30,7 @@
 #include <stdint.h>
 
 #include "../../include/bsg.h"
+#include "internal.h"
 
 namespace bsg_quant {
 
@@ -65,24 +66,26 @@ struct Fmt<FMT_E2M1> {
   static constexpr int EMAX = 2;
 };
 
-// Scale byte of a block from its largest bf16 magnitude h (sign bit clear).
-// A bf16 magnitude is sig * 2^ex with sig the 8-bit significand (hidden bit
-// included) or, below the normal range, the 7-bit fraction at ex = -133.
-// Normalising sig to sn in [128, 256) gives floor(log2) p, and amax = sn/256 *
-// 2^(p+1), so with qmax = qt/256 * 2^qx the smallest e with amax <= qmax * 2^e
-// is p + 1 - qx, plus one when sn > qt.  h == 0 needs no branch: clz gives
-// 32, so p = -134 and the byte clamps to 0.
+// Scale byte of a block from its largest magnitude, given as fp32 bits a (sign
+// bit clear; a bf16 magnitude h is a = h << 16).  The magnitude is sig * 2^ex
+// with sig the 24-bit significand (hidden bit included) or, below the normal
+// range, the 23-bit fraction at ex = -149.  Normalising sig to sn in [2^23,
+// 2^24) gives floor(log2) p, and amax = sn/2^24 * 2^(p+1); with qmax = qt/256 *
+// 2^qx the smallest e with amax <= qmax * 2^e is p + 1 - qx, plus one when
+// sn > qt * 2^16.  a == 0 needs no branch: clz gives 32, p = -150 and the byte
+// clamps to 0.
 template <int FMT, int RULE>
-__device__ __forceinline__ int scale_byte(uint32_t h) {
+__device__ __forceinline__ int scale_byte(uint32_t a) {
   using F = Fmt<FMT>;
-  const uint32_t E = h >> 7;
-  const uint32_t sig = E ? (0x80u | (h & 0x7Fu)) : (h & 0x7Fu);
-  const int ex = E ? (int)E - 134 : -133;
-  const int lz = __clz(sig) - 24;
+  const uint32_t E = a >> 23;
+  const uint32_t sig = E ? (0x800000u | (a & 0x7FFFFFu)) : (a & 0x7FFFFFu);
+  const int ex = E ? (int)E - 150 : -149;
+  const int lz = __clz(sig) - 8;
   const uint32_t sn = sig << lz;
-  const int p = 7 - lz + ex;
-  const int e = RULE == BSG_SCALE_CEIL ? p + 1 - F::QX + (sn > (uint32_t)F::QT ? 1 : 0)
-                                       : p - F::EMAX;
+  const int p = 23 - lz + ex;
+  const int e = RULE == BSG_SCALE_CEIL
+                    ? p + 1 - F::QX + (sn > ((uint32_t)F::QT << 16) ? 1 : 0)
+                    : p - F::EMAX;
   const int b = e + 127;
   return b < 0 ? 0 : (b > 254 ? 254 : b);
 }
@@ -179,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
     const uint32_t m23 = pk_max_u16(w[2] & 0x7FFF7FFFu, w[3] & 0x7FFF7FFFu);
     const uint32_t m = pk_max_u16(m01, m23);
     const uint32_t h = block_max<F::LANES>(max(m & 0xFFFFu, m >> 16));
-    const int byte = scale_byte<FMT, RULE>(h);
+    const int byte = scale_byte<FMT, RULE>(h << 16);
     const float sc = scale_f32(byte);
     // The gfx950 scaled conversions compute x / sc, round to nearest even and
     // saturate e2m1 at 6; e4m3 beyond 448 would turn into NaN, which only the
@@ -214,6 +217,103 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
       const int blk = (k0 / F::GK) + lane / F::LANES;  // even block of the pair
       const uint32_t hi = (blk + 1 < kb_total) ? (uint32_t)hb : 0x7Fu;
       words[lane / (2 * F::LANES)][rl] = (uint16_t)(byte | (hi << 8));
+    }
+  }
+  __syncthreads();
+  const int kp0 = k0 / (2 * F::GK);
+  const int kp_total = (kb_total + 1) / 2;
+  for (int t = threadIdx.x; t < KPT * ROWS; t += kThreads) {
+    const int kp = t / ROWS, rl = t % ROWS;
+    if (kp0 + kp < kp_total && m0 + rl < M)
+      sf[(int64_t)(kp0 + kp) * ld_sf + m0 + rl] = (int16_t)words[kp][rl];
+  }
+}
+
+// SiLU in fp32: g / (1 + e^-g) with the accurate expf and a reciprocal (about 3
+// ulp in all).  For g below about -88 e^-g is +inf, the reciprocal 0 and the
+// result a zero with g's sign, the limit.
+__device__ __forceinline__ float silu_f32(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + expf(-g));
+}
+
+// SwiGLU of an up-projection output followed by FP8 1x128 quantisation.  H is
+// bf16 [M][ldh] with the gate in columns [0, I) and the up projection in
+// [I, 2I); y = silu(gate) * up is formed in fp32 and quantised exactly as
+// quant_kernel quantises its input (same tile, scale rules and scale layout),
+// with the gfx950 fp32 scaled conversion.  The pages place SwiGLU between the
+// two grouped GEMMs of the fused MoE step ("DeepGEMM-Ascend cobre quantas
+// operacoes no Ascend 950?" third page, "Kernels de computacao: DeepGEMM-Ascend
+// versus DeepGEMM", section "Execucao de MoE: MegaMoE e distribuicao de
+// especialistas").
+template <int RULE, int ROWS = kRows, int LAUX = kLoadAux>
+__global__ __launch_bounds__(kThreads) void swiglu_quant_kernel(
+    const uint16_t* __restrict__ H, int64_t ldh, uint8_t* __restrict__ Q, int64_t ldq,
+    int16_t* __restrict__ sf, int64_t ld_sf, int M, int I) {
+  using F = Fmt<FMT_E4M3>;
+  constexpr int kRowsPerWave = ROWS / kWaves;
+  constexpr int KPT = kCols / F::GK / 2;
+  __shared__ uint16_t words[KPT][ROWS];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m0 = blockIdx.x * ROWS;
+  const int rows = min(ROWS, M - m0);
+  const int k0 = blockIdx.y * kCols;
+  const int k = k0 + lane * 8;
+  const bool kin = k < I;
+  const int kb_total = I / F::GK;
+
+  const __amdgpu_buffer_rsrc_t hr =
+      make_rsrc(H + (int64_t)m0 * ldh, (uint32_t)(((int64_t)(rows - 1) * ldh + 2 * (int64_t)I) * 2));
+  const __amdgpu_buffer_rsrc_t qr =
+      make_rsrc(Q + (int64_t)m0 * ldq, (uint32_t)((int64_t)(rows - 1) * ldq + I));
+  const uint32_t goff = kin ? (uint32_t)k * 2 : kOOB;
+  const uint32_t uoff = kin ? (uint32_t)(I + k) * 2 : kOOB;
+  const uint32_t qoff = kin ? (uint32_t)k : kOOB;
+
+  u32x4_t gr[kRowsPerWave], ur[kRowsPerWave];
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const int so = (wave + i * kWaves) * (int)ldh * 2;
+    gr[i] = __builtin_amdgcn_raw_buffer_load_b128(hr, goff, so, LAUX);
+    ur[i] = __builtin_amdgcn_raw_buffer_load_b128(hr, uoff, so, LAUX);
+  }
+
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const int rl = wave + i * kWaves;
+    float y[8];
+    uint32_t a = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t g = gr[i][j], u = ur[i][j];
+      y[2 * j] = silu_f32(__uint_as_float(g << 16)) * __uint_as_float(u << 16);
+      y[2 * j + 1] = silu_f32(__uint_as_float(g & 0xFFFF0000u)) * __uint_as_float(u & 0xFFFF0000u);
+      a = max(a, __float_as_uint(y[2 * j]) & 0x7FFFFFFFu);
+      a = max(a, __float_as_uint(y[2 * j + 1]) & 0x7FFFFFFFu);
+    }
+    a = block_max<F::LANES>(a);
+    const int byte = scale_byte<FMT_E4M3, RULE>(a);
+    const float sc = scale_f32(byte);
+    if (RULE == BSG_SCALE_OCP_MX) {
+      // saturate at 448 * sc before the conversion (which would give NaN)
+      const float lim = 448.0f * sc;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        y[j] = __builtin_copysignf(fminf(fabsf(y[j]), lim), y[j]);
+    }
+    short2_t lo = {0, 0}, hi = {0, 0};
+    lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, y[0], y[1], sc, false);
+    lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, y[2], y[3], sc, true);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, y[4], y[5], sc, false);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, y[6], y[7], sc, true);
+    const u32x2_t v = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+    __builtin_amdgcn_raw_buffer_store_b64(v, qr, qoff, rl * (int)ldq, 0);
+    const int hb = __shfl_down(byte, F::LANES);
+    if ((lane % (2 * F::LANES)) == 0) {
+      const int blk = (k0 / F::GK) + lane / F::LANES;
+      const uint32_t hbyte = (blk + 1 < kb_total) ? (uint32_t)hb : 0x7Fu;
+      words[lane / (2 * F::LANES)][rl] = (uint16_t)(byte | (hbyte << 8));
     }
   }
   __syncthreads();
@@ -261,6 +361,30 @@ static int check(const void* X, int64_t ldx, const void* Q, int64_t ldq, const i
   return BSG_OK;
 }
 
+static int swiglu_check(const void* H, int64_t ldh, const void* Q, int64_t ldq, const int16_t* sf,
+                        int64_t ld_sf, int64_t M, int64_t I, int32_t rule) {
+  // H rows are read as 2I elements; the checks of an FP8 quantiser of width I
+  // cover Q and sf, and ldh must hold both halves.
+  if (I < 0) return BSG_ERR_INVALID_ARG;
+  const int st = check(H, ldh, Q, ldq, sf, ld_sf, M, I, rule, 128, I, 8);
+  if (st != BSG_OK || M == 0 || I == 0) return st;
+  if (ldh < 2 * I) return BSG_ERR_INVALID_ARG;
+  return BSG_OK;
+}
+
+static int swiglu_launch(const void* H, int64_t ldh, void* Q, int64_t ldq, int16_t* sf,
+                         int64_t ld_sf, int64_t M, int64_t I, int32_t rule, hipStream_t stream) {
+  const dim3 grid((unsigned)((M + kRows - 1) / kRows), (unsigned)((I + kCols - 1) / kCols));
+  (void)hipGetLastError();
+  if (rule == BSG_SCALE_CEIL)
+    hipLaunchKernelGGL((swiglu_quant_kernel<BSG_SCALE_CEIL>), grid, dim3(kThreads), 0, stream,
+                       (const uint16_t*)H, ldh, (uint8_t*)Q, ldq, sf, ld_sf, (int)M, (int)I);
+  else
+    hipLaunchKernelGGL((swiglu_quant_kernel<BSG_SCALE_OCP_MX>), grid, dim3(kThreads), 0, stream,
+                       (const uint16_t*)H, ldh, (uint8_t*)Q, ldq, sf, ld_sf, (int)M, (int)I);
+  return hipGetLastError() == hipSuccess ? BSG_OK : BSG_ERR_HIP;
+}
+
 }  // namespace bsg_quant
 
 using namespace bsg_quant;
@@ -279,6 +403,43 @@ int quantize_fp4_per_token(const void* X, int64_t ldx, void* Q, int64_t ldq, int
   const int st = check(X, ldx, Q, ldq, sf, ld_sf, M, K, rule, 32, K / 2, 4);
   if (st != BSG_OK || M == 0 || K == 0) return st;
   return launch<FMT_E2M1>(X, ldx, Q, ldq, sf, ld_sf, M, K, rule, (hipStream_t)stream);
+}
+
+int swiglu_quantize_fp8(const void* H, int64_t ldh, void* Q, int64_t ldq, int16_t* sf,
+                        int64_t ld_sf, int64_t M, int64_t I, int32_t rule, void* stream) {
+  const int st = swiglu_check(H, ldh, Q, ldq, sf, ld_sf, M, I, rule);
+  if (st != BSG_OK || M == 0 || I == 0) return st;
+  return swiglu_launch(H, ldh, Q, ldq, sf, ld_sf, M, I, rule, (hipStream_t)stream);
+}
+
+int moe_ffn_fp8(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
+                const void* W13, int64_t ldw13, int64_t stride_w13, const int16_t* sfw13,
+                int64_t ld_sfw13, int64_t stride_sfw13,
+                const void* W2, int64_t ldw2, int64_t stride_w2, const int16_t* sfw2,
+                int64_t ld_sfw2, int64_t stride_sfw2,
+                const int32_t* group_offsets, int32_t G, int64_t M_total, int64_t hidden,
+                int64_t inter, void* H, int64_t ldh, void* Y, int64_t ldy, int16_t* sfy,
+                int64_t ld_sfy, void* D, int64_t ldd, int32_t rule, void* stream) {
+  if (inter < 0 || hidden < 0) return BSG_ERR_INVALID_ARG;
+  // every check before the first launch, so a bad argument launches nothing
+  int st = bsg::grouped_fp8_check(A, lda, sfa, ld_sfa, W13, ldw13, stride_w13, sfw13, ld_sfw13,
+                                  stride_sfw13, H, ldh, group_offsets, G, M_total, 2 * inter,
+                                  hidden);
+  if (st != BSG_OK) return st;
+  st = swiglu_check(H, ldh, Y, ldy, sfy, ld_sfy, M_total, inter, rule);
+  if (st != BSG_OK) return st;
+  st = bsg::grouped_fp8_check(Y, ldy, sfy, ld_sfy, W2, ldw2, stride_w2, sfw2, ld_sfw2, stride_sfw2,
+                              D, ldd, group_offsets, G, M_total, hidden, inter);
+  if (st != BSG_OK) return st;
+  if (M_total == 0 || G == 0 || hidden == 0 || inter == 0) return BSG_OK;
+  st = m_grouped_gemm_fp8(A, lda, sfa, ld_sfa, W13, ldw13, stride_w13, sfw13, ld_sfw13,
+                          stride_sfw13, H, ldh, group_offsets, G, M_total, 2 * inter, hidden,
+                          stream);
+  if (st != BSG_OK) return st;
+  st = swiglu_launch(H, ldh, Y, ldy, sfy, ld_sfy, M_total, inter, rule, (hipStream_t)stream);
+  if (st != BSG_OK) return st;
+  return m_grouped_gemm_fp8(Y, ldy, sfy, ld_sfy, W2, ldw2, stride_w2, sfw2, ld_sfw2, stride_sfw2,
+                            D, ldd, group_offsets, G, M_total, hidden, inter, stream);
 }
 
 }  // extern "C"

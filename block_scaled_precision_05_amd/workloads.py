@@ -20,6 +20,9 @@ para calculo e comunicacao de IA", section "Resultados de kernel e comunicacao")
   fp4_large     FP4 4096x7168x16384, 1x32 UE8M0 scales on both operands
   act_large     bf16 activations 4096x16384 (A of the dense shape), to be quantised
   act_moe       bf16 activations 16384x7168 (the MoE tokens), to be quantised
+  moe_ffn       MoE FFN core on one GPU's share of the pages' fused MoE case:
+                384 experts over EP8 -> 48 local experts plus the shared expert,
+                16384 tokens top-6, hidden 7168, intermediate 2048
 
 Value recipes:
   * FP8: for every scale entry an exponent e ~ U{-8..4}; a value is
@@ -32,6 +35,11 @@ Value recipes:
     over 256 experts with popularity p_r ~ r^-1.1 (rank r = 1..256), ranks mapped
     to expert ids by a seeded permutation; every count is padded up to a multiple
     of 128.  Padding rows hold zero codes and scale byte 127.
+  * MoE FFN share: 98304 assignments drawn as for moe_fp8 but over 384 experts;
+    the local experts are those the seeded permutation puts on rank 0 of 8
+    (48 of them), plus one shared expert that every token visits; counts padded
+    to multiples of 128.  W13 [G][2*inter][hidden] (gate rows first) and W2
+    [G][hidden][inter] follow the FP8 recipe with 128x128 scales.
   * Activations (bf16, input of the per-token quantiser): x ~ N(0,1) times a
     per-row power of two 2^U{-6..6}; one column in 64 (a seeded choice) is an
     outlier channel scaled by 32; the last ``zero_rows`` rows are zero.
@@ -159,6 +167,8 @@ class Workload:
         """Algorithmic flops, 2*M*N*K (useful rows only for the grouped case)."""
         if self.kind == "grouped_fp8":
             return 2.0 * float(self.meta["useful_rows"]) * self.N * self.K
+        if self.kind == "moe_ffn":
+            return float(self.meta["useful_flops"])
         return 2.0 * self.M * self.N * self.K
 
 
@@ -171,6 +181,7 @@ SHAPES = {
     "fp8_large": ("fp8", 4096, 7168, 16384, 1006),
     "act_large": ("act", 4096, None, 16384, 1007),
     "act_moe": ("act", 16384, None, 7168, 1008),
+    "moe_ffn": ("moe_ffn", None, None, None, 1009),
 }
 
 
@@ -230,12 +241,61 @@ def grouped(G: int, N: int, K: int, seed: int, device="cpu", counts=None, name="
     return w
 
 
+def moe_ffn(seed: int, device="cpu", hidden: int = 7168, inter: int = 2048, experts: int = 384,
+            ranks: int = 8, rank: int = 0, shared: int = 1, tokens: int = 16384, topk: int = 6,
+            zipf: float = 1.1, counts=None, name: str = "custom", align: int = 128):
+    """Inputs of the MoE FFN core for one rank's experts (recipe in the module
+    docstring).  ``counts`` (length G) overrides the routing draw."""
+    g = _gen(device, seed)
+    if counts is None:
+        all_counts = moe_counts(g, device, tokens=tokens, topk=topk, experts=experts, zipf=zipf)
+        per = experts // ranks
+        local = all_counts[rank * per:(rank + 1) * per]
+        counts = torch.cat([local, torch.full((shared,), tokens, dtype=torch.int64,
+                                              device=local.device)])
+    else:
+        counts = torch.as_tensor(list(counts), dtype=torch.int64, device=device)
+    G = counts.numel()
+    off = pad_offsets(counts, align)
+    m_total = int(off[-1].item())
+    A, sfa = fp8_operand(max(m_total, 1), hidden, 1, g, device)
+    A, sfa = A[:m_total], sfa[:m_total]
+    valid = torch.zeros(m_total, dtype=torch.bool, device=device)
+    for e in range(G):
+        s0, c = int(off[e]), int(counts[e])
+        if c:
+            valid[s0:s0 + c] = True
+    A[~valid] = 0
+    sfa[~valid] = 127
+    W13, s13, W2, s2 = [], [], [], []
+    for _ in range(G):
+        w, sw = fp8_operand(2 * inter, hidden, 128, g, device)
+        W13.append(w)
+        s13.append(sw)
+        w, sw = fp8_operand(hidden, inter, 128, g, device)
+        W2.append(w)
+        s2.append(sw)
+    w = Workload(name, "moe_ffn", m_total, hidden, hidden)
+    w.tensors.update(A=A.contiguous(), sfa=sfa.contiguous(), W13=torch.stack(W13),
+                     sfw13=torch.stack(s13), W2=torch.stack(W2), sfw2=torch.stack(s2),
+                     offsets=off, counts=counts)
+    useful = int(counts.sum().item())
+    w.meta.update(seed=seed, G=G, hidden=hidden, inter=inter, useful_rows=useful,
+                  m_total=m_total,
+                  routing=f"rank {rank} of {ranks}: {experts // ranks} of {experts} experts "
+                          f"+ {shared} shared, multinomial({tokens}x{topk}), zipf {zipf}, pad {align}",
+                  useful_flops=2.0 * useful * (2 * inter * hidden + hidden * inter))
+    return w
+
+
 def make(name: str, device="cpu", seed: int | None = None) -> Workload:
     """One of the named workloads in ``SHAPES``."""
     kind, M, N, K, default_seed = SHAPES[name]
     seed = default_seed if seed is None else seed
     if kind == "grouped_fp8":
         w = grouped(256, N, K, seed, device=device, name=name)
+    elif kind == "moe_ffn":
+        w = moe_ffn(seed, device=device, name=name)
     elif kind == "act":
         w = Workload(name, "act", M, 0, K)
         w.tensors["X"] = activations(M, K, seed, device=device)

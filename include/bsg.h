@@ -169,6 +169,52 @@ int quantize_fp8_per_token(const void* X, int64_t ldx, void* Q, int64_t ldq, int
 int quantize_fp4_per_token(const void* X, int64_t ldx, void* Q, int64_t ldq, int16_t* sf,
                            int64_t ld_sf, int64_t M, int64_t K, int32_t rule, void* stream);
 
+/* SwiGLU followed by FP8 1x128 quantisation (device kernel on `stream`), the step
+ * between the two grouped GEMMs of an MoE FFN (the pages list SwiGLU between the
+ * two grouped GEMMs of the fused MoE benchmark: third page, "Kernels de computacao:
+ * DeepGEMM-Ascend versus DeepGEMM", section "Execucao de MoE: MegaMoE e
+ * distribuicao de especialistas"; the function itself is not defined there, the
+ * textbook SwiGLU is the reading):
+ *   y[m][i] = silu(H[m][i]) * H[m][I + i],  silu(g) = g / (1 + e^-g),  0 <= i < I,
+ * formed in fp32, then quantised per 128-wide block of each row exactly as
+ * quantize_fp8_per_token does (same rules, codes and packed scales).
+ *   H: bf16 [M][ldh], ldh >= 2I (gate in columns [0, I), up in [I, 2I)).
+ *   Q: e4m3 [M][ldq] bytes, ldq >= I; sf: packed int16 [ceil(I/256)][ld_sf >= M].
+ *   Requires I % 128 == 0 plus the alignment rules of quantize_fp8_per_token (H
+ *   takes X's).  Because y is an fp32 result (a few ulps from the exact value), a
+ *   code whose exact value sits within that distance of a rounding boundary may
+ *   round either way. */
+int swiglu_quantize_fp8(const void* H, int64_t ldh, void* Q, int64_t ldq, int16_t* sf,
+                        int64_t ld_sf, int64_t M, int64_t I, int32_t rule, void* stream);
+
+/* MoE FFN core on one GPU (the expert computation of the fused MoE step named on
+ * the pages, without the dispatch / combine communication):
+ *   H = m_grouped_gemm_fp8(A, W13)          bf16 [M_total][2*inter]
+ *   (Y, sfy) = swiglu_quantize_fp8(H)       e4m3 [M_total][inter] + packed 1x128 scales
+ *   D = m_grouped_gemm_fp8(Y, W2)           bf16 [M_total][hidden]
+ * three launches on `stream`, with the same expert row ranges (group_offsets,
+ * device int32 [G+1]) in both GEMMs.
+ *   A: e4m3 [M_total][lda] tokens, hidden wide; sfa packed [ceil(hidden/256)][ld_sfa].
+ *   W13: e4m3 [G][2*inter][ldw13] (expert g at W13 + g*stride_w13 bytes; gate
+ *        rows [0, inter), up rows [inter, 2*inter)); sfw13 packed int16
+ *        [G][ceil(hidden/256)][ld_sfw13 >= ceil(2*inter/128)], expert stride
+ *        stride_sfw13 elements.
+ *   W2: e4m3 [G][hidden][ldw2] (K = inter); sfw2 packed [G][ceil(inter/256)][ld_sfw2].
+ *   H, Y, sfy: caller-owned workspace (the library allocates nothing), with
+ *        ldh >= 2*inter, ldy >= inter, ld_sfy >= M_total.
+ *   D: bf16 [M_total][ldd].  Rows outside [off[0], off[G]) of H, Y and D are not
+ *   meaningful.  Every argument of all three steps is checked before the first
+ *   launch; the requirements are those of the three calls above (hidden and inter
+ *   multiples of 128). */
+int moe_ffn_fp8(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
+                const void* W13, int64_t ldw13, int64_t stride_w13, const int16_t* sfw13,
+                int64_t ld_sfw13, int64_t stride_sfw13,
+                const void* W2, int64_t ldw2, int64_t stride_w2, const int16_t* sfw2,
+                int64_t ld_sfw2, int64_t stride_sfw2,
+                const int32_t* group_offsets, int32_t G, int64_t M_total, int64_t hidden,
+                int64_t inter, void* H, int64_t ldh, void* Y, int64_t ldy, int16_t* sfy,
+                int64_t ld_sfy, void* D, int64_t ldd, int32_t rule, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,7 +22,8 @@ def test_header_declares_the_api():
     names = _declared_functions()
     for n in ("gemm_bf16", "gemm_fp8_blockscaled", "gemm_fp4_blockscaled", "m_grouped_gemm_fp8",
               "pack_ue8m0_scales", "unpack_ue8m0_scales", "bsg_status_string",
-              "quantize_fp8_per_token", "quantize_fp4_per_token"):
+              "quantize_fp8_per_token", "quantize_fp4_per_token", "swiglu_quantize_fp8",
+              "moe_ffn_fp8"):
         assert n in names
 
 
@@ -173,6 +174,46 @@ def test_quantize_validation(name, gk, qalign):
     # empty problems are no-ops and need no pointers
     assert f(0, 0, 0, 0, 0, 0, 0, K, 0, None) == bsg.BSG_OK
     assert f(0, 0, 0, 0, 0, 0, 8, 0, 1, None) == bsg.BSG_OK
+
+
+def test_swiglu_validation():
+    f = bsg.lib().swiglu_quantize_fp8
+    I = 256
+    ok = [P, 2 * I, P2, I, P2 + 0x8000, 64, 64, I, 0, None]
+    a = list(ok); a[1] = 2 * I - 8                      # ldh < 2I
+    assert f(*a) == bsg.BSG_ERR_INVALID_ARG
+    a = list(ok); a[7] = 200                            # I % 128
+    assert f(*a) == bsg.BSG_ERR_UNSUPPORTED_SHAPE
+    a = list(ok); a[8] = 7
+    assert f(*a) == bsg.BSG_ERR_INVALID_ARG
+    a = list(ok); a[2] = P2 + 4                         # Q not 8-byte aligned
+    assert f(*a) == bsg.BSG_ERR_MISALIGNED
+    assert f(0, 0, 0, 0, 0, 0, 0, I, 0, None) == bsg.BSG_OK
+
+
+def test_moe_ffn_validation_launches_nothing_on_a_bad_late_argument():
+    """Every step's arguments are checked before the first launch: a bad
+    down-projection argument fails with fake (never dereferenced) pointers."""
+    f = bsg.lib().moe_ffn_fp8
+    hidden, inter, G, M = 512, 256, 4, 256
+    W13 = 0x100000
+    W2 = 0x400000
+    args = [P, hidden, P2, M,                                 # A, lda, sfa, ld_sfa
+            W13, hidden, 2 * inter * hidden, P2, 4, 4 * 2,     # W13, ldw13, stride, sfw13, ld, stride
+            W2, inter, hidden * inter, P2, 4, 4,               # W2 ...
+            P2, G, M, hidden, inter,                           # offsets, G, M_total, hidden, inter
+            0x800000, 2 * inter, 0x900000, inter, 0xA00000, M, # H, ldh, Y, ldy, sfy, ld_sfy
+            0xB00000, hidden, 0, None]                         # D, ldd, rule, stream
+    bad = list(args); bad[11] = inter - 16                   # ldw2 < inter
+    assert f(*bad) == bsg.BSG_ERR_INVALID_ARG
+    bad = list(args); bad[29] = 5                            # rule
+    assert f(*bad) == bsg.BSG_ERR_INVALID_ARG
+    bad = list(args); bad[22] = 2 * inter - 8                # ldh too small
+    assert f(*bad) == bsg.BSG_ERR_INVALID_ARG
+    bad = list(args); bad[20] = 200                          # inter % 128
+    assert f(*bad) == bsg.BSG_ERR_UNSUPPORTED_SHAPE
+    empty = list(args); empty[18] = 0                        # M_total = 0: no-op
+    assert f(*empty) == bsg.BSG_OK
 
 
 def test_binding_refuses_cpu_tensors():
