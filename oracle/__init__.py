@@ -17,7 +17,7 @@ e4m3 or e2m1 codes with UE8M0 block scales.
 Parity status of each function (what pins it is in ``tests/test_oracle_pins.py``
 and ``tests/test_quantize_pins.py``):
   decoders, bf16 rounding, pack/unpack, dense BF16/FP8/FP4, grouped FP8,
-  per-token quantisation: pinned.
+  masked grouped FP8, per-token quantisation: pinned.
 """
 from __future__ import annotations
 
@@ -289,6 +289,28 @@ def grouped_fp8(A, sfa, B, sfb, offsets, rows=None, cols=None) -> np.ndarray:
                 (_ptr(A), _ld(A), _ptr(sfa), _ld(sfa), _ptr(B), K, N * K,
                  _ptr(sfb), sfb.shape[2], sfb.shape[1] * sfb.shape[2], _ptr(off), G, K),
                 rows, cols)
+
+
+def masked_fp8(A, sfa, B, sfb, masked_m, max_m: int, rows=None, cols=None) -> np.ndarray:
+    """Masked M-grouped FP8 GEMM.  Expert g owns rows [g*max_m, (g+1)*max_m) of A
+    (uint8 [G*max_m][K]) and of D; the first m_g = min(max(masked_m[g], 0), max_m)
+    of them are computed as A_row x B[g]^T (B uint8 [G][N][K], sfb packed
+    [G][ceil(K/256)][>=ceil(N/128)]; sfa packed over all G*max_m rows).  Rows
+    past m_g come back as NaN."""
+    A = _c2d(A, np.uint8)
+    B = np.asarray(B)
+    sfb = np.asarray(sfb)
+    G = B.shape[0]
+    m = np.clip(np.asarray(masked_m, dtype=np.int64), 0, max_m)
+    rows = _sel(rows, G * max_m)
+    cols = _sel(cols, B.shape[1])
+    out = np.full((rows.size, cols.size), np.nan)
+    g_of = rows // max_m
+    valid = (rows - g_of * max_m) < m[g_of]
+    for g in np.unique(g_of[valid]):
+        sel = np.nonzero(valid & (g_of == g))[0]
+        out[sel] = gemm_fp8(A, sfa, B[g], sfb[g], rows=rows[sel], cols=cols)
+    return out
 
 
 def row_norms(fmt: str, data, sf=None, K: int | None = None, rows=None,

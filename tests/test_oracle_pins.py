@@ -510,3 +510,26 @@ def test_grouped_expert_selection_scale_only(orc):
     assert np.all(D[:128] == 128.0 * 1)
     assert np.all(D[128:256] == 128.0 * 4)      # expert 2
     assert np.all(D[256:384] == 128.0 * 8)      # expert 3
+
+
+def test_masked_is_grouped_over_fixed_capacity(orc):
+    """The masked layout reduces to the (pinned) contiguous grouped GEMM with
+    offsets g*max_m on the valid rows; rows past each expert's count are not
+    computed; counts clamp to [0, max_m]."""
+    from block_scaled_precision_05_amd import workloads
+    G, cap, N, K = 4, 64, 96, 256
+    w = workloads.grouped(G, N, K, seed=12, counts=[cap] * G, align=cap)
+    A = w.tensors["A"].numpy()
+    sfa = orc.pack_scales(w.tensors["sfa"].numpy())
+    B = w.tensors["B"].numpy()
+    sfb = np.stack([orc.pack_scales(x) for x in w.tensors["sfb"].numpy()])
+    off = np.arange(G + 1, dtype=np.int32) * cap
+    full = orc.grouped_fp8(A, sfa, B, sfb, off)
+    masked = np.array([-3, 17, cap, cap + 9], dtype=np.int32)   # clamp to 0, 17, 64, 64
+    got = orc.masked_fp8(A, sfa, B, sfb, masked, cap)
+    m = np.clip(masked, 0, cap)
+    for g in range(G):
+        r = np.arange(g * cap, (g + 1) * cap)
+        ok = r - g * cap < m[g]
+        assert np.array_equal(got[r[ok]], full[r[ok]])
+        assert np.all(np.isnan(got[r[~ok]]))
