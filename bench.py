@@ -1,7 +1,7 @@
 """Benchmark of the block-scaled GEMM library on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--dtypes bf16,fp8,fp4,grouped,quant_fp8,quant_fp4,quant_fp8_moe,moe_ffn]
+                    [--dtypes bf16,fp8,fp4,grouped,quant_fp8,quant_fp4,quant_fp8_moe,moe_ffn,masked]
 
 Workload: D = A * B^T at M=4096, N=7168, K=16384, the dense shape the pages time
 (431 TFLOPS BF16 on the other accelerator: "DeepSeek lanza kernels de DeepGEMM
@@ -30,6 +30,10 @@ down-projection) runs on one GPU's share of the pages' fused MoE case: 48 of 384
 experts (EP8) plus the shared expert, 16384 tokens top-6, hidden 7168,
 intermediate 2048; TFLOPS count useful (unpadded) rows.
 
+The masked M-grouped FP8 GEMM runs a decode-sized case: 48 local experts of
+384, capacity 512 rows, N=4096, K=7168, counts from 4096 tokens top-6; it is
+bound by reading the experts' weights, so GB/s is reported beside TFLOPS.
+
 `cpu_baseline` times the CPU oracle (plain C, fp64) on a bounded row sample of
 the BF16 workload on this host's cores.
 """
@@ -51,7 +55,8 @@ if ROOT not in sys.path:
 METRIC = "TFLOPS and % of MI355X dense MFMA peak, GEMM 4096×7168×16384 per dtype"
 
 # MI355X published dense MFMA peaks (TFLOP/s).
-PEAK = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0, "grouped": 5000.0, "moe_ffn": 5000.0}
+PEAK = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0, "grouped": 5000.0, "moe_ffn": 5000.0,
+        "masked": 5000.0}
 # MI355X published HBM3E bandwidth (GB/s): the bound of the quantisers.
 HBM_PEAK_GBS = 8000.0
 QUANT_KINDS = ("quant_fp8", "quant_fp4", "quant_fp8_moe")
@@ -67,6 +72,7 @@ KERNEL_NAME = {
     "quant_fp4": "quant_kernel<1, 0, 32, 2, 0>",
     "quant_fp8_moe": "quant_kernel<0, 0, 32, 2, 0>",
     "moe_ffn": "gemm_kernel<1, 128, 512, 1, 4, 64, 4, 1, true> x2 + swiglu_quant_kernel<0>",
+    "masked": "gemm_kernel<1, 128, 512, 1, 4, 64, 4, 1, true>",
 }
 
 
@@ -121,7 +127,7 @@ def make_case(kind, dev):
 
     name = {"bf16": "bf16_large", "fp8": "fp8_large", "fp4": "fp4_large",
             "grouped": "moe_fp8", "quant_fp8": "act_large", "quant_fp4": "act_large",
-            "quant_fp8_moe": "act_moe", "moe_ffn": "moe_ffn"}[kind]
+            "quant_fp8_moe": "act_moe", "moe_ffn": "moe_ffn", "masked": "masked_fp8"}[kind]
     w = workloads.make(name, device=dev)
     t = w.tensors
     M, N, K = w.M, w.N, w.K
@@ -149,6 +155,20 @@ def make_case(kind, dev):
                 "bytes_per_call": nbytes}
         meta.update({"M": M, "K": K})
         return call, 0.0, nbytes, meta
+    if kind == "masked":
+        A, B, m = t["A"], t["B"], t["masked_m"]
+        G, cap, _ = A.shape
+        sfa = bsg.ensure_packed(t["sfa"], G * cap, K // 128)
+        sfb = torch.stack([bsg.ensure_packed(x, (N + 127) // 128, K // 128) for x in t["sfb"]])
+        D = torch.empty(G, cap, N, dtype=torch.bfloat16, device=dev)
+        call = lambda: bsg.m_grouped_gemm_fp8_masked(A, sfa, B, sfb, m, out=D)
+        useful = w.meta["useful_rows"]
+        nbytes = B.numel() + useful * K + 2 * useful * N + 2 * sfb.numel()
+        meta = {"experts": G, "capacity": cap, "useful_rows": useful, "routing": w.meta["routing"],
+                "bytes_per_call": nbytes,
+                "note": "decode-sized: the weights dominate, so HBM bounds it (see gb_per_s)"}
+        meta.update({"M": G * cap, "N": N, "K": K})
+        return call, w.flops, nbytes, meta
     if kind == "moe_ffn":
         G, two_i, hidden = t["W13"].shape
         inter = two_i // 2
@@ -291,6 +311,9 @@ def summarize(kind, r, steps):
         "tflop_per_call": r["flops"] / 1e12,
         "min_hbm_mb": r["min_bytes"] / 1e6,
     }
+    if kind == "masked":
+        out["gb_per_s"] = r["min_bytes"] * steps / r["wall_s"] / 1e9
+        out["frac_of_hbm_peak"] = out["gb_per_s"] / HBM_PEAK_GBS
     if "cold_us" in r:
         c = sorted(r["cold_us"])
         out["cold_l2_us_median"] = statistics.median(c)
@@ -330,7 +353,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--dtypes",
-                    default="bf16,fp8,fp4,grouped,quant_fp8,quant_fp4,quant_fp8_moe,moe_ffn")
+                    default="bf16,fp8,fp4,grouped,quant_fp8,quant_fp4,quant_fp8_moe,moe_ffn,masked")
     ap.add_argument("--cold-samples", type=int, default=10)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle time for cpu_baseline (0 disables it)")

@@ -9,6 +9,7 @@ if ``libbsg.so`` is missing or cannot be loaded, every call raises.
     D = gemm_fp8_blockscaled(A, sfa, B, sfb)    # e4m3 with UE8M0 1x128 / 128x128 scales
     D = gemm_fp4_blockscaled(A, sfa, B, sfb)    # e2m1 (2 per byte) with UE8M0 1x32 scales
     D = m_grouped_gemm_fp8(A, sfa, B, sfb, offsets)
+    D = m_grouped_gemm_fp8_masked(A, sfa, B, sfb, masked_m)   # A [G, max_m, K], counts on the GPU
     P = pack_ue8m0_scales(sf)                   # uint8 [mn, kb] -> int16 [ceil(kb/2), mn]
     sf = unpack_ue8m0_scales(P, mn, kb)
     P = ensure_packed(sf, mn, kb)               # reuse if already packed, else pack
@@ -51,6 +52,8 @@ EXPORTS = {
                              _i64, _i64, _i64, _vp],
     "m_grouped_gemm_fp8": [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64,
                            _vp, _i32, _i64, _i64, _i64, _vp],
+    "m_grouped_gemm_fp8_masked": [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp,
+                                  _i64, _vp, _i32, _i64, _i64, _i64, _vp],
     "pack_ue8m0_scales": [_vp, _i64, _i64, _i64, _vp, _i64, _vp],
     "unpack_ue8m0_scales": [_vp, _i64, _i64, _i64, _vp, _i64, _vp],
     "quantize_fp8_per_token": [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i32, _vp],
@@ -220,6 +223,37 @@ def m_grouped_gemm_fp8(A, sfa, B, sfb, offsets, out=None, stream=None):
         _ptr(sfb), sfb.stride(1), sfb.stride(0), _ptr(D), _mat(D, "out"), _ptr(offsets), G, M, N,
         K, _stream(stream)))
     return D
+
+
+def m_grouped_gemm_fp8_masked(A, sfa, B, sfb, masked_m, out=None, stream=None):
+    """Masked M-grouped FP8 GEMM.  A e4m3 [G, max_m, K]; B e4m3 [G, N, K]; sfa packed
+    int16 [ceil(K/256), >=G*max_m] over the G*max_m rows; sfb packed int16
+    [G, ceil(K/256), >=ceil(N/128)]; masked_m int32 [G] on the GPU.  Returns D bf16
+    [G, max_m, N]; rows r >= masked_m[g] of expert g are left untouched."""
+    _dev(A, sfa, B, sfb, masked_m, out)
+    A, B = _bytes_u8(A), _bytes_u8(B)
+    if A.dim() != 3 or B.dim() != 3 or sfb.dim() != 3:
+        raise ValueError("A must be [G, max_m, K], B [G, N, K] and sfb [G, kp, ld]")
+    if masked_m.dtype != torch.int32 or masked_m.dim() != 1 or not masked_m.is_contiguous():
+        raise TypeError("masked_m must be a contiguous int32 vector")
+    G, max_m, K = A.shape
+    N = B.shape[1]
+    if B.shape[0] != G or B.shape[2] != K or masked_m.numel() != G:
+        raise ValueError("A, B and masked_m disagree on G or K")
+    if A.stride(2) != 1 or A.stride(0) != max_m * A.stride(1):
+        raise ValueError("A's experts must be stacked rows of one [G*max_m, K] matrix")
+    if B.stride(2) != 1 or sfb.stride(2) != 1 or sfb.dtype != torch.int16:
+        raise ValueError("B and sfb must be contiguous along their last dimension")
+    if out is None:
+        out = torch.empty((G, max_m, N), dtype=torch.bfloat16, device=A.device)
+    if out.dtype != torch.bfloat16 or out.dim() != 3 or out.stride(2) != 1 or \
+            out.stride(0) != max_m * out.stride(1) or out.shape[1] != max_m or out.shape[2] < N:
+        raise ValueError("out must be bfloat16 [G, max_m, >=N] stacked rows")
+    _check("m_grouped_gemm_fp8_masked", lib().m_grouped_gemm_fp8_masked(
+        _ptr(A), A.stride(1), _ptr(sfa), _packed(sfa, "sfa"), _ptr(B), B.stride(1), B.stride(0),
+        _ptr(sfb), sfb.stride(1), sfb.stride(0), _ptr(out), out.stride(1), _ptr(masked_m), G,
+        max_m, N, K, _stream(stream)))
+    return out
 
 
 def pack_ue8m0_scales(sf: torch.Tensor, ld_packed: int | None = None, out=None, stream=None):

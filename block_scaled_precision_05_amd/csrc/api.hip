@@ -276,6 +276,43 @@ int m_grouped_gemm_fp8(const void* A, int64_t lda, const int16_t* sfa, int64_t l
   return launch<KIND_FP8, BSG_GROUPED_CFG, true>(a, (hipStream_t)stream);
 }
 
+int m_grouped_gemm_fp8_masked(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
+                              const void* B, int64_t ldb, int64_t stride_b,
+                              const int16_t* sfb, int64_t ld_sfb, int64_t stride_sfb,
+                              void* D, int64_t ldd, const int32_t* masked_m, int32_t G,
+                              int64_t max_m, int64_t N, int64_t K, void* stream) {
+  if (max_m < 0) return BSG_ERR_INVALID_ARG;
+  if (G > 0 && max_m > kMaxDim / G) return BSG_ERR_UNSUPPORTED_SHAPE;
+  const int64_t M_total = (int64_t)(G > 0 ? G : 0) * max_m;
+  const int st = grouped_fp8_check(A, lda, sfa, ld_sfa, B, ldb, stride_b, sfb, ld_sfb, stride_sfb, D,
+                                   ldd, masked_m, G, M_total, N, K);
+  if (st != BSG_OK || M_total == 0 || N == 0 || G == 0) return st;
+  const int64_t kp = (K / 128 + 1) / 2;
+  GemmArgs a = {};
+  a.A = (const uint8_t*)A;
+  a.B = (const uint8_t*)B;
+  a.D = (uint16_t*)D;
+  a.sfa = sfa;
+  a.sfb = sfb;
+  a.offsets = masked_m;
+  a.cap = (int32_t)max_m;
+  a.lda = lda;
+  a.ldb = ldb;
+  a.ldd = ldd;
+  a.ld_sfa = ld_sfa;
+  a.ld_sfb = ld_sfb;
+  a.stride_b = stride_b;
+  a.stride_sfb = stride_sfb;
+  a.M = (int32_t)M_total;
+  a.N = (int32_t)N;
+  a.K = (int32_t)K;
+  a.k_bytes = (int32_t)K;
+  a.kp_count = (int32_t)kp;
+  a.sfb_rows = (int32_t)((N + 127) / 128);
+  a.G = G;
+  return launch<KIND_FP8, BSG_GROUPED_CFG, true>(a, (hipStream_t)stream);
+}
+
 static int launch_pack(bool unpack, const void* src, int64_t mn, int64_t kb, int64_t ld_src,
                        void* dst, int64_t ld_dst, void* stream) {
   const int64_t total = (kb + 1) / 2 * mn;

@@ -76,6 +76,8 @@ struct GemmArgs {
   int32_t tiles_n;
   int32_t G;                // grouped: number of experts
   int32_t d_vec;            // 1 when D rows allow 8-byte stores (D and ldd*2 8-aligned)
+  int32_t cap;              // grouped: 0 = contiguous experts, rows [offsets[g], offsets[g+1]);
+                            // > 0 = masked layout, rows [g*cap, g*cap + min(offsets[g], cap))
 };
 
 // Buffer resource word 3 for raw (unswizzled, stride 0) byte-addressed buffers on
@@ -257,19 +259,34 @@ struct GroupCursor {
   int before;
 };
 
+// Rows of expert g: [off[g], off[g+1]) in the contiguous layout, or, in the masked
+// layout (cap > 0, off = per-expert valid counts), the first min(off[g], cap) of
+// its cap rows.
+__device__ __forceinline__ void group_range(const int32_t* off, int g, int cap, int& lo, int& hi) {
+  if (cap > 0) {
+    const int m = off[g];
+    lo = g * cap;
+    hi = lo + (m < 0 ? 0 : (m > cap ? cap : m));
+  } else {
+    lo = off[g];
+    hi = off[g + 1];
+  }
+}
+
 template <int BM>
-__device__ __forceinline__ int group_tiles(const int32_t* off, int g, int G) {
+__device__ __forceinline__ int group_tiles(const int32_t* off, int g, int G, int cap) {
   if (g >= G) return 0;
-  int lo = off[g], hi = off[g + 1];
+  int lo, hi;
+  group_range(off, g, cap, lo, hi);
   return hi > lo ? (hi - lo + BM - 1) / BM : 0;
 }
 
 // Total row tiles over all experts.
 template <int BM>
-__device__ int grouped_total_row_tiles(const int32_t* off, int G) {
+__device__ int grouped_total_row_tiles(const int32_t* off, int G, int cap) {
   int total = 0;
   for (int g0 = 0; g0 < G; g0 += 64) {
-    int t = group_tiles<BM>(off, g0 + (threadIdx.x & 63), G);
+    int t = group_tiles<BM>(off, g0 + (threadIdx.x & 63), G, cap);
     int s = wave_incl_scan(t);
     total += __shfl(s, 63, 64);
   }
@@ -278,11 +295,11 @@ __device__ int grouped_total_row_tiles(const int32_t* off, int G) {
 
 // Finds the expert owning row tile `rt`; returns false when rt is past the end.
 template <int BM>
-__device__ bool grouped_find(const int32_t* off, int G, int rt, GroupCursor& cur, int& g,
+__device__ bool grouped_find(const int32_t* off, int G, int cap, int rt, GroupCursor& cur, int& g,
                              int& row_lo, int& row_hi) {
   const int lane = threadIdx.x & 63;
   while (cur.g0 < G) {
-    int t = group_tiles<BM>(off, cur.g0 + lane, G);
+    int t = group_tiles<BM>(off, cur.g0 + lane, G, cap);
     int incl = wave_incl_scan(t) + cur.before;
     uint64_t hit = __ballot(incl > rt);
     if (hit) {
@@ -291,9 +308,9 @@ __device__ bool grouped_find(const int32_t* off, int G, int rt, GroupCursor& cur
       int t_j = __shfl(t, j, 64);
       g = cur.g0 + j;
       int tile_in_g = rt - (incl_j - t_j);
-      int base = off[g];
+      int base, end;
+      group_range(off, g, cap, base, end);
       row_lo = base + tile_in_g * BM;
-      int end = off[g + 1];
       row_hi = row_lo + BM < end ? row_lo + BM : end;
       return true;
     }
@@ -386,7 +403,7 @@ void gemm_kernel(const GemmArgs args) {
   int total_tiles;
   GroupCursor cur{0, 0};
   if constexpr (GROUPED) {
-    total_tiles = grouped_total_row_tiles<BM>(args.offsets, args.G) * args.tiles_n;
+    total_tiles = grouped_total_row_tiles<BM>(args.offsets, args.G, args.cap) * args.tiles_n;
   } else {
     total_tiles = args.tiles_m * args.tiles_n;
   }
@@ -428,7 +445,7 @@ void gemm_kernel(const GemmArgs args) {
       const int rt = p / args.tiles_n;
       n0 = (p - rt * args.tiles_n) * BN;
       int g;
-      if (!grouped_find<BM>(args.offsets, args.G, rt, cur, g, m0, m_end)) break;
+      if (!grouped_find<BM>(args.offsets, args.G, args.cap, rt, cur, g, m0, m_end)) break;
       Bbase += (int64_t)g * args.stride_b;
       sfb += (int64_t)g * args.stride_sfb;
     } else {

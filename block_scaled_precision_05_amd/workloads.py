@@ -20,6 +20,8 @@ para calculo e comunicacao de IA", section "Resultados de kernel e comunicacao")
   fp4_large     FP4 4096x7168x16384, 1x32 UE8M0 scales on both operands
   act_large     bf16 activations 4096x16384 (A of the dense shape), to be quantised
   act_moe       bf16 activations 16384x7168 (the MoE tokens), to be quantised
+  masked_fp8    masked M-grouped FP8 (decode): 48 local experts of 384 (EP8),
+                capacity 512 rows each, N=4096, K=7168, 4096 tokens top-6
   moe_ffn       MoE FFN core on one GPU's share of the pages' fused MoE case:
                 384 experts over EP8 -> 48 local experts plus the shared expert,
                 16384 tokens top-6, hidden 7168, intermediate 2048
@@ -40,6 +42,9 @@ Value recipes:
     (48 of them), plus one shared expert that every token visits; counts padded
     to multiples of 128.  W13 [G][2*inter][hidden] (gate rows first) and W2
     [G][hidden][inter] follow the FP8 recipe with 128x128 scales.
+  * Masked layout: expert g owns rows [g*cap, (g+1)*cap) of A; its valid count is
+    the rank-0 share of a Zipf(1.1) top-6 routing of the decode tokens, capped at
+    cap; rows past the count hold random codes too (the GEMM must ignore them).
   * Activations (bf16, input of the per-token quantiser): x ~ N(0,1) times a
     per-row power of two 2^U{-6..6}; one column in 64 (a seeded choice) is an
     outlier channel scaled by 32; the last ``zero_rows`` rows are zero.
@@ -167,6 +172,8 @@ class Workload:
         """Algorithmic flops, 2*M*N*K (useful rows only for the grouped case)."""
         if self.kind == "grouped_fp8":
             return 2.0 * float(self.meta["useful_rows"]) * self.N * self.K
+        if self.kind == "masked_fp8":
+            return 2.0 * float(self.meta["useful_rows"]) * self.N * self.K
         if self.kind == "moe_ffn":
             return float(self.meta["useful_flops"])
         return 2.0 * self.M * self.N * self.K
@@ -182,6 +189,7 @@ SHAPES = {
     "act_large": ("act", 4096, None, 16384, 1007),
     "act_moe": ("act", 16384, None, 7168, 1008),
     "moe_ffn": ("moe_ffn", None, None, None, 1009),
+    "masked_fp8": ("masked_fp8", None, 4096, 7168, 1010),
 }
 
 
@@ -241,6 +249,32 @@ def grouped(G: int, N: int, K: int, seed: int, device="cpu", counts=None, name="
     return w
 
 
+def masked(seed: int, device="cpu", G: int = 48, cap: int = 512, N: int = 4096, K: int = 7168,
+           experts: int = 384, tokens: int = 4096, topk: int = 6, zipf: float = 1.1, counts=None,
+           name: str = "custom"):
+    """Masked M-grouped FP8 inputs (recipe in the module docstring)."""
+    g = _gen(device, seed)
+    if counts is None:
+        all_counts = moe_counts(g, device, tokens=tokens, topk=topk, experts=experts, zipf=zipf)
+        counts = all_counts[:G].clamp(max=cap)
+    else:
+        counts = torch.as_tensor(list(counts), dtype=torch.int64, device=device)
+    A, sfa = fp8_operand(G * cap, K, 1, g, device)
+    Bs, sfbs = [], []
+    for _ in range(G):
+        b, sb = fp8_operand(N, K, 128, g, device)
+        Bs.append(b)
+        sfbs.append(sb)
+    w = Workload(name, "masked_fp8", G * cap, N, K)
+    w.tensors.update(A=A.view(G, cap, K), sfa=sfa, B=torch.stack(Bs), sfb=torch.stack(sfbs),
+                     masked_m=counts.to(torch.int32))
+    useful = int(counts.clamp(min=0, max=cap).sum().item())
+    w.meta.update(seed=seed, G=G, cap=cap, useful_rows=useful,
+                  routing=f"{G} of {experts} experts, multinomial({tokens}x{topk}), zipf {zipf}, "
+                          f"capacity {cap}")
+    return w
+
+
 def moe_ffn(seed: int, device="cpu", hidden: int = 7168, inter: int = 2048, experts: int = 384,
             ranks: int = 8, rank: int = 0, shared: int = 1, tokens: int = 16384, topk: int = 6,
             zipf: float = 1.1, counts=None, name: str = "custom", align: int = 128):
@@ -296,6 +330,8 @@ def make(name: str, device="cpu", seed: int | None = None) -> Workload:
         w = grouped(256, N, K, seed, device=device, name=name)
     elif kind == "moe_ffn":
         w = moe_ffn(seed, device=device, name=name)
+    elif kind == "masked_fp8":
+        w = masked(seed, device=device, N=N, K=K, name=name)
     elif kind == "act":
         w = Workload(name, "act", M, 0, K)
         w.tensors["X"] = activations(M, K, seed, device=device)

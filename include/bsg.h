@@ -125,6 +125,25 @@ int m_grouped_gemm_fp8(const void* A, int64_t lda, const int16_t* sfa, int64_t l
                        void* D, int64_t ldd, const int32_t* group_offsets, int32_t G,
                        int64_t M_total, int64_t N, int64_t K, void* stream);
 
+/* Masked M-grouped FP8 GEMM: every expert owns a fixed capacity of max_m rows and
+ * a device-side count of valid rows (the pages list masked grouped GEMM among
+ * the interfaces the reference repository declares but leaves unimplemented:
+ * first page, "Cobertura de operacoes e a lacuna declarada no repositorio").
+ * The layout reading: A is [G][max_m][K] viewed as [G*max_m][lda] rows, D is
+ * [G][max_m][N] viewed as [G*max_m][ldd]; sfa packs the scales of all G*max_m
+ * rows (ld_sfa >= G*max_m), exactly what quantize_fp8_per_token writes for that
+ * view.  For expert g and r < m_g = min(max(masked_m[g], 0), max_m):
+ *     D[g*max_m + r][n] = bf16( sum_k a[g*max_m + r][k] * 2^(sa-127) * b_g[n][k] * 2^(sb_g-127) )
+ * with B_g, sfb_g as in m_grouped_gemm_fp8.  Rows r >= m_g are not written.
+ *   masked_m: DEVICE int32 [G] (read by the kernel; no host synchronisation).
+ *   G == 0 or max_m == 0 is a no-op.  Requires G * max_m < 2^31 plus the
+ *   requirements of m_grouped_gemm_fp8 with M_total = G * max_m. */
+int m_grouped_gemm_fp8_masked(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
+                              const void* B, int64_t ldb, int64_t stride_b,
+                              const int16_t* sfb, int64_t ld_sfb, int64_t stride_sfb,
+                              void* D, int64_t ldd, const int32_t* masked_m, int32_t G,
+                              int64_t max_m, int64_t N, int64_t K, void* stream);
+
 /* Pack UE8M0 scales (device kernel on `stream`):
  *   sf: uint8 [mn][ld_sf], K-blocks contiguous (kb of them per scale row)
  *   -> packed: int16 [ceil(kb/2)][ld_packed], MN-major, as described above.

@@ -23,7 +23,7 @@ def test_header_declares_the_api():
     for n in ("gemm_bf16", "gemm_fp8_blockscaled", "gemm_fp4_blockscaled", "m_grouped_gemm_fp8",
               "pack_ue8m0_scales", "unpack_ue8m0_scales", "bsg_status_string",
               "quantize_fp8_per_token", "quantize_fp4_per_token", "swiglu_quantize_fp8",
-              "moe_ffn_fp8"):
+              "moe_ffn_fp8", "m_grouped_gemm_fp8_masked"):
         assert n in names
 
 
@@ -213,6 +213,27 @@ def test_moe_ffn_validation_launches_nothing_on_a_bad_late_argument():
     bad = list(args); bad[20] = 200                          # inter % 128
     assert f(*bad) == bsg.BSG_ERR_UNSUPPORTED_SHAPE
     empty = list(args); empty[18] = 0                        # M_total = 0: no-op
+    assert f(*empty) == bsg.BSG_OK
+
+
+def test_masked_validation():
+    f = bsg.lib().m_grouped_gemm_fp8_masked
+    G, cap, N, K = 4, 128, 256, 512
+    args = [P, K, P2, G * cap, 0x100000, K, N * K, P2, 2, 2 * 2,
+            0x900000, N, P2, G, cap, N, K, None]
+    bad = list(args); bad[14] = -1                        # max_m < 0
+    assert f(*bad) == bsg.BSG_ERR_INVALID_ARG
+    bad = list(args); bad[3] = G * cap - 1                # ld_sfa < G*max_m
+    assert f(*bad) == bsg.BSG_ERR_INVALID_ARG
+    bad = list(args); bad[12] = 0                         # no counts
+    assert f(*bad) == bsg.BSG_ERR_INVALID_ARG
+    bad = list(args); bad[16] = 100                       # K % 128
+    assert f(*bad) == bsg.BSG_ERR_UNSUPPORTED_SHAPE
+    bad = list(args); bad[14] = 1 << 30                   # G * max_m >= 2^31
+    assert f(*bad) == bsg.BSG_ERR_UNSUPPORTED_SHAPE
+    empty = list(args); empty[14] = 0                     # max_m = 0: no-op
+    assert f(*empty) == bsg.BSG_OK
+    empty = list(args); empty[13] = 0                     # G = 0: no-op
     assert f(*empty) == bsg.BSG_OK
 
 
