@@ -78,9 +78,9 @@ static int num_cus() {
   return g_num_cus[dev];
 }
 
-template <int KIND, int BM, int BN, int WM, int WN, int SB, int NS, int PR, bool GROUPED>
+template <int KIND, int BM, int BN, int WM, int WN, int SB, int NS, int PR, bool GROUPED, int SV = 0>
 static int launch(GemmArgs a, hipStream_t stream) {
-  using T = GemmTile<KIND, BM, BN, WM, WN, SB, NS, PR>;
+  using T = GemmTile<KIND, BM, BN, WM, WN, SB, NS, PR, SV>;
   a.d_vec = (((uintptr_t)a.D & 7) == 0 && (a.ldd % 4) == 0) ? 1 : 0;
   a.tiles_m = (a.M + BM - 1) / BM;
   a.tiles_n = (a.N + BN - 1) / BN;
@@ -93,7 +93,7 @@ static int launch(GemmArgs a, hipStream_t stream) {
     grid = (int)(tiles < num_cus() ? tiles : num_cus());
   }
   (void)hipGetLastError();
-  hipLaunchKernelGGL((gemm_kernel<KIND, BM, BN, WM, WN, SB, NS, PR, GROUPED>), dim3(grid), dim3(T::NT), 0,
+  hipLaunchKernelGGL((gemm_kernel<KIND, BM, BN, WM, WN, SB, NS, PR, GROUPED, SV>), dim3(grid), dim3(T::NT), 0,
                      stream, a);
   return hipGetLastError() == hipSuccess ? BSG_OK : BSG_ERR_HIP;
 }
@@ -240,7 +240,12 @@ int gemm_fp4_blockscaled(const void* A, int64_t lda, const int16_t* sfa, int64_t
   a.k_bytes = (int32_t)(K / 2);
   a.kp_count = (int32_t)((K / 32 + 1) / 2);
   a.sfb_rows = (int32_t)N;
-  return launch<KIND_FP4, BSG_FP4_CFG, false>(a, (hipStream_t)stream);
+  // 8-byte scale loads when both packed arrays allow them (8-byte aligned, leading
+  // dimensions multiples of 4 int16), 2-byte loads otherwise.
+  const bool sv = ((uintptr_t)sfa % 8 == 0) && ((uintptr_t)sfb % 8 == 0) && (ld_sfa % 4 == 0) &&
+                  (ld_sfb % 4 == 0);
+  if (sv) return launch<KIND_FP4, BSG_FP4_CFG, false, 1>(a, (hipStream_t)stream);
+  return launch<KIND_FP4, BSG_FP4_CFG, false, 0>(a, (hipStream_t)stream);
 }
 
 int m_grouped_gemm_fp8(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,

@@ -49,6 +49,7 @@ typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(8))) int i32x8_t;
 typedef __attribute__((ext_vector_type(4))) int i32x4_t;
 typedef __attribute__((ext_vector_type(2))) int i32x2_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 
 // Kernel arguments (by value).  Leading dimensions are in bytes here.
 struct GemmArgs {
@@ -105,6 +106,14 @@ __device__ __forceinline__ f32x16_t mfma_scaled(i32x8_t b, i32x8_t a, f32x16_t c
                                                          (int)sa);
 }
 
+// Scaled MFMA with separate byte selects for the B and A scale words.
+template <int FMT, int SELB, int SELA>
+__device__ __forceinline__ f32x16_t mfma_scaled2(i32x8_t b, i32x8_t a, f32x16_t c, uint32_t sb,
+                                                 uint32_t sa) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, FMT, FMT, SELB, (int)sb, SELA,
+                                                         (int)sa);
+}
+
 // Compile-time shape of one kernel instance.
 //   BM x BN   workgroup tile, WM x WN waves (one per SIMD), each wave TM x TN made
 //             of 32x32 MFMA fragments (FM x FN of them);
@@ -119,7 +128,7 @@ __device__ __forceinline__ f32x16_t mfma_scaled(i32x8_t b, i32x8_t a, f32x16_t c
 //             its copies are spread over the next 2J k-steps (one chunk per
 //             k-step): a copy instruction waits in the address unit, and in-order
 //             issue makes the MFMAs behind it wait too, so copies must trickle.
-template <int KIND, int BM, int BN, int WM, int WN, int SB, int NS, int PR>
+template <int KIND, int BM, int BN, int WM, int WN, int SB, int NS, int PR, int SV = 0>
 struct GemmTile {
   static constexpr int NW = WM * WN;
   static constexpr int NT = NW * 64;
@@ -152,7 +161,20 @@ struct GemmTile {
   // packed scale words per lane per fragment per stage: FP8 one (the K-block's
   // pair), FP4 NC/4 (lane group lg takes NC/2 K-blocks of 32)
   static constexpr int SW = KIND == KIND_BF16 ? 0 : (KIND == KIND_FP8 ? 1 : NC / 4);
-  static constexpr int NSC = (FM + NSB) * SW;
+  // FP4 permutes the rows of every 128-row wave block, A and B alike: LDS slot
+  // 32f + i (fragment f, lane row i) holds tile row 4i + f.  A lane's four
+  // fragment rows are then adjacent in memory, and so are their packed scale
+  // words: SV = 1 fetches them with one 8-byte load per operand and stage (the
+  // arrays must be 8-byte aligned, with leading dimensions that are multiples of
+  // 4), SV = 0 with four 2-byte loads.
+  static constexpr bool PERM = KIND == KIND_FP4;
+  static_assert(!PERM || (FM == 4 && FN == 4 && SW == 1),
+                "the FP4 row permutation needs 128-row wave blocks and 64-byte stages");
+  static_assert(SV == 0 || PERM, "vector scale loads need the FP4 row permutation");
+  static constexpr int perm(int x) {
+    return PERM ? ((x & ~127) | ((x & 31) << 2) | ((x >> 5) & 3)) : x;
+  }
+  static constexpr int NSC = SV ? 2 * SW : (FM + NSB) * SW;
   static constexpr int VMEM_PER_STAGE = N_DMA + NSC;
   static_assert(SB == 64 || SB == 128, "a stage is 64 or 128 bytes of K per row");
   static_assert(NS >= 2 && NS <= 8, "ring of 2..8 stages");
@@ -384,10 +406,10 @@ __device__ __forceinline__ void ring_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int KIND, int BM, int BN, int WM, int WN, int SB, int NS, int PR, bool GROUPED>
+template <int KIND, int BM, int BN, int WM, int WN, int SB, int NS, int PR, bool GROUPED, int SV = 0>
 __global__ __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(const GemmArgs args) {
-  using T = GemmTile<KIND, BM, BN, WM, WN, SB, NS, PR>;
+  using T = GemmTile<KIND, BM, BN, WM, WN, SB, NS, PR, SV>;
   constexpr int FM = T::FM, FN = T::FN, J = T::J, RPF = T::RPF, NC = T::NC, SW = T::SW;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
 
@@ -467,10 +489,11 @@ void gemm_kernel(const GemmArgs args) {
         make_rsrc(args.A + (int64_t)m0 * args.lda, (uint32_t)((rows_a - 1) * args.lda + args.k_bytes));
     const __amdgpu_buffer_rsrc_t rb =
         make_rsrc(Bbase + (int64_t)n0 * args.ldb, (uint32_t)((rows_b - 1) * args.ldb + args.k_bytes));
-    uint32_t a_vbase = (uint32_t)((T::ROWS_PER_COPY * wave + cp_row) * args.lda) + cp_c16;
-    uint32_t b_vbase = (uint32_t)((T::ROWS_PER_COPY * wave + cp_row) * args.ldb) + cp_c16;
-    const uint32_t a_qstep = (uint32_t)(T::ROWS_PER_COPY * T::NW * args.lda);
-    const uint32_t b_qstep = (uint32_t)(T::ROWS_PER_COPY * T::NW * args.ldb);
+    // Copy q of a wave fills LDS rows (slots) (q*NW + wave) * ROWS_PER_COPY + cp_row
+    // from tile row perm(slot); the lane part and the q part of the slot occupy
+    // disjoint bits, so perm splits into a per-lane row and a per-q row.
+    uint32_t a_vbase = (uint32_t)(T::perm(T::ROWS_PER_COPY * wave + cp_row) * args.lda) + cp_c16;
+    uint32_t b_vbase = (uint32_t)(T::perm(T::ROWS_PER_COPY * wave + cp_row) * args.ldb) + cp_c16;
     // Opaque per tile: otherwise the compiler hoists every copy offset of the
     // prologue out of the tile loop and spills them all.
     asm volatile("" : "+v"(a_vbase), "+v"(b_vbase));
@@ -489,7 +512,8 @@ void gemm_kernel(const GemmArgs args) {
       if (q < T::A_LOADS) {
         const int ci = q * T::NW + wave;
         const bool dummy = T::DUMMY && ci >= T::A_COPIES;
-        const uint32_t off = (a_vbase + q * a_qstep + kb) | oob | (dummy ? kOOB : 0u);
+        const uint32_t qrow = (uint32_t)T::perm(q * T::NW * T::ROWS_PER_COPY);
+        const uint32_t off = (a_vbase + qrow * (uint32_t)args.lda + kb) | oob | (dummy ? kOOB : 0u);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             ra, (__attribute__((address_space(3))) void*)(dummy ? spare : sA + T::ROWS_PER_COPY * ci * SB),
             16, off, 0, 0, 0);
@@ -497,7 +521,8 @@ void gemm_kernel(const GemmArgs args) {
         const int qb = q - T::A_LOADS;
         const int ci = qb * T::NW + wave;
         const bool dummy = T::DUMMY && ci >= T::B_COPIES;
-        const uint32_t off = (b_vbase + qb * b_qstep + kb) | oob | (dummy ? kOOB : 0u);
+        const uint32_t qrow = (uint32_t)T::perm(qb * T::NW * T::ROWS_PER_COPY);
+        const uint32_t off = (b_vbase + qrow * (uint32_t)args.ldb + kb) | oob | (dummy ? kOOB : 0u);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rb, (__attribute__((address_space(3))) void*)(dummy ? spare : sB + T::ROWS_PER_COPY * ci * SB),
             16, off, 0, 0, 0);
@@ -529,17 +554,23 @@ void gemm_kernel(const GemmArgs args) {
         args.sfa, (uint32_t)(2 * ((int64_t)(args.kp_count - 1) * args.ld_sfa + args.M)));
     const __amdgpu_buffer_rsrc_t rsb = make_rsrc(
         sfb, (uint32_t)(2 * ((int64_t)(args.kp_count - 1) * args.ld_sfb + args.sfb_rows)));
-    uint32_t sa_voff = 2u * (uint32_t)(m0 + wm * T::TM + l32);
+    // (FP4: the lane's fragment rows are 4*l32 .. 4*l32 + 3 of the wave block)
+    uint32_t sa_voff = 2u * (uint32_t)(m0 + wm * T::TM + (T::PERM ? 4 * l32 : l32));
     asm volatile("" : "+v"(sa_voff));
     uint32_t sb_voff = KIND == KIND_FP8 ? 2u * (uint32_t)((n0 + wn * T::TN) / 128)
-                                        : 2u * (uint32_t)(n0 + wn * T::TN + l32);
+                                        : 2u * (uint32_t)(n0 + wn * T::TN + (T::PERM ? 4 * l32 : l32));
     asm volatile("" : "+v"(sb_voff));
     // Raw scale words of stage kt (packed int16, not decoded yet).
     //   FP8: K-block kt*SB/128, held in packed row kb/2, byte kb%2.
     //   FP4: lane group lg needs K-blocks kt*NC + (NC/2)*lg + j (j < NC/2), the
     //        packed rows kt*NC/2 + (NC/4)*lg + w for w < NC/4.
-    auto load_scales = [&](int kt, uint16_t (&ra_)[FM][SW > 0 ? SW : 1],
-                           uint16_t (&rb_)[NSB][SW > 0 ? SW : 1]) {
+    // Raw scale words, one register set per ring slot (the slot is a compile-time
+    // value at every call).  FP4 with SV: the two dwords of each operand's 8-byte
+    // load, fragments 2i and 2i+1 in the low and high halves of dword i.
+    uint16_t rs_a[NS][FM][SW > 0 ? SW : 1] = {}, rs_b[NS][NSB][SW > 0 ? SW : 1] = {};
+    uint32_t rv_a[SV ? NS : 1][2] = {}, rv_b[SV ? NS : 1][2] = {};
+    auto load_scales = [&](int kt, auto slot) {
+      constexpr int sl = decltype(slot)::value;
       if constexpr (KIND != KIND_BF16) {
 #pragma unroll
         for (int w = 0; w < SW; ++w) {
@@ -547,40 +578,59 @@ void gemm_kernel(const GemmArgs args) {
           kp = kp < args.kp_count ? kp : args.kp_count - 1;
           const uint32_t va = sa_voff + 2u * (uint32_t)(kp * args.ld_sfa);
           const uint32_t vb = sb_voff + 2u * (uint32_t)(kp * args.ld_sfb);
+          if constexpr (SV) {
+            const u32x2_t da = __builtin_amdgcn_raw_buffer_load_b64(rsa, va, 0, 0);
+            const u32x2_t db = __builtin_amdgcn_raw_buffer_load_b64(rsb, vb, 0, 0);
+            rv_a[sl][0] = da[0];
+            rv_a[sl][1] = da[1];
+            rv_b[sl][0] = db[0];
+            rv_b[sl][1] = db[1];
+          } else {
+            // fragment f's word: 2 bytes further on (FP4, adjacent rows) or 64
+            // bytes (32 rows) further on
+            constexpr uint32_t fstep = T::PERM ? 2 : 64;
 #pragma unroll
-          for (int f = 0; f < FM; ++f)
-            ra_[f][w] = __builtin_amdgcn_raw_buffer_load_b16(rsa, va + 64 * f, 0, 0);
+            for (int f = 0; f < FM; ++f)
+              rs_a[sl][f][w] = __builtin_amdgcn_raw_buffer_load_b16(rsa, va + fstep * f, 0, 0);
 #pragma unroll
-          for (int f = 0; f < NSB; ++f) {
-            if constexpr (KIND == KIND_FP8 && !T::ONE_B_SCALE)
-              rb_[f][w] = __builtin_amdgcn_raw_buffer_load_b16(
-                  rsb, 2u * (uint32_t)(((nrow0 + 32 * f) >> 7) + kp * args.ld_sfb), 0, 0);
-            else
-              rb_[f][w] = __builtin_amdgcn_raw_buffer_load_b16(rsb, vb + 64 * f, 0, 0);
+            for (int f = 0; f < NSB; ++f) {
+              if constexpr (KIND == KIND_FP8 && !T::ONE_B_SCALE)
+                rs_b[sl][f][w] = __builtin_amdgcn_raw_buffer_load_b16(
+                    rsb, 2u * (uint32_t)(((nrow0 + 32 * f) >> 7) + kp * args.ld_sfb), 0, 0);
+              else
+                rs_b[sl][f][w] = __builtin_amdgcn_raw_buffer_load_b16(rsb, vb + fstep * f, 0, 0);
+            }
           }
         }
       }
     };
     // Decoded per-lane scale operand of stage kt.  FP8: the K-block's byte in
-    // bits 0..7.  FP4: k-step j's byte in byte j.  (The raw words stay 16-bit
-    // until here, so nothing touches a load's result before the barrier that
-    // waits for it.)
-    auto decode_scales = [&](int kt, const uint16_t (&ra_)[FM][SW > 0 ? SW : 1],
-                             const uint16_t (&rb_)[NSB][SW > 0 ? SW : 1], uint32_t (&sa)[FM],
-                             uint32_t (&sb)[FN]) {
+    // bits 0..7.  FP4 (permuted rows): dword i holds fragment 2i's word in its low
+    // half and fragment 2i+1's in its high half; k-step j of fragment f uses byte
+    // 2*(f%2) + j of dword f/2, picked by the MFMA's byte select.  (The raw words
+    // stay untouched until here, so nothing uses a load's result before the
+    // barrier that waits for it.)
+    auto decode_scales = [&](int kt, auto slot, uint32_t (&sa)[FM], uint32_t (&sb)[FN]) {
+      constexpr int sl = decltype(slot)::value;
       if constexpr (KIND == KIND_FP8) {
         const int sh = ((kt * SB / 128) & 1) * 8;
 #pragma unroll
-        for (int f = 0; f < FM; ++f) sa[f] = ((uint32_t)ra_[f][0] >> sh) & 0xFF;
+        for (int f = 0; f < FM; ++f) sa[f] = ((uint32_t)rs_a[sl][f][0] >> sh) & 0xFF;
 #pragma unroll
-        for (int f = 0; f < FN; ++f) sb[f] = ((uint32_t)rb_[T::ONE_B_SCALE ? 0 : f][0] >> sh) & 0xFF;
+        for (int f = 0; f < FN; ++f) sb[f] = ((uint32_t)rs_b[sl][T::ONE_B_SCALE ? 0 : f][0] >> sh) & 0xFF;
       } else if constexpr (KIND == KIND_FP4) {
+        if constexpr (SV) {
+          sa[0] = rv_a[sl][0];
+          sa[1] = rv_a[sl][1];
+          sb[0] = rv_b[sl][0];
+          sb[1] = rv_b[sl][1];
+        } else {
 #pragma unroll
-        for (int f = 0; f < FM; ++f)
-          sa[f] = SW == 2 ? ((uint32_t)ra_[f][0] | ((uint32_t)ra_[f][SW - 1] << 16)) : (uint32_t)ra_[f][0];
-#pragma unroll
-        for (int f = 0; f < FN; ++f)
-          sb[f] = SW == 2 ? ((uint32_t)rb_[f][0] | ((uint32_t)rb_[f][SW - 1] << 16)) : (uint32_t)rb_[f][0];
+          for (int i = 0; i < 2; ++i) {
+            sa[i] = (uint32_t)rs_a[sl][2 * i][0] | ((uint32_t)rs_a[sl][2 * i + 1][0] << 16);
+            sb[i] = (uint32_t)rs_b[sl][2 * i][0] | ((uint32_t)rs_b[sl][2 * i + 1][0] << 16);
+          }
+        }
       }
     };
 
@@ -631,22 +681,29 @@ void gemm_kernel(const GemmArgs args) {
     auto mfmas = [&](auto jc, const frag_t (&xa)[FM], const frag_t (&xb)[FN], const uint32_t (&sa)[FM],
                      const uint32_t (&sb)[FN]) {
       constexpr int j = decltype(jc)::value;
+      if constexpr (T::PERM) {
+        // a-outer, b-inner as below; fragment f's scale is byte 2*(f%2) + j of
+        // dword f/2
+        [&]<int... ab>(std::integer_sequence<int, ab...>) {
+          ((acc[ab / FN][ab % FN] = mfma_scaled2<4, 2 * ((ab % FN) % 2) + j, 2 * ((ab / FN) % 2) + j>(
+                xb[ab % FN], xa[ab / FN], acc[ab / FN][ab % FN], sb[(ab % FN) / 2], sa[(ab / FN) / 2])),
+           ...);
+        }(std::make_integer_sequence<int, FM * FN>{});
+      } else {
 #pragma unroll
-      for (int a = 0; a < FM; ++a)
+        for (int a = 0; a < FM; ++a)
 #pragma unroll
-        for (int b = 0; b < FN; ++b) {
-          if constexpr (KIND == KIND_BF16)
-            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb[b], xa[a], acc[a][b], 0, 0, 0);
-          else if constexpr (KIND == KIND_FP8)
-            acc[a][b] = mfma_scaled<0, 0>(xb[b], xa[a], acc[a][b], sb[b], sa[a]);
-          else
-            acc[a][b] = mfma_scaled<4, j>(xb[b], xa[a], acc[a][b], sb[b], sa[a]);
-        }
+          for (int b = 0; b < FN; ++b) {
+            if constexpr (KIND == KIND_BF16)
+              acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb[b], xa[a], acc[a][b], 0, 0, 0);
+            else if constexpr (KIND == KIND_FP8)
+              acc[a][b] = mfma_scaled<0, 0>(xb[b], xa[a], acc[a][b], sb[b], sa[a]);
+            else
+              acc[a][b] = mfma_scaled<4, j>(xb[b], xa[a], acc[a][b], sb[b], sa[a]);
+          }
+      }
     };
 
-    // Raw scale words, one register set per ring slot (indexed by the stage's
-    // buffer, a compile-time value in the unrolled loop below).
-    uint16_t rs_a[NS][FM][SW > 0 ? SW : 1] = {}, rs_b[NS][NSB][SW > 0 ? SW : 1] = {};
     uint32_t sa_cur[FM] = {}, sb_cur[FN] = {};
 
     // Prologue: the previous tile's LDS reads are over once every wave is here;
@@ -661,8 +718,9 @@ void gemm_kernel(const GemmArgs args) {
       constexpr int c = T::chunk_at(g), tl = T::pair_start(g) + NS - 1;
       constexpr int b0 = T::pmod(tl, NS), b1 = T::pmod(tl + 1, NS);
       const int t = round + tl;
-      if constexpr (c == 0) load_scales(t < nk ? t : 0, rs_a[b0], rs_b[b0]);
-      if constexpr (c == 1 && !T::SHARED_SCALES) load_scales(t + 1 < nk ? t + 1 : 0, rs_a[b1], rs_b[b1]);
+      if constexpr (c == 0) load_scales(t < nk ? t : 0, std::integral_constant<int, b0>{});
+      if constexpr (c == 1 && !T::SHARED_SCALES)
+        load_scales(t + 1 < nk ? t + 1 : 0, std::integral_constant<int, b1>{});
       issue_chunk(t, b0, b1, c);
     };
     if constexpr (PR) {
@@ -675,12 +733,12 @@ void gemm_kernel(const GemmArgs args) {
       }(std::make_integer_sequence<int, (NS + 2) * J>{});
     } else {
       [&]<int... bs>(std::integer_sequence<int, bs...>) {
-        ((load_scales(bs < nk ? bs : 0, rs_a[bs], rs_b[bs]), issue_stage(bs, bs)), ...);
+        ((load_scales(bs < nk ? bs : 0, std::integral_constant<int, bs>{}), issue_stage(bs, bs)), ...);
       }(std::make_integer_sequence<int, NS>{});
     }
     wait_vm_lds<T::wait_prologue()>();
     ring_barrier();
-    decode_scales(0, rs_a[0], rs_b[0], sa_cur, sb_cur);
+    decode_scales(0, std::integral_constant<int, 0>{}, sa_cur, sb_cur);
     read_frags(0, 0, fa[0], fb[0]);
 
     // One stage.  Every stage runs the same code: after the last real one, the
@@ -716,7 +774,7 @@ void gemm_kernel(const GemmArgs args) {
           if constexpr (PR) {
             pair_chunk(std::integral_constant<int, g>{}, round);
           } else {
-            load_scales(s + NS < nk ? s + NS : 0, rs_a[buf], rs_b[buf]);
+            load_scales(s + NS < nk ? s + NS : 0, std::integral_constant<int, buf>{});
             issue_stage(s + NS, buf);
           }
           read_frags(nbuf, 0, fa[nx], fb[nx]);
@@ -725,7 +783,7 @@ void gemm_kernel(const GemmArgs args) {
           __builtin_amdgcn_sched_barrier(0);
           // (shared scales: stage s+1 reads the set of its pair's first stage)
           constexpr int sbuf = T::SHARED_SCALES ? T::pmod(((si + 1) & ~1), NS) : nbuf;
-          decode_scales(s + 1, rs_a[sbuf], rs_b[sbuf], sa_cur, sb_cur);
+          decode_scales(s + 1, std::integral_constant<int, sbuf>{}, sa_cur, sb_cur);
         }
       };
       [&]<int... js>(std::integer_sequence<int, js...>) {
@@ -741,11 +799,31 @@ void gemm_kernel(const GemmArgs args) {
     // Epilogue.  MFMA operands were (B fragment, A fragment), so accumulator
     // register r of lane l holds D[m][n] with m = l%32 and
     // n = 8*(r/4) + 4*(l/32) + r%4: four consecutive columns per register quad.
+    // FP4's permuted rows: fragment a's row l32 is tile row 4*l32 + a, and
+    // fragment b's column i is tile column 4*i + b, so the four fragments b hold
+    // four consecutive columns in the same register.
 #pragma unroll
     for (int a = 0; a < FM; ++a) {
-      const int m = m0 + wm * T::TM + 32 * a + l32;
+      const int m = m0 + wm * T::TM + (T::PERM ? 4 * l32 + a : 32 * a + l32);
       if (m >= m_end) continue;
       uint16_t* drow = args.D + (int64_t)m * args.ldd;
+      if constexpr (T::PERM) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int n = n0 + wn * T::TN + 4 * (8 * (r / 4) + 4 * lg + r % 4);
+          const float v0 = acc[a][0][r], v1 = acc[a][1][r], v2 = acc[a][2][r], v3 = acc[a][3][r];
+          if (args.d_vec && n + 3 < n_end) {
+            i32x2_t w = {(int)pack_bf16x2(v0, v1), (int)pack_bf16x2(v2, v3)};
+            *(i32x2_t*)(drow + n) = w;
+          } else {
+            const float vv[4] = {v0, v1, v2, v3};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < n_end) drow[n + e] = (uint16_t)(pack_bf16x2(vv[e], 0.0f) & 0xFFFF);
+          }
+        }
+        continue;
+      }
 #pragma unroll
       for (int b = 0; b < FN; ++b) {
 #pragma unroll

@@ -402,3 +402,22 @@ def test_grouped_moe_workload_sampled():
     g = np.random.default_rng(7)
     rows += list(g.integers(off[0], off[-1], 6))
     check_grouped(w, D, sorted(set(int(r) for r in rows)), "moe_fp8")
+
+
+def test_fp4_scale_load_variants_agree():
+    """FP4 fetches a lane's four scale words with one 8-byte load when the packed
+    arrays allow it (8-byte aligned, leading dimension a multiple of 4) and with
+    2-byte loads otherwise; both must give the same bits, and match the oracle."""
+    _say("fp4 scale load variants")
+    M, N, K = 512, 384, 1024
+    w = workloads.dense("fp4", M, N, K, 77, device="cpu")
+    t = {k: v.to(DEV) for k, v in w.tensors.items()}
+    outs = []
+    for pad in (0, 2):
+        sfa = bsg.pack_ue8m0_scales(t["sfa"], ld_packed=M + pad)
+        sfb = bsg.pack_ue8m0_scales(t["sfb"], ld_packed=N + pad)
+        outs.append(gpu_bits(bsg.gemm_fp4_blockscaled(t["A"], sfa[:, :M], t["B"], sfb[:, :N], K=K)))
+    torch.cuda.synchronize()
+    assert np.array_equal(outs[0], outs[1])
+    ref, na, nb = run_oracle("fp4", host(w.tensors), K)
+    assert_parity(outs[0], ref, na, nb, what="fp4 512x384x1024 (8-byte scale loads)")
