@@ -100,6 +100,9 @@ static int launch(GemmArgs a, hipStream_t stream) {
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+// A packed scale array whose rows of four int16 can be fetched as one 8-byte word.
+static bool sv_ok(const int16_t* sf, int64_t ld) { return ((uintptr_t)sf % 8 == 0) && (ld % 4 == 0); }
+
 // Byte strides must keep 256 rows of offsets inside 31 bits.
 static const int64_t kMaxRowBytes = (int64_t(1) << 31) / 256 - 1;
 static const int64_t kMaxDim = (int64_t(1) << 31) - 1;
@@ -213,7 +216,9 @@ int gemm_fp8_blockscaled(const void* A, int64_t lda, const int16_t* sfa, int64_t
   a.k_bytes = (int32_t)K;
   a.kp_count = (int32_t)((K / 128 + 1) / 2);
   a.sfb_rows = (int32_t)((N + 127) / 128);
-  return launch<KIND_FP8, BSG_FP8_CFG, false>(a, (hipStream_t)stream);
+  // one 8-byte load for a lane's four A scale words when sfa allows it
+  if (sv_ok(sfa, ld_sfa)) return launch<KIND_FP8, BSG_FP8_CFG, false, 1>(a, (hipStream_t)stream);
+  return launch<KIND_FP8, BSG_FP8_CFG, false, 0>(a, (hipStream_t)stream);
 }
 
 int gemm_fp4_blockscaled(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
@@ -242,9 +247,7 @@ int gemm_fp4_blockscaled(const void* A, int64_t lda, const int16_t* sfa, int64_t
   a.sfb_rows = (int32_t)N;
   // 8-byte scale loads when both packed arrays allow them (8-byte aligned, leading
   // dimensions multiples of 4 int16), 2-byte loads otherwise.
-  const bool sv = ((uintptr_t)sfa % 8 == 0) && ((uintptr_t)sfb % 8 == 0) && (ld_sfa % 4 == 0) &&
-                  (ld_sfb % 4 == 0);
-  if (sv) return launch<KIND_FP4, BSG_FP4_CFG, false, 1>(a, (hipStream_t)stream);
+  if (sv_ok(sfa, ld_sfa) && sv_ok(sfb, ld_sfb)) return launch<KIND_FP4, BSG_FP4_CFG, false, 1>(a, (hipStream_t)stream);
   return launch<KIND_FP4, BSG_FP4_CFG, false, 0>(a, (hipStream_t)stream);
 }
 
@@ -278,7 +281,8 @@ int m_grouped_gemm_fp8(const void* A, int64_t lda, const int16_t* sfa, int64_t l
   a.kp_count = (int32_t)kp;
   a.sfb_rows = (int32_t)((N + 127) / 128);
   a.G = G;
-  return launch<KIND_FP8, BSG_GROUPED_CFG, true>(a, (hipStream_t)stream);
+  if (sv_ok(sfa, ld_sfa)) return launch<KIND_FP8, BSG_GROUPED_CFG, true, 1>(a, (hipStream_t)stream);
+  return launch<KIND_FP8, BSG_GROUPED_CFG, true, 0>(a, (hipStream_t)stream);
 }
 
 int m_grouped_gemm_fp8_masked(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
@@ -315,7 +319,8 @@ int m_grouped_gemm_fp8_masked(const void* A, int64_t lda, const int16_t* sfa, in
   a.kp_count = (int32_t)kp;
   a.sfb_rows = (int32_t)((N + 127) / 128);
   a.G = G;
-  return launch<KIND_FP8, BSG_GROUPED_CFG, true>(a, (hipStream_t)stream);
+  if (sv_ok(sfa, ld_sfa)) return launch<KIND_FP8, BSG_GROUPED_CFG, true, 1>(a, (hipStream_t)stream);
+  return launch<KIND_FP8, BSG_GROUPED_CFG, true, 0>(a, (hipStream_t)stream);
 }
 
 static int launch_pack(bool unpack, const void* src, int64_t mn, int64_t kb, int64_t ld_src,

@@ -161,20 +161,24 @@ struct GemmTile {
   // packed scale words per lane per fragment per stage: FP8 one (the K-block's
   // pair), FP4 NC/4 (lane group lg takes NC/2 K-blocks of 32)
   static constexpr int SW = KIND == KIND_BF16 ? 0 : (KIND == KIND_FP8 ? 1 : NC / 4);
-  // FP4 permutes the rows of every 128-row wave block, A and B alike: LDS slot
-  // 32f + i (fragment f, lane row i) holds tile row 4i + f.  A lane's four
-  // fragment rows are then adjacent in memory, and so are their packed scale
-  // words: SV = 1 fetches them with one 8-byte load per operand and stage (the
-  // arrays must be 8-byte aligned, with leading dimensions that are multiples of
-  // 4), SV = 0 with four 2-byte loads.
-  static constexpr bool PERM = KIND == KIND_FP4;
-  static_assert(!PERM || (FM == 4 && FN == 4 && SW == 1),
-                "the FP4 row permutation needs 128-row wave blocks and 64-byte stages");
-  static_assert(SV == 0 || PERM, "vector scale loads need the FP4 row permutation");
-  static constexpr int perm(int x) {
-    return PERM ? ((x & ~127) | ((x & 31) << 2) | ((x >> 5) & 3)) : x;
+  // Operands with one scale per row (A for FP8 and FP4, B for FP4) permute the
+  // rows of every 128-row wave block: LDS slot 32f + i (fragment f, lane row i)
+  // holds tile row 4i + f.  A lane's four fragment rows are then adjacent in
+  // memory, and so are their packed scale words: SV = 1 fetches them with one
+  // 8-byte load per operand (the packed arrays must be 8-byte aligned, with
+  // leading dimensions that are multiples of 4), SV = 0 with four 2-byte loads.
+  static constexpr bool PERM_A = KIND != KIND_BF16;
+  static constexpr bool PERM_B = KIND == KIND_FP4;
+  static constexpr bool PERM = PERM_B;   // FP4: both operands
+  static_assert(!PERM_A || (FM == 4 && SW == 1),
+                "the row permutation needs 128-row wave blocks and one scale word per stage");
+  static_assert(!PERM_B || FN == 4, "the row permutation needs 128-row wave blocks");
+  static constexpr int perm_rows(bool on, int x) {
+    return on ? ((x & ~127) | ((x & 31) << 2) | ((x >> 5) & 3)) : x;
   }
-  static constexpr int NSC = SV ? 2 * SW : (FM + NSB) * SW;
+  static constexpr int perm_a(int x) { return perm_rows(PERM_A, x); }
+  static constexpr int perm_b(int x) { return perm_rows(PERM_B, x); }
+  static constexpr int NSC = SV ? (1 + (PERM_B ? 1 : NSB)) * SW : (FM + NSB) * SW;
   static constexpr int VMEM_PER_STAGE = N_DMA + NSC;
   static_assert(SB == 64 || SB == 128, "a stage is 64 or 128 bytes of K per row");
   static_assert(NS >= 2 && NS <= 8, "ring of 2..8 stages");
@@ -492,8 +496,8 @@ void gemm_kernel(const GemmArgs args) {
     // Copy q of a wave fills LDS rows (slots) (q*NW + wave) * ROWS_PER_COPY + cp_row
     // from tile row perm(slot); the lane part and the q part of the slot occupy
     // disjoint bits, so perm splits into a per-lane row and a per-q row.
-    uint32_t a_vbase = (uint32_t)(T::perm(T::ROWS_PER_COPY * wave + cp_row) * args.lda) + cp_c16;
-    uint32_t b_vbase = (uint32_t)(T::perm(T::ROWS_PER_COPY * wave + cp_row) * args.ldb) + cp_c16;
+    uint32_t a_vbase = (uint32_t)(T::perm_a(T::ROWS_PER_COPY * wave + cp_row) * args.lda) + cp_c16;
+    uint32_t b_vbase = (uint32_t)(T::perm_b(T::ROWS_PER_COPY * wave + cp_row) * args.ldb) + cp_c16;
     // Opaque per tile: otherwise the compiler hoists every copy offset of the
     // prologue out of the tile loop and spills them all.
     asm volatile("" : "+v"(a_vbase), "+v"(b_vbase));
@@ -512,7 +516,7 @@ void gemm_kernel(const GemmArgs args) {
       if (q < T::A_LOADS) {
         const int ci = q * T::NW + wave;
         const bool dummy = T::DUMMY && ci >= T::A_COPIES;
-        const uint32_t qrow = (uint32_t)T::perm(q * T::NW * T::ROWS_PER_COPY);
+        const uint32_t qrow = (uint32_t)T::perm_a(q * T::NW * T::ROWS_PER_COPY);
         const uint32_t off = (a_vbase + qrow * (uint32_t)args.lda + kb) | oob | (dummy ? kOOB : 0u);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             ra, (__attribute__((address_space(3))) void*)(dummy ? spare : sA + T::ROWS_PER_COPY * ci * SB),
@@ -521,7 +525,7 @@ void gemm_kernel(const GemmArgs args) {
         const int qb = q - T::A_LOADS;
         const int ci = qb * T::NW + wave;
         const bool dummy = T::DUMMY && ci >= T::B_COPIES;
-        const uint32_t qrow = (uint32_t)T::perm(qb * T::NW * T::ROWS_PER_COPY);
+        const uint32_t qrow = (uint32_t)T::perm_b(qb * T::NW * T::ROWS_PER_COPY);
         const uint32_t off = (b_vbase + qrow * (uint32_t)args.ldb + kb) | oob | (dummy ? kOOB : 0u);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rb, (__attribute__((address_space(3))) void*)(dummy ? spare : sB + T::ROWS_PER_COPY * ci * SB),
@@ -555,10 +559,10 @@ void gemm_kernel(const GemmArgs args) {
     const __amdgpu_buffer_rsrc_t rsb = make_rsrc(
         sfb, (uint32_t)(2 * ((int64_t)(args.kp_count - 1) * args.ld_sfb + args.sfb_rows)));
     // (FP4: the lane's fragment rows are 4*l32 .. 4*l32 + 3 of the wave block)
-    uint32_t sa_voff = 2u * (uint32_t)(m0 + wm * T::TM + (T::PERM ? 4 * l32 : l32));
+    uint32_t sa_voff = 2u * (uint32_t)(m0 + wm * T::TM + (T::PERM_A ? 4 * l32 : l32));
     asm volatile("" : "+v"(sa_voff));
     uint32_t sb_voff = KIND == KIND_FP8 ? 2u * (uint32_t)((n0 + wn * T::TN) / 128)
-                                        : 2u * (uint32_t)(n0 + wn * T::TN + (T::PERM ? 4 * l32 : l32));
+                                        : 2u * (uint32_t)(n0 + wn * T::TN + (T::PERM_B ? 4 * l32 : l32));
     asm volatile("" : "+v"(sb_voff));
     // Raw scale words of stage kt (packed int16, not decoded yet).
     //   FP8: K-block kt*SB/128, held in packed row kb/2, byte kb%2.
@@ -578,27 +582,30 @@ void gemm_kernel(const GemmArgs args) {
           kp = kp < args.kp_count ? kp : args.kp_count - 1;
           const uint32_t va = sa_voff + 2u * (uint32_t)(kp * args.ld_sfa);
           const uint32_t vb = sb_voff + 2u * (uint32_t)(kp * args.ld_sfb);
+          // fragment f's word: 2 bytes further on (permuted rows: adjacent) or
+          // 64 bytes (32 rows) further on
+          constexpr uint32_t fstep_a = T::PERM_A ? 2 : 64, fstep_b = T::PERM_B ? 2 : 64;
           if constexpr (SV) {
             const u32x2_t da = __builtin_amdgcn_raw_buffer_load_b64(rsa, va, 0, 0);
-            const u32x2_t db = __builtin_amdgcn_raw_buffer_load_b64(rsb, vb, 0, 0);
             rv_a[sl][0] = da[0];
             rv_a[sl][1] = da[1];
+          } else {
+#pragma unroll
+            for (int f = 0; f < FM; ++f)
+              rs_a[sl][f][w] = __builtin_amdgcn_raw_buffer_load_b16(rsa, va + fstep_a * f, 0, 0);
+          }
+          if constexpr (SV && T::PERM_B) {
+            const u32x2_t db = __builtin_amdgcn_raw_buffer_load_b64(rsb, vb, 0, 0);
             rv_b[sl][0] = db[0];
             rv_b[sl][1] = db[1];
           } else {
-            // fragment f's word: 2 bytes further on (FP4, adjacent rows) or 64
-            // bytes (32 rows) further on
-            constexpr uint32_t fstep = T::PERM ? 2 : 64;
-#pragma unroll
-            for (int f = 0; f < FM; ++f)
-              rs_a[sl][f][w] = __builtin_amdgcn_raw_buffer_load_b16(rsa, va + fstep * f, 0, 0);
 #pragma unroll
             for (int f = 0; f < NSB; ++f) {
               if constexpr (KIND == KIND_FP8 && !T::ONE_B_SCALE)
                 rs_b[sl][f][w] = __builtin_amdgcn_raw_buffer_load_b16(
                     rsb, 2u * (uint32_t)(((nrow0 + 32 * f) >> 7) + kp * args.ld_sfb), 0, 0);
               else
-                rs_b[sl][f][w] = __builtin_amdgcn_raw_buffer_load_b16(rsb, vb + fstep * f, 0, 0);
+                rs_b[sl][f][w] = __builtin_amdgcn_raw_buffer_load_b16(rsb, vb + fstep_b * f, 0, 0);
             }
           }
         }
@@ -614,8 +621,14 @@ void gemm_kernel(const GemmArgs args) {
       constexpr int sl = decltype(slot)::value;
       if constexpr (KIND == KIND_FP8) {
         const int sh = ((kt * SB / 128) & 1) * 8;
+        if constexpr (SV) {
+          // the K-block's byte of fragments 2i and 2i+1 moves to bytes 0 and 2
+          sa[0] = rv_a[sl][0] >> sh;
+          sa[1] = rv_a[sl][1] >> sh;
+        } else {
 #pragma unroll
-        for (int f = 0; f < FM; ++f) sa[f] = ((uint32_t)rs_a[sl][f][0] >> sh) & 0xFF;
+          for (int f = 0; f < FM; ++f) sa[f] = ((uint32_t)rs_a[sl][f][0] >> sh) & 0xFF;
+        }
 #pragma unroll
         for (int f = 0; f < FN; ++f) sb[f] = ((uint32_t)rs_b[sl][T::ONE_B_SCALE ? 0 : f][0] >> sh) & 0xFF;
       } else if constexpr (KIND == KIND_FP4) {
@@ -681,7 +694,14 @@ void gemm_kernel(const GemmArgs args) {
     auto mfmas = [&](auto jc, const frag_t (&xa)[FM], const frag_t (&xb)[FN], const uint32_t (&sa)[FM],
                      const uint32_t (&sb)[FN]) {
       constexpr int j = decltype(jc)::value;
-      if constexpr (T::PERM) {
+      if constexpr (KIND == KIND_FP8 && SV) {
+        // A fragment f's scale: byte 2*(f%2) of dword f/2 (decoded per K-block)
+        [&]<int... ab>(std::integer_sequence<int, ab...>) {
+          ((acc[ab / FN][ab % FN] = mfma_scaled2<0, 0, 2 * ((ab / FN) % 2)>(
+                xb[ab % FN], xa[ab / FN], acc[ab / FN][ab % FN], sb[ab % FN], sa[(ab / FN) / 2])),
+           ...);
+        }(std::make_integer_sequence<int, FM * FN>{});
+      } else if constexpr (T::PERM) {
         // a-outer, b-inner as below; fragment f's scale is byte 2*(f%2) + j of
         // dword f/2
         [&]<int... ab>(std::integer_sequence<int, ab...>) {
@@ -799,12 +819,12 @@ void gemm_kernel(const GemmArgs args) {
     // Epilogue.  MFMA operands were (B fragment, A fragment), so accumulator
     // register r of lane l holds D[m][n] with m = l%32 and
     // n = 8*(r/4) + 4*(l/32) + r%4: four consecutive columns per register quad.
-    // FP4's permuted rows: fragment a's row l32 is tile row 4*l32 + a, and
-    // fragment b's column i is tile column 4*i + b, so the four fragments b hold
-    // four consecutive columns in the same register.
+    // Permuted rows: fragment a's row l32 is tile row 4*l32 + a; with B permuted
+    // too (FP4), fragment b's column i is tile column 4*i + b, so the four
+    // fragments b hold four consecutive columns in the same register.
 #pragma unroll
     for (int a = 0; a < FM; ++a) {
-      const int m = m0 + wm * T::TM + (T::PERM ? 4 * l32 + a : 32 * a + l32);
+      const int m = m0 + wm * T::TM + (T::PERM_A ? 4 * l32 + a : 32 * a + l32);
       if (m >= m_end) continue;
       uint16_t* drow = args.D + (int64_t)m * args.ldd;
       if constexpr (T::PERM) {

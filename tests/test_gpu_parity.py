@@ -421,3 +421,33 @@ def test_fp4_scale_load_variants_agree():
     assert np.array_equal(outs[0], outs[1])
     ref, na, nb = run_oracle("fp4", host(w.tensors), K)
     assert_parity(outs[0], ref, na, nb, what="fp4 512x384x1024 (8-byte scale loads)")
+
+
+def test_fp8_scale_load_variants_agree():
+    """FP8 fetches a lane's four A scale words with one 8-byte load when sfa
+    allows it and with 2-byte loads otherwise: same bits, dense and grouped."""
+    _say("fp8 scale load variants (dense and grouped)")
+    M, N, K = 512, 384, 1024
+    w = workloads.dense("fp8", M, N, K, 78, device="cpu")
+    t = {k: v.to(DEV) for k, v in w.tensors.items()}
+    sfb = bsg.ensure_packed(t["sfb"], (N + 127) // 128, K // 128)
+    outs = []
+    for pad in (0, 2):
+        sfa = bsg.pack_ue8m0_scales(t["sfa"], ld_packed=M + pad)[:, :M]
+        outs.append(gpu_bits(bsg.gemm_fp8_blockscaled(t["A"], sfa, t["B"], sfb)))
+    torch.cuda.synchronize()
+    assert np.array_equal(outs[0], outs[1])
+    ref, na, nb = run_oracle("fp8", host(w.tensors), K)
+    assert_parity(outs[0], ref, na, nb, what="fp8 512x384x1024 (8-byte A scale loads)")
+    g = workloads.grouped(4, 256, 512, seed=79, counts=[130, 0, 256, 77], device=DEV)
+    tg = g.tensors
+    Mt = tg["A"].shape[0]
+    sfbg = torch.stack([bsg.ensure_packed(x, 2, 4) for x in tg["sfb"]])
+    outs = []
+    for pad in (0, 2):
+        sfa = bsg.pack_ue8m0_scales(tg["sfa"], ld_packed=Mt + pad)[:, :Mt]
+        D = torch.zeros(Mt, 256, dtype=torch.bfloat16, device=DEV)
+        bsg.m_grouped_gemm_fp8(tg["A"], sfa, tg["B"], sfbg, tg["offsets"], out=D)
+        outs.append(gpu_bits(D))
+    torch.cuda.synchronize()
+    assert np.array_equal(outs[0], outs[1])
