@@ -451,3 +451,33 @@ def test_fp8_scale_load_variants_agree():
         outs.append(gpu_bits(D))
     torch.cuda.synchronize()
     assert np.array_equal(outs[0], outs[1])
+
+
+def test_bf16_largest_row_stride():
+    """Row strides at the library's limit (256 rows of offsets inside 31 bits):
+    lda = ldb = 4194296 bf16 elements (8 MiB rows, 2 GiB per operand), only the
+    first K of each row used."""
+    _say("bf16 largest row stride (2 GiB operands)")
+    M, N, K, ld = 256, 256, 1024, 4194296
+    w = workloads.dense("bf16", M, N, K, 91, device="cpu")
+    Ab = torch.empty(M, ld, dtype=torch.bfloat16, device=DEV)
+    Bb = torch.empty(N, ld, dtype=torch.bfloat16, device=DEV)
+    Ab[:, :K] = w.tensors["A"].to(DEV)
+    Bb[:, :K] = w.tensors["B"].to(DEV)
+    Ab[:, K:K + 64] = float("nan")          # must never be read
+    Bb[:, K:K + 64] = float("nan")
+    D = bsg.gemm_bf16(Ab[:, :K], Bb[:, :K])
+    torch.cuda.synchronize()
+    del Ab, Bb
+    torch.cuda.empty_cache()
+    ref, na, nb = run_oracle("bf16", host(w.tensors), K)
+    assert_parity(gpu_bits(D), ref, na, nb, what="bf16 256x256x1024, lda = ldb = 4194296")
+
+
+@pytest.mark.parametrize("kind", ["fp8", "fp4"])
+def test_long_k(kind):
+    """K = 131072 (1024 FP8 K-blocks, 4096 FP4 K-blocks): long scale arrays and
+    offsets far into each row."""
+    _say(f"{kind} 64x96x131072")
+    M, N, K = 64, 96, 131072
+    dense_full(kind, M, N, K, 92)
