@@ -16,7 +16,7 @@ e4m3 or e2m1 codes with UE8M0 block scales.
 
 Parity status of each function (what pins it is in ``tests/test_oracle_pins.py``
 and ``tests/test_quantize_pins.py``):
-  decoders, bf16 rounding, pack/unpack, dense BF16/FP8/FP4, grouped FP8,
+  decoders, bf16 rounding, pack/unpack, dense BF16/FP8/FP4, grouped BF16/FP8/FP4,
   masked grouped FP8, per-token quantisation: pinned.
 """
 from __future__ import annotations
@@ -289,6 +289,46 @@ def grouped_fp8(A, sfa, B, sfb, offsets, rows=None, cols=None) -> np.ndarray:
                 (_ptr(A), _ld(A), _ptr(sfa), _ld(sfa), _ptr(B), K, N * K,
                  _ptr(sfb), sfb.shape[2], sfb.shape[1] * sfb.shape[2], _ptr(off), G, K),
                 rows, cols)
+
+
+def _expert_rows(offsets, rows):
+    off = np.asarray(offsets, dtype=np.int64)
+    g = np.searchsorted(off, rows, side="right") - 1
+    inside = (rows >= off[0]) & (rows < off[-1])
+    return np.where(inside, g, -1)
+
+
+def grouped_bf16(A, B, offsets, rows=None, cols=None) -> np.ndarray:
+    """M-grouped BF16 GEMM: rows [off[g], off[g+1]) of A (bf16 bits uint16
+    [M_total][K]) multiply B[g] (uint16 [G][N][K]).  Rows outside every group
+    come back as NaN."""
+    A = _c2d(A, np.uint16)
+    B = np.asarray(B)
+    rows = _sel(rows, A.shape[0])
+    cols = _sel(cols, B.shape[1])
+    out = np.full((rows.size, cols.size), np.nan)
+    g_of = _expert_rows(offsets, rows)
+    for g in np.unique(g_of[g_of >= 0]):
+        sel = np.nonzero(g_of == g)[0]
+        out[sel] = gemm_bf16(A, B[g], rows=rows[sel], cols=cols)
+    return out
+
+
+def grouped_fp4(A, sfa, B, sfb, offsets, K: int, rows=None, cols=None) -> np.ndarray:
+    """M-grouped FP4 GEMM: rows [off[g], off[g+1]) of A (uint8 [M_total][K/2],
+    sfa packed [ceil(K/64)][>=M_total]) multiply B[g] (uint8 [G][N][K/2], sfb
+    packed [G][ceil(K/64)][>=N]).  Rows outside every group come back as NaN."""
+    A = _c2d(A, np.uint8)
+    B = np.asarray(B)
+    sfb = np.asarray(sfb)
+    rows = _sel(rows, A.shape[0])
+    cols = _sel(cols, B.shape[1])
+    out = np.full((rows.size, cols.size), np.nan)
+    g_of = _expert_rows(offsets, rows)
+    for g in np.unique(g_of[g_of >= 0]):
+        sel = np.nonzero(g_of == g)[0]
+        out[sel] = gemm_fp4(A, sfa, B[g], sfb[g], K, rows=rows[sel], cols=cols)
+    return out
 
 
 def masked_fp8(A, sfa, B, sfb, masked_m, max_m: int, rows=None, cols=None) -> np.ndarray:

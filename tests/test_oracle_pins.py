@@ -533,3 +533,35 @@ def test_masked_is_grouped_over_fixed_capacity(orc):
         ok = r - g * cap < m[g]
         assert np.array_equal(got[r[ok]], full[r[ok]])
         assert np.all(np.isnan(got[r[~ok]]))
+
+
+def test_grouped_bf16_expert_selection_closed_form(orc):
+    """A = all ones, B[g] = (g + 1) everywhere: D[r][n] = K * (g + 1) exactly for
+    a row r of expert g (empty and 1-row experts included); rows outside every
+    group are not computed."""
+    G, N, K = 5, 48, 64
+    off = np.array([0, 3, 3, 4, 70, 70], dtype=np.int32)
+    one = exact.bf16_bits(1.0)
+    A = np.full((72, K), one, np.uint16)
+    B = np.stack([np.full((N, K), exact.bf16_bits(float(g + 1)), np.uint16) for g in range(G)])
+    D = orc.grouped_bf16(A, B, off)
+    for g in range(G):
+        assert np.all(D[off[g]:off[g + 1]] == K * (g + 1))
+    assert np.all(np.isnan(D[70:]))
+
+
+def test_grouped_fp4_expert_selection_closed_form(orc):
+    """FP4: A codes 1.0 (0x2), scale 1; B[g] codes 1.0 with scale byte 127 + g:
+    D[r][n] = K * 2^g exactly; one expert with B scales per row differing pins
+    the per-row B scale indexing (row n of expert 2 has byte 127 + (n % 3))."""
+    G, N, K = 3, 40, 128
+    off = np.array([0, 5, 5, 37], dtype=np.int32)
+    A = np.full((37, K // 2), 0x22, np.uint8)
+    sfa = orc.pack_scales(np.full((37, K // 32), 127, np.uint8))
+    B = np.full((G, N, K // 2), 0x22, np.uint8)
+    sf = np.stack([np.full((N, K // 32), 127 + g, np.uint8) for g in range(G)])
+    sf[2] = (127 + np.arange(N) % 3)[:, None]
+    sfb = np.stack([orc.pack_scales(x) for x in sf])
+    D = orc.grouped_fp4(A, sfa, B, sfb, off, K)
+    assert np.all(D[0:5] == K * 1.0)
+    assert np.all(D[5:37] == K * 2.0 ** (np.arange(N) % 3)[None, :])
