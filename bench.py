@@ -1,14 +1,15 @@
 """Benchmark of the block-scaled GEMM library on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--dtypes bf16,fp8,fp4,grouped,quant_fp8,quant_fp4,quant_fp8_moe,moe_ffn,masked]
+                    [--dtypes bf16,fp8,fp4,grouped,grouped_bf16,grouped_fp4,quant_fp8,
+                              quant_fp4,quant_fp8_moe,moe_ffn,masked]
 
 Workload: D = A * B^T at M=4096, N=7168, K=16384, the dense shape the pages time
 (431 TFLOPS BF16 on the other accelerator: "DeepSeek lanza kernels de DeepGEMM
 para Huawei Ascend 950", section "Que alcance tienen las pruebas de
 rendimiento"), in BF16, in FP8 e4m3 with 1x128 / 128x128 UE8M0 scales and in FP4
-e2m1 with 1x32 scales, plus the M-grouped FP8 MoE GEMM (256 experts, N=2048,
-K=7168, 16384 tokens routed top-6 with Zipf(1.1) popularity).  All inputs are
+e2m1 with 1x32 scales, plus the M-grouped MoE GEMM (256 experts, N=2048,
+K=7168, 16384 tokens routed top-6 with Zipf(1.1) popularity) in FP8, BF16 and FP4.  All inputs are
 seeded synthetic data generated straight into HBM before timing starts.
 
 One JSON line is printed.  `value` is the BF16 GEMM's whole-run throughput in
@@ -56,7 +57,7 @@ METRIC = "TFLOPS and % of MI355X dense MFMA peak, GEMM 4096×7168×16384 per dty
 
 # MI355X published dense MFMA peaks (TFLOP/s).
 PEAK = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0, "grouped": 5000.0, "moe_ffn": 5000.0,
-        "masked": 5000.0}
+        "masked": 5000.0, "grouped_bf16": 2500.0, "grouped_fp4": 10100.0}
 # MI355X published HBM3E bandwidth (GB/s): the bound of the quantisers.
 HBM_PEAK_GBS = 8000.0
 QUANT_KINDS = ("quant_fp8", "quant_fp4", "quant_fp8_moe")
@@ -73,6 +74,8 @@ KERNEL_NAME = {
     "quant_fp8_moe": "quant_kernel<0, 0, 32, 2, 0>",
     "moe_ffn": "gemm_kernel<1, 256, 256, 2, 2, 64, 5, 1, true, 1> x2 + swiglu_quant_kernel<0>",
     "masked": "gemm_kernel<1, 128, 512, 1, 4, 64, 4, 1, true, 1>",
+    "grouped_bf16": "gemm_kernel<0, 256, 256, 2, 2, 64, 5, 1, true, 0>",
+    "grouped_fp4": "gemm_kernel<2, 256, 256, 2, 2, 64, 5, 1, true, 1>",
 }
 
 
@@ -127,7 +130,8 @@ def make_case(kind, dev):
 
     name = {"bf16": "bf16_large", "fp8": "fp8_large", "fp4": "fp4_large",
             "grouped": "moe_fp8", "quant_fp8": "act_large", "quant_fp4": "act_large",
-            "quant_fp8_moe": "act_moe", "moe_ffn": "moe_ffn", "masked": "masked_fp8"}[kind]
+            "quant_fp8_moe": "act_moe", "moe_ffn": "moe_ffn", "masked": "masked_fp8",
+            "grouped_bf16": "moe_bf16", "grouped_fp4": "moe_fp4"}[kind]
     w = workloads.make(name, device=dev)
     t = w.tensors
     M, N, K = w.M, w.N, w.K
@@ -155,6 +159,22 @@ def make_case(kind, dev):
                 "bytes_per_call": nbytes}
         meta.update({"M": M, "K": K})
         return call, 0.0, nbytes, meta
+    if kind in ("grouped_bf16", "grouped_fp4"):
+        A, B, off = t["A"], t["B"], t["offsets"]
+        G = B.shape[0]
+        D = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        if kind == "grouped_bf16":
+            call = lambda: bsg.m_grouped_gemm_bf16(A, B, off, out=D)
+            nbytes = 2 * (A.numel() + B.numel()) + 2 * M * N
+        else:
+            sfa = bsg.ensure_packed(t["sfa"], M, K // 32)
+            sfb = torch.stack([bsg.ensure_packed(x, N, K // 32) for x in t["sfb"]])
+            call = lambda: bsg.m_grouped_gemm_fp4(A, sfa, B, sfb, off, K=K, out=D)
+            nbytes = A.numel() + B.numel() + 2 * M * N + 2 * (sfa.numel() + sfb.numel())
+        meta = {"experts": G, "m_total": M, "useful_rows": w.meta["useful_rows"],
+                "routing": w.meta["routing"], "executed_tflop": 2.0 * M * N * K / 1e12}
+        meta.update({"M": M, "N": N, "K": K})
+        return call, w.flops, nbytes, meta
     if kind == "masked":
         A, B, m = t["A"], t["B"], t["masked_m"]
         G, cap, _ = A.shape
@@ -353,7 +373,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--dtypes",
-                    default="bf16,fp8,fp4,grouped,quant_fp8,quant_fp4,quant_fp8_moe,moe_ffn,masked")
+                    default="bf16,fp8,fp4,grouped,grouped_bf16,grouped_fp4,quant_fp8,quant_fp4,"
+                            "quant_fp8_moe,moe_ffn,masked")
     ap.add_argument("--cold-samples", type=int, default=10)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle time for cpu_baseline (0 disables it)")

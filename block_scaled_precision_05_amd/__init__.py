@@ -9,6 +9,7 @@ if ``libbsg.so`` is missing or cannot be loaded, every call raises.
     D = gemm_fp8_blockscaled(A, sfa, B, sfb)    # e4m3 with UE8M0 1x128 / 128x128 scales
     D = gemm_fp4_blockscaled(A, sfa, B, sfb)    # e2m1 (2 per byte) with UE8M0 1x32 scales
     D = m_grouped_gemm_fp8(A, sfa, B, sfb, offsets)
+    D = m_grouped_gemm_bf16(A, B, offsets) / m_grouped_gemm_fp4(A, sfa, B, sfb, offsets, K=K)
     D = m_grouped_gemm_fp8_masked(A, sfa, B, sfb, masked_m)   # A [G, max_m, K], counts on the GPU
     P = pack_ue8m0_scales(sf)                   # uint8 [mn, kb] -> int16 [ceil(kb/2), mn]
     sf = unpack_ue8m0_scales(P, mn, kb)
@@ -51,6 +52,9 @@ EXPORTS = {
     "gemm_fp4_blockscaled": [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
                              _i64, _i64, _i64, _vp],
     "m_grouped_gemm_fp8": [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64,
+                           _vp, _i32, _i64, _i64, _i64, _vp],
+    "m_grouped_gemm_bf16": [_vp, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i32, _i64, _i64, _i64, _vp],
+    "m_grouped_gemm_fp4": [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64,
                            _vp, _i32, _i64, _i64, _i64, _vp],
     "m_grouped_gemm_fp8_masked": [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp,
                                   _i64, _vp, _i32, _i64, _i64, _i64, _vp],
@@ -219,6 +223,58 @@ def m_grouped_gemm_fp8(A, sfa, B, sfb, offsets, out=None, stream=None):
         raise ValueError("B and sfb must be contiguous along their last dimension")
     D = _out(out, M, N, A.device)
     _check("m_grouped_gemm_fp8", lib().m_grouped_gemm_fp8(
+        _ptr(A), _mat(A, "A"), _ptr(sfa), _packed(sfa, "sfa"), _ptr(B), B.stride(1), B.stride(0),
+        _ptr(sfb), sfb.stride(1), sfb.stride(0), _ptr(D), _mat(D, "out"), _ptr(offsets), G, M, N,
+        K, _stream(stream)))
+    return D
+
+
+def _offsets_check(offsets, G):
+    if offsets.dtype != torch.int32 or offsets.dim() != 1 or not offsets.is_contiguous():
+        raise TypeError("offsets must be a contiguous int32 vector")
+    if offsets.numel() != G + 1:
+        raise ValueError("offsets must have G+1 entries")
+
+
+def m_grouped_gemm_bf16(A, B, offsets, out=None, stream=None):
+    """M-grouped BF16 GEMM.  A bf16 [M_total, K]; B bf16 [G, N, K]; offsets int32
+    [G+1] on the GPU.  Rows outside [off[0], off[G]) of ``out`` are left untouched."""
+    _dev(A, B, offsets, out)
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise TypeError("A and B must be bfloat16")
+    if B.dim() != 3 or B.stride(2) != 1:
+        raise ValueError("B must be [G, N, K], contiguous along K")
+    G, N, K = B.shape
+    _offsets_check(offsets, G)
+    M = A.shape[0]
+    if A.shape[1] != K:
+        raise ValueError("K mismatch")
+    D = _out(out, M, N, A.device)
+    _check("m_grouped_gemm_bf16", lib().m_grouped_gemm_bf16(
+        _ptr(A), _mat(A, "A"), _ptr(B), B.stride(1), B.stride(0), _ptr(D), _mat(D, "out"),
+        _ptr(offsets), G, M, N, K, _stream(stream)))
+    return D
+
+
+def m_grouped_gemm_fp4(A, sfa, B, sfb, offsets, K: int | None = None, out=None, stream=None):
+    """M-grouped FP4 GEMM.  A uint8 [M_total, K/2]; B uint8 [G, N, K/2] (two e2m1
+    values per byte, even K index in the low nibble); sfa packed int16
+    [ceil(K/64), >=M_total]; sfb packed int16 [G, ceil(K/64), >=N]; offsets int32
+    [G+1] on the GPU."""
+    _dev(A, sfa, B, sfb, offsets, out)
+    A, B = _bytes_u8(A), _bytes_u8(B)
+    if B.dim() != 3 or sfb.dim() != 3:
+        raise ValueError("B must be [G, N, K/2] and sfb [G, kp, ld]")
+    G, N, kb = B.shape
+    K = 2 * kb if K is None else K
+    _offsets_check(offsets, G)
+    M = A.shape[0]
+    if A.shape[1] * 2 < K or kb * 2 < K:
+        raise ValueError("K larger than the operands")
+    if B.stride(2) != 1 or sfb.stride(2) != 1 or sfb.dtype != torch.int16:
+        raise ValueError("B and sfb must be contiguous along their last dimension")
+    D = _out(out, M, N, A.device)
+    _check("m_grouped_gemm_fp4", lib().m_grouped_gemm_fp4(
         _ptr(A), _mat(A, "A"), _ptr(sfa), _packed(sfa, "sfa"), _ptr(B), B.stride(1), B.stride(0),
         _ptr(sfb), sfb.stride(1), sfb.stride(0), _ptr(D), _mat(D, "out"), _ptr(offsets), G, M, N,
         K, _stream(stream)))

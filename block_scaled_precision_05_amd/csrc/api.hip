@@ -65,6 +65,9 @@ __global__ void unpack_kernel(const int16_t* __restrict__ packed, int64_t mn, in
 // MoE workload (256 experts, N=2048, K=7168) 256x256 measured 1914 us against
 // 2100 us, although a quarter of its row tiles are half empty.
 #define BSG_GROUPED_CFG 256, 256, 2, 2, 64, 5, 1
+// Grouped BF16 and FP4: the dense tiles of their kind.
+#define BSG_GROUPED_BF16_CFG 256, 256, 2, 2, 64, 5, 1
+#define BSG_GROUPED_FP4_CFG 256, 256, 2, 2, 64, 5, 1
 // Masked (decode-sized experts, tens of rows each): 128-row tiles, 1x4 waves of
 // 128x128 over 512 columns, four 40 KiB stages; 256-row tiles would multiply
 // mostly empty rows (measured 419 us against 340 us on the decode case).
@@ -144,23 +147,39 @@ static int check_scales(const int16_t* sfa, int64_t ld_sfa, int64_t rows_a, cons
   return BSG_OK;
 }
 
+// Argument checks of the M-grouped GEMMs.  kind: KIND_BF16, KIND_FP8, KIND_FP4.
+int grouped_check(int kind, const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
+                  const void* B, int64_t ldb, int64_t stride_b, const int16_t* sfb,
+                  int64_t ld_sfb, int64_t stride_sfb, const void* D, int64_t ldd,
+                  const int32_t* group_offsets, int32_t G, int64_t M_total, int64_t N, int64_t K) {
+  if (G < 0 || G > 1024) return G < 0 ? BSG_ERR_INVALID_ARG : BSG_ERR_UNSUPPORTED_SHAPE;
+  const int64_t gran = kind == KIND_BF16 ? 8 : (kind == KIND_FP8 ? 128 : 32);
+  const int64_t k_bytes = kind == KIND_BF16 ? 2 * K : (kind == KIND_FP8 ? K : K / 2);
+  const int64_t elem = kind == KIND_BF16 ? 2 : 1;
+  int st = check_dense(A, lda, B, ldb, D, ldd, M_total, N, K, gran, k_bytes, elem);
+  if (st != BSG_OK || M_total == 0 || N == 0 || G == 0) return st;
+  if (!group_offsets) return BSG_ERR_INVALID_ARG;
+  int64_t kp = 0;
+  if (kind != KIND_BF16) {
+    const int64_t b_rows = kind == KIND_FP8 ? (N + 127) / 128 : N;
+    st = check_scales(sfa, ld_sfa, M_total, sfb, ld_sfb, b_rows, K);
+    if (st != BSG_OK) return st;
+    kp = (K / gran + 1) / 2;
+  }
+  if (G > 1 && (stride_b < (N - 1) * ldb + k_bytes / elem || (K > 0 && stride_sfb < kp * ld_sfb)))
+    return BSG_ERR_INVALID_ARG;
+  if (stride_b < 0 || stride_sfb < 0) return BSG_ERR_INVALID_ARG;
+  if ((stride_b * elem) % 16) return BSG_ERR_MISALIGNED;
+  return BSG_OK;
+}
+
 int grouped_fp8_check(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
                       const void* B, int64_t ldb, int64_t stride_b, const int16_t* sfb,
                       int64_t ld_sfb, int64_t stride_sfb, const void* D, int64_t ldd,
                       const int32_t* group_offsets, int32_t G, int64_t M_total, int64_t N,
                       int64_t K) {
-  if (G < 0 || G > 1024) return G < 0 ? BSG_ERR_INVALID_ARG : BSG_ERR_UNSUPPORTED_SHAPE;
-  int st = check_dense(A, lda, B, ldb, D, ldd, M_total, N, K, 128, K, 1);
-  if (st != BSG_OK || M_total == 0 || N == 0 || G == 0) return st;
-  if (!group_offsets) return BSG_ERR_INVALID_ARG;
-  st = check_scales(sfa, ld_sfa, M_total, sfb, ld_sfb, (N + 127) / 128, K);
-  if (st != BSG_OK) return st;
-  const int64_t kp = (K / 128 + 1) / 2;
-  if (G > 1 && (stride_b < (N - 1) * ldb + K || (K > 0 && stride_sfb < kp * ld_sfb)))
-    return BSG_ERR_INVALID_ARG;
-  if (stride_b < 0 || stride_sfb < 0) return BSG_ERR_INVALID_ARG;
-  if (stride_b % 16) return BSG_ERR_MISALIGNED;
-  return BSG_OK;
+  return grouped_check(KIND_FP8, A, lda, sfa, ld_sfa, B, ldb, stride_b, sfb, ld_sfb, stride_sfb, D,
+                       ldd, group_offsets, G, M_total, N, K);
 }
 
 }  // namespace bsg
@@ -327,6 +346,64 @@ int m_grouped_gemm_fp8_masked(const void* A, int64_t lda, const int16_t* sfa, in
   a.G = G;
   if (sv_ok(sfa, ld_sfa)) return launch<KIND_FP8, BSG_MASKED_CFG, true, 1>(a, (hipStream_t)stream);
   return launch<KIND_FP8, BSG_MASKED_CFG, true, 0>(a, (hipStream_t)stream);
+}
+
+int m_grouped_gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t stride_b,
+                        void* D, int64_t ldd, const int32_t* group_offsets, int32_t G,
+                        int64_t M_total, int64_t N, int64_t K, void* stream) {
+  const int st = grouped_check(KIND_BF16, A, lda, nullptr, 0, B, ldb, stride_b, nullptr, 0, 0, D,
+                               ldd, group_offsets, G, M_total, N, K);
+  if (st != BSG_OK || M_total == 0 || N == 0 || G == 0) return st;
+  GemmArgs a = {};
+  a.A = (const uint8_t*)A;
+  a.B = (const uint8_t*)B;
+  a.D = (uint16_t*)D;
+  a.offsets = group_offsets;
+  a.lda = lda * 2;
+  a.ldb = ldb * 2;
+  a.ldd = ldd;
+  a.stride_b = stride_b * 2;
+  a.M = (int32_t)M_total;
+  a.N = (int32_t)N;
+  a.K = (int32_t)K;
+  a.k_bytes = (int32_t)(2 * K);
+  a.G = G;
+  return launch<KIND_BF16, BSG_GROUPED_BF16_CFG, true>(a, (hipStream_t)stream);
+}
+
+int m_grouped_gemm_fp4(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
+                       const void* B, int64_t ldb, int64_t stride_b,
+                       const int16_t* sfb, int64_t ld_sfb, int64_t stride_sfb,
+                       void* D, int64_t ldd, const int32_t* group_offsets, int32_t G,
+                       int64_t M_total, int64_t N, int64_t K, void* stream) {
+  const int st = grouped_check(KIND_FP4, A, lda, sfa, ld_sfa, B, ldb, stride_b, sfb, ld_sfb,
+                               stride_sfb, D, ldd, group_offsets, G, M_total, N, K);
+  if (st != BSG_OK || M_total == 0 || N == 0 || G == 0) return st;
+  GemmArgs a = {};
+  a.A = (const uint8_t*)A;
+  a.B = (const uint8_t*)B;
+  a.D = (uint16_t*)D;
+  a.sfa = sfa;
+  a.sfb = sfb;
+  a.offsets = group_offsets;
+  a.lda = lda;
+  a.ldb = ldb;
+  a.ldd = ldd;
+  a.ld_sfa = ld_sfa;
+  a.ld_sfb = ld_sfb;
+  a.stride_b = stride_b;
+  a.stride_sfb = stride_sfb;
+  a.M = (int32_t)M_total;
+  a.N = (int32_t)N;
+  a.K = (int32_t)K;
+  a.k_bytes = (int32_t)(K / 2);
+  a.kp_count = (int32_t)((K / 32 + 1) / 2);
+  a.sfb_rows = (int32_t)N;
+  a.G = G;
+  // the per-expert scale arrays must all allow 8-byte loads: base and stride
+  const bool sv = sv_ok(sfa, ld_sfa) && sv_ok(sfb, ld_sfb) && (stride_sfb % 4 == 0);
+  if (sv) return launch<KIND_FP4, BSG_GROUPED_FP4_CFG, true, 1>(a, (hipStream_t)stream);
+  return launch<KIND_FP4, BSG_GROUPED_FP4_CFG, true, 0>(a, (hipStream_t)stream);
 }
 
 static int launch_pack(bool unpack, const void* src, int64_t mn, int64_t kb, int64_t ld_src,

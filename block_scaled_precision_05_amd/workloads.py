@@ -17,6 +17,8 @@ para calculo e comunicacao de IA", section "Resultados de kernel e comunicacao")
   bf16_large    BF16 4096x7168x16384
   fp8_large     FP8 4096x7168x16384, scales as fp8_mid
   moe_fp8       M-grouped FP8: 256 experts, N=2048, K=7168, Zipf(1.1) routing
+  moe_bf16      the same routing and shape in BF16
+  moe_fp4       the same routing and shape in FP4 (1x32 scales)
   fp4_large     FP4 4096x7168x16384, 1x32 UE8M0 scales on both operands
   act_large     bf16 activations 4096x16384 (A of the dense shape), to be quantised
   act_moe       bf16 activations 16384x7168 (the MoE tokens), to be quantised
@@ -170,7 +172,7 @@ class Workload:
     @property
     def flops(self) -> float:
         """Algorithmic flops, 2*M*N*K (useful rows only for the grouped case)."""
-        if self.kind == "grouped_fp8":
+        if self.kind.startswith("grouped_"):
             return 2.0 * float(self.meta["useful_rows"]) * self.N * self.K
         if self.kind == "masked_fp8":
             return 2.0 * float(self.meta["useful_rows"]) * self.N * self.K
@@ -184,6 +186,8 @@ SHAPES = {
     "fp8_mid": ("fp8", 1024, 2048, 4096, 1002),
     "bf16_large": ("bf16", 4096, 7168, 16384, 1003),
     "moe_fp8": ("grouped_fp8", None, 2048, 7168, 1004),
+    "moe_bf16": ("grouped_bf16", None, 2048, 7168, 1011),
+    "moe_fp4": ("grouped_fp4", None, 2048, 7168, 1012),
     "fp4_large": ("fp4", 4096, 7168, 16384, 1005),
     "fp8_large": ("fp8", 4096, 7168, 16384, 1006),
     "act_large": ("act", 4096, None, 16384, 1007),
@@ -213,9 +217,11 @@ def dense(kind: str, M: int, N: int, K: int, seed: int, device="cpu", name: str 
 
 
 def grouped(G: int, N: int, K: int, seed: int, device="cpu", counts=None, name="custom",
-            align: int = 128, tokens: int = 16384, topk: int = 6, zipf: float = 1.1):
-    """M-grouped FP8 inputs.  ``counts`` (int sequence, length G) overrides the
-    Zipf routing draw; counts are padded to multiples of ``align``."""
+            align: int = 128, tokens: int = 16384, topk: int = 6, zipf: float = 1.1,
+            kind: str = "fp8"):
+    """M-grouped inputs (kind "fp8", "bf16" or "fp4").  ``counts`` (int sequence,
+    length G) overrides the Zipf routing draw; counts are padded to multiples of
+    ``align``.  Padding rows hold zero operands (scale byte 127)."""
     g = _gen(device, seed)
     if counts is None:
         counts = moe_counts(g, device, tokens=tokens, topk=topk, experts=G, zipf=zipf)
@@ -223,10 +229,18 @@ def grouped(G: int, N: int, K: int, seed: int, device="cpu", counts=None, name="
         counts = torch.as_tensor(list(counts), dtype=torch.int64, device=device)
     off = pad_offsets(counts, align)
     m_total = int(off[-1].item())
-    A, sfa = fp8_operand(max(m_total, 1), K, 1, g, device)
+    rows = max(m_total, 1)
+    sfa = None
+    if kind == "fp8":
+        A, sfa = fp8_operand(rows, K, 1, g, device)
+    elif kind == "fp4":
+        A, sfa = fp4_operand(rows, K, g, device)
+    elif kind == "bf16":
+        A = bf16_normal(rows, K, g, device)
+    else:
+        raise ValueError(kind)
     A = A[:m_total]
-    sfa = sfa[:m_total]
-    # zero the padding rows of every expert (codes 0, scale byte 127)
+    # zero the padding rows of every expert
     valid = torch.zeros(m_total, dtype=torch.bool, device=device)
     starts = off[:-1].to(torch.int64)
     for e in range(G):
@@ -235,15 +249,23 @@ def grouped(G: int, N: int, K: int, seed: int, device="cpu", counts=None, name="
         if c:
             valid[s:s + c] = True
     A[~valid] = 0
-    sfa[~valid] = 127
+    if sfa is not None:
+        sfa = sfa[:m_total]
+        sfa[~valid] = 127
     Bs, sfbs = [], []
     for _ in range(G):
-        b, sb = fp8_operand(N, K, 128, g, device)
+        if kind == "fp8":
+            b, sb = fp8_operand(N, K, 128, g, device)
+        elif kind == "fp4":
+            b, sb = fp4_operand(N, K, g, device)
+        else:
+            b, sb = bf16_normal(N, K, g, device), None
         Bs.append(b)
         sfbs.append(sb)
-    w = Workload(name, "grouped_fp8", m_total, N, K)
-    w.tensors.update(A=A.contiguous(), sfa=sfa.contiguous(), B=torch.stack(Bs),
-                     sfb=torch.stack(sfbs), offsets=off, counts=counts)
+    w = Workload(name, "grouped_" + kind, m_total, N, K)
+    w.tensors.update(A=A.contiguous(), B=torch.stack(Bs), offsets=off, counts=counts)
+    if sfa is not None:
+        w.tensors.update(sfa=sfa.contiguous(), sfb=torch.stack(sfbs))
     w.meta.update(seed=seed, G=G, useful_rows=int(counts.sum().item()), m_total=m_total,
                   routing=f"multinomial({tokens}x{topk}), zipf {zipf}, pad {align}")
     return w
@@ -326,8 +348,8 @@ def make(name: str, device="cpu", seed: int | None = None) -> Workload:
     """One of the named workloads in ``SHAPES``."""
     kind, M, N, K, default_seed = SHAPES[name]
     seed = default_seed if seed is None else seed
-    if kind == "grouped_fp8":
-        w = grouped(256, N, K, seed, device=device, name=name)
+    if kind.startswith("grouped_"):
+        w = grouped(256, N, K, seed, device=device, name=name, kind=kind[len("grouped_"):])
     elif kind == "moe_ffn":
         w = moe_ffn(seed, device=device, name=name)
     elif kind == "masked_fp8":

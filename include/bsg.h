@@ -125,6 +125,28 @@ int m_grouped_gemm_fp8(const void* A, int64_t lda, const int16_t* sfa, int64_t l
                        void* D, int64_t ldd, const int32_t* group_offsets, int32_t G,
                        int64_t M_total, int64_t N, int64_t K, void* stream);
 
+/* M-grouped BF16 GEMM: as m_grouped_gemm_fp8 without scales (the pages list BF16
+ * among the formats and grouped MoE GEMM among the kernels: same passages).
+ *   A: bf16 [M_total][lda]; B_g = B + g*stride_b: bf16 [N][ldb] (strides in bf16
+ *   elements); D: bf16 [M_total][ldd]; group_offsets: DEVICE int32 [G+1] with the
+ *   same precondition and row rules as m_grouped_gemm_fp8.
+ *   Requires K % 8 == 0, G <= 1024, stride_b >= (N-1)*ldb + K, stride_b*2 % 16 == 0,
+ *   plus the gemm_bf16 requirements. */
+int m_grouped_gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t stride_b,
+                        void* D, int64_t ldd, const int32_t* group_offsets, int32_t G,
+                        int64_t M_total, int64_t N, int64_t K, void* stream);
+
+/* M-grouped FP4 GEMM: as m_grouped_gemm_fp8 with the FP4 operand and scale rules
+ * of gemm_fp4_blockscaled (1x32 UE8M0 scales on both operands; expert g's B scales
+ * sfb + g*stride_sfb, scale rows = N).
+ *   Requires K % 32 == 0, G <= 1024, stride_b >= (N-1)*ldb + K/2 (bytes),
+ *   stride_sfb >= ceil(K/64)*ld_sfb, plus the gemm_fp4_blockscaled requirements. */
+int m_grouped_gemm_fp4(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
+                       const void* B, int64_t ldb, int64_t stride_b,
+                       const int16_t* sfb, int64_t ld_sfb, int64_t stride_sfb,
+                       void* D, int64_t ldd, const int32_t* group_offsets, int32_t G,
+                       int64_t M_total, int64_t N, int64_t K, void* stream);
+
 /* Masked M-grouped FP8 GEMM: every expert owns a fixed capacity of max_m rows and
  * a device-side count of valid rows (the pages list masked grouped GEMM among
  * the interfaces the reference repository declares but leaves unimplemented:

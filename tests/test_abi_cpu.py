@@ -23,7 +23,8 @@ def test_header_declares_the_api():
     for n in ("gemm_bf16", "gemm_fp8_blockscaled", "gemm_fp4_blockscaled", "m_grouped_gemm_fp8",
               "pack_ue8m0_scales", "unpack_ue8m0_scales", "bsg_status_string",
               "quantize_fp8_per_token", "quantize_fp4_per_token", "swiglu_quantize_fp8",
-              "moe_ffn_fp8", "m_grouped_gemm_fp8_masked"):
+              "moe_ffn_fp8", "m_grouped_gemm_fp8_masked", "m_grouped_gemm_bf16",
+              "m_grouped_gemm_fp4"):
         assert n in names
 
 
@@ -214,6 +215,32 @@ def test_moe_ffn_validation_launches_nothing_on_a_bad_late_argument():
     assert f(*bad) == bsg.BSG_ERR_UNSUPPORTED_SHAPE
     empty = list(args); empty[18] = 0                        # M_total = 0: no-op
     assert f(*empty) == bsg.BSG_OK
+
+
+def test_grouped_bf16_fp4_validation():
+    L = bsg.lib()
+    G, M, N, K = 4, 512, 256, 512
+    bf = [P, K, 0x100000, K, N * K, 0x900000, N, P2, G, M, N, K, None]
+    bad = list(bf); bad[9] = -1
+    assert L.m_grouped_gemm_bf16(*bad) == bsg.BSG_ERR_INVALID_ARG
+    bad = list(bf); bad[11] = 100                          # K % 8
+    assert L.m_grouped_gemm_bf16(*bad) == bsg.BSG_ERR_UNSUPPORTED_SHAPE
+    bad = list(bf); bad[4] = N * K - 8                     # stride_b too small
+    assert L.m_grouped_gemm_bf16(*bad) == bsg.BSG_ERR_INVALID_ARG
+    bad = list(bf); bad[7] = 0                             # no offsets
+    assert L.m_grouped_gemm_bf16(*bad) == bsg.BSG_ERR_INVALID_ARG
+    bad = list(bf); bad[8] = 0                             # G = 0: no-op
+    assert L.m_grouped_gemm_bf16(*bad) == bsg.BSG_OK
+    f4 = [P, K // 2, P2, M, 0x100000, K // 2, N * K // 2, P2, N, 8 * N,
+          0x900000, N, P2, G, M, N, K, None]
+    bad = list(f4); bad[16] = 48                           # K % 32
+    assert L.m_grouped_gemm_fp4(*bad) == bsg.BSG_ERR_UNSUPPORTED_SHAPE
+    bad = list(f4); bad[8] = N - 1                         # ld_sfb < N
+    assert L.m_grouped_gemm_fp4(*bad) == bsg.BSG_ERR_INVALID_ARG
+    bad = list(f4); bad[9] = 8 * N - 1                     # stride_sfb too small
+    assert L.m_grouped_gemm_fp4(*bad) == bsg.BSG_ERR_INVALID_ARG
+    bad = list(f4); bad[13] = 2000                         # G > 1024
+    assert L.m_grouped_gemm_fp4(*bad) == bsg.BSG_ERR_UNSUPPORTED_SHAPE
 
 
 def test_masked_validation():
