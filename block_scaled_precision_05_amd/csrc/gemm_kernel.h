@@ -26,12 +26,16 @@
 //
 // Scale handling (FP8 and FP4): the UE8M0 bytes go straight into the scaled
 // MFMA's per-lane scale operand, so promotion by 2^(e-127) happens inside the
-// matrix core and is exact.  FP8 uses one byte per (row, 128-K block): the stage
-// is exactly one K-block, so every MFMA of a stage sees a row-uniform scale.
-// FP4 uses one byte per (row, 32-K block): each lane's 16-byte operand is
-// exactly one K-block and carries that block's byte.  Scale words are loaded
-// from global memory together with the tile copy of their stage, and are only
-// decoded after the barrier that waits for that copy, so they never add a wait.
+// matrix core and is exact; the instruction's per-operand byte select picks one
+// of the four bytes of the 32-bit scale register.  FP8 uses one byte per (row,
+// 128-K block): the two 64-byte stages of a pair lie in one K-block and share
+// its scale word.  FP4 uses one byte per (row, 32-K block): each lane's 16-byte
+// operand is exactly one K-block and carries that block's byte.  Operands with a
+// scale per row permute the rows of each 128-row wave block (GemmTile::PERM_A,
+// PERM_B) so that a lane's four fragment rows, and their packed scale words, are
+// adjacent: one 8-byte load fetches all four.  Scale words are loaded together
+// with the tile copy of their stage and only decoded after the barrier that
+// waits for that copy, so they never add a wait.
 #pragma once
 
 #include <hip/hip_runtime.h>
