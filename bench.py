@@ -86,7 +86,7 @@ def log(msg):
 # Kernel sources behind each measured kind: a change to any of them detaches the
 # committed rocprofv3 counters from the kernel.
 SOURCES = {
-    "gemm": ("gemm_kernel.h", "api.hip"),
+    "gemm": ("gemm_kernel.h", "configs.h"),
     "quant": ("quant.hip",),
 }
 
