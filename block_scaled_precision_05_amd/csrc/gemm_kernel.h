@@ -730,10 +730,15 @@ void gemm_kernel(const GemmArgs args) {
 
     uint32_t sa_cur[FM] = {}, sb_cur[FN] = {};
 
-    // Prologue: the previous tile's LDS reads are over once every wave is here;
-    // then stages 0 .. T0-1 are put in flight and stage 0 is waited for.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    // Prologue: the previous tile's LDS reads are over once every wave has
+    // drained its own and met the others here; then stages 0 .. T0-1 are put in
+    // flight and stage 0 is waited for.  The previous tile's D stores are not
+    // waited for (a __syncthreads would wait for every outstanding memory
+    // operation): their latency overlaps this tile's first copies, and since
+    // loads complete in order, the prologue's vmcnt wait below still covers
+    // stage 0 whatever the stores do.
+    wait_vm_lds<63>();
+    ring_barrier();
     // Paired copies due at a k-step g: chunk chunk_at(g) of the pair started at
     // the barrier of stage pair_start(g); chunk 0 also loads the first stage's
     // scale words, chunk 1 the second's.
