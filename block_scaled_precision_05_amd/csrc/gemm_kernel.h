@@ -323,10 +323,12 @@ __device__ int grouped_total_row_tiles(const int32_t* off, int G, int cap) {
   return total;
 }
 
-// Finds the expert owning row tile `rt`; returns false when rt is past the end.
+// Finds the expert owning row tile `rt` (row tiles numbered over all experts in
+// order); returns false when rt is past the end.  Outputs the expert g, the index
+// of its first row tile, its number of row tiles and its row range.
 template <int BM>
 __device__ bool grouped_find(const int32_t* off, int G, int cap, int rt, GroupCursor& cur, int& g,
-                             int& row_lo, int& row_hi) {
+                             int& tile0, int& ntiles, int& row_lo, int& row_hi) {
   const int lane = threadIdx.x & 63;
   while (cur.g0 < G) {
     int t = group_tiles<BM>(off, cur.g0 + lane, G, cap);
@@ -335,13 +337,10 @@ __device__ bool grouped_find(const int32_t* off, int G, int cap, int rt, GroupCu
     if (hit) {
       int j = __builtin_ctzll(hit);
       int incl_j = __shfl(incl, j, 64);
-      int t_j = __shfl(t, j, 64);
+      ntiles = __shfl(t, j, 64);
       g = cur.g0 + j;
-      int tile_in_g = rt - (incl_j - t_j);
-      int base, end;
-      group_range(off, g, cap, base, end);
-      row_lo = base + tile_in_g * BM;
-      row_hi = row_lo + BM < end ? row_lo + BM : end;
+      tile0 = incl_j - ntiles;
+      group_range(off, g, cap, row_lo, row_hi);
       return true;
     }
     cur.before = __shfl(incl, 63, 64);
@@ -472,10 +471,18 @@ void gemm_kernel(const GemmArgs args) {
     const uint8_t* Bbase = args.B;
     const int16_t* sfb = args.sfb;
     if constexpr (GROUPED) {
-      const int rt = p / args.tiles_n;
-      n0 = (p - rt * args.tiles_n) * BN;
-      int g;
-      if (!grouped_find<BM>(args.offsets, args.G, args.cap, rt, cur, g, m0, m_end)) break;
+      // An expert's tiles form a contiguous range of the order; inside it they
+      // are rasterised like a dense matrix (super-rows of row tiles, N-major), so
+      // the tiles an XCD runs together share expert weights as well as rows.
+      int g, tile0, ntl, row_lo, row_hi;
+      if (!grouped_find<BM>(args.offsets, args.G, args.cap, p / args.tiles_n, cur, g, tile0, ntl,
+                            row_lo, row_hi))
+        break;
+      int tm, tn;
+      raster(p - tile0 * args.tiles_n, ntl, args.tiles_n, tm, tn);
+      m0 = row_lo + tm * BM;
+      m_end = m0 + BM < row_hi ? m0 + BM : row_hi;
+      n0 = tn * BN;
       Bbase += (int64_t)g * args.stride_b;
       sfb += (int64_t)g * args.stride_sfb;
     } else {
