@@ -90,9 +90,15 @@ struct GemmArgs {
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr uint32_t kOOB = 0x80000000u;  // a byte offset past any valid record count
 
+// Every caller passes a wave-uniform base and size; reading them from the first
+// lane states that to the compiler, which otherwise may keep a descriptor in
+// VGPRs and wrap each buffer access in a loop over lanes.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           kRsrcWord3);
+  const uint64_t a = (uint64_t)base;
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(lo | (hi << 32)), (short)0,
+                                           __builtin_amdgcn_readfirstlane((int)bytes), kRsrcWord3);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {

@@ -78,6 +78,20 @@ def test_grouped_small_full(kind, align):
 
 
 @pytest.mark.parametrize("kind", ["bf16", "fp4"])
+def test_grouped_half_and_full_row_tiles(kind):
+    """Last row tiles of at most half a tile's rows (128, 1, and 257 = a full
+    tile then one row) beside full ones, ragged last column tile (N = 320)."""
+    _say(f"grouped {kind} half and full row tiles")
+    K = 512
+    w = workloads.grouped(8, 320, K, seed=62, device=DEV, counts=[129, 128, 257, 1, 384, 255, 0, 64],
+                          align=1, kind=kind)
+    got = _run(kind, w, pad_rows=3)
+    off = w.tensors["offsets"].cpu().numpy()
+    _check(kind, w, got, np.arange(off[0], off[-1]), f"grouped {kind} half/full tiles")
+    assert np.all(got[off[-1]:] == SENTINEL)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp4"])
 def test_grouped_moe_workload_sampled(kind):
     """256 experts, N=2048, K=7168, Zipf routing, in the launch the benchmark
     times; the oracle checks the first, middle and last row of 12 experts."""

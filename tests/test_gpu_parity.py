@@ -351,6 +351,32 @@ def test_grouped_small_full():
             assert_parity(Dh[lo:hi], ref[lo:hi], na[lo:hi], nb, what=f"grouped small expert {g}")
 
 
+def test_grouped_half_and_full_row_tiles():
+    """Experts whose last row tile holds at most half a tile's rows (129 = one
+    full-height tile, 128 and 1 = half tiles, 257 = a full tile then one row)
+    next to multi-tile experts, with a ragged last column tile (N = 320)."""
+    counts = [129, 128, 257, 1, 384, 255, 0, 64]
+    G, N, K = len(counts), 320, 1024
+    w = workloads.grouped(G, N, K, seed=24, device=DEV, counts=counts, align=1)
+    D = run_grouped(w)
+    torch.cuda.synchronize()
+    t = w.tensors
+    off = t["offsets"].cpu().numpy()
+    rows = np.arange(off[-1])
+    A8, sfa = _u8(t["A"]), oracle.pack_scales(t["sfa"].cpu().numpy())
+    ref = oracle.grouped_fp8(A8, sfa, np.stack([_u8(b) for b in t["B"]]),
+                             np.stack([oracle.pack_scales(s.cpu().numpy()) for s in t["sfb"]]),
+                             off, rows=rows)
+    na = oracle.row_norms("e4m3", A8, sfa)
+    Dh = gpu_bits(D)
+    for g in range(G):
+        lo, hi = off[g], off[g + 1]
+        if hi > lo:
+            nb = oracle.row_norms("e4m3", _u8(t["B"][g]), oracle.pack_scales(t["sfb"][g].cpu().numpy()),
+                                  gran_mn=128)
+            assert_parity(Dh[lo:hi], ref[lo:hi], na[lo:hi], nb, what=f"half/full tiles expert {g}")
+
+
 def test_grouped_unaligned_offsets_and_untouched_rows():
     """Offsets need no alignment; rows outside [off[0], off[G]) are not written."""
     G, N, K = 5, 256, 256
