@@ -334,6 +334,18 @@ def summarize(kind, r, steps):
     if kind == "masked":
         out["gb_per_s"] = r["min_bytes"] * steps / r["wall_s"] / 1e9
         out["frac_of_hbm_peak"] = out["gb_per_s"] / HBM_PEAK_GBS
+    # per-launch roofline of the case's GEMM kernel (the FFN core: its three
+    # kernels together, against the FP8 peak)
+    sha = kernel_sources_sha()
+    if kind == "masked":
+        ach = r["min_bytes"] / (mean_us * 1e-6) / 1e9
+        out["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        ach = r["flops"] / (mean_us * 1e-6) / 1e12
+        out["roofline"] = {"bound": "mfma", "achieved": ach, "peak": PEAK[kind], "unit": "TFLOP/s"}
+    out["roofline"].update(kernel=KERNEL_NAME[kind], frac=ach / out["roofline"]["peak"],
+                           traffic=None if kind == "moe_ffn" else load_traffic(kind, sha),
+                           src_sha=sha)
     if "cold_us" in r:
         c = sorted(r["cold_us"])
         out["cold_l2_us_median"] = statistics.median(c)
