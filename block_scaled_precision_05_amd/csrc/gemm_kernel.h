@@ -80,7 +80,7 @@ struct GemmArgs {
   int32_t tiles_m;          // dense: M tiles
   int32_t tiles_n;
   int32_t G;                // grouped: number of experts
-  int32_t d_vec;            // 1 when D rows allow 8-byte stores (D and ldd*2 8-aligned)
+  int32_t d_vec;            // 1 when D rows allow 16-byte stores (D and ldd*2 16-aligned)
   int32_t cap;              // grouped: 0 = contiguous experts, rows [offsets[g], offsets[g+1]);
                             // > 0 = masked layout, rows [g*cap, g*cap + min(offsets[g], cap))
 };
@@ -164,6 +164,17 @@ struct GemmTile {
   // same number of copies and the vmcnt arithmetic holds for all of them.
   static constexpr bool DUMMY = A_LOADS * NW != A_COPIES || B_LOADS * NW != B_COPIES;
   static constexpr int LDS_BYTES = NS * STAGE_BYTES + (DUMMY ? 1024 : 0);
+  // Epilogue staging: each wave's TM x TN bf16 block, row-major (EPI_ROW bytes a
+  // row) in the ring's LDS; 16-byte chunk c of row r sits at chunk c ^ epi_swz(r),
+  // which walks the chunks along the rows that one lane-row group writes at once
+  // (consecutive rows, or every fourth row when the rows are permuted).
+  static constexpr int EPI_ROW = 2 * TN;
+  static constexpr int EPI_WAVE_BYTES = TM * EPI_ROW;
+  static constexpr int EPI_CHUNKS = EPI_ROW / 16;
+  static_assert(TN % 8 == 0 && 64 % (TN / 8) == 0 && TM % (64 / (TN / 8)) == 0,
+                "staged rows must split evenly over the lanes");
+  static_assert(NW * EPI_WAVE_BYTES <= NS * STAGE_BYTES, "the epilogue staging must fit the ring");
+  static_assert((EPI_CHUNKS & (EPI_CHUNKS - 1)) == 0, "the chunk swizzle is a mask");
   // FP8 B scales: one 128-row block per wave when the wave's TN rows stay inside
   // one block, else one word per 32-row fragment.
   static constexpr bool ONE_B_SCALE = TN <= 128 && 128 % TN == 0 && BN % 128 == 0;
@@ -187,6 +198,9 @@ struct GemmTile {
     return on ? ((x & ~127) | ((x & 31) << 2) | ((x >> 5) & 3)) : x;
   }
   static constexpr int perm_a(int x) { return perm_rows(PERM_A, x); }
+  static constexpr int epi_swz(int row) {
+    return (PERM_A ? (row >> 2) : row) & (EPI_CHUNKS - 1);
+  }
   static constexpr int perm_b(int x) { return perm_rows(PERM_B, x); }
   static constexpr int NSC = SV ? (1 + (PERM_B ? 1 : NSB)) * SW : (FM + NSB) * SW;
   static constexpr int VMEM_PER_STAGE = N_DMA + NSC;
@@ -844,46 +858,83 @@ void gemm_kernel(const GemmArgs args) {
     // Permuted rows: fragment a's row l32 is tile row 4*l32 + a; with B permuted
     // too (FP4), fragment b's column i is tile column 4*i + b, so the four
     // fragments b hold four consecutive columns in the same register.
+    //
+    // Stored straight from those registers, every store instruction would put 16
+    // bytes into each of 32 rows, one L2 request per 16 bytes.  Instead each wave
+    // converts its TM x TN block to bf16 into its own part of the idle LDS ring,
+    // row-major, then stores it row by row with 16 bytes per lane, so an
+    // instruction writes whole 2*TN-byte row segments.  The 16-byte chunks of a
+    // staged row are XOR-swizzled by the row (epi_swz) so that the 32 rows one
+    // write instruction touches spread over the banks.
+    //
+    // The ring is idle once no copy is in flight (the dead stages' out-of-range
+    // copies still write zeros into it) and every wave has passed the barrier.
+    wait_vm_lds<0>();
+    ring_barrier();
+    // rows of this wave's block that exist (an expert's last row tile, the
+    // matrix edge): a wave with none skips its part
+    const int rows_w = m_end - (m0 + wm * T::TM) < T::TM ? m_end - (m0 + wm * T::TM) : T::TM;
+    if (rows_w <= 0) continue;
+    uint8_t* const stg = smem + wave * T::EPI_WAVE_BYTES;
+    // The lane index, made opaque here: every staging address derives from it,
+    // and the compiler would otherwise hoist all of them out of the tile loop and
+    // spill them.
+    int el = lane;
+    asm volatile("" : "+v"(el));
+    const int el32 = el & 31, elg = el >> 5;
+    auto stage_quad = [&](int row, int col, float v0, float v1, float v2, float v3) {
+      // four consecutive columns col .. col+3 (col a multiple of 4) of `row`
+      const int chunk = (col >> 3) ^ T::epi_swz(row);
+      const i32x2_t w = {(int)pack_bf16x2(v0, v1), (int)pack_bf16x2(v2, v3)};
+      *(i32x2_t*)(stg + row * T::EPI_ROW + 16 * chunk + 2 * (col & 7)) = w;
+    };
 #pragma unroll
     for (int a = 0; a < FM; ++a) {
-      const int m = m0 + wm * T::TM + (T::PERM_A ? 4 * l32 + a : 32 * a + l32);
-      if (m >= m_end) continue;
-      uint16_t* drow = args.D + (int64_t)m * args.ldd;
+      const int row = T::PERM_A ? 4 * el32 + a : 32 * a + el32;
       if constexpr (T::PERM) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int n = n0 + wn * T::TN + 4 * (8 * (r / 4) + 4 * lg + r % 4);
-          const float v0 = acc[a][0][r], v1 = acc[a][1][r], v2 = acc[a][2][r], v3 = acc[a][3][r];
-          if (args.d_vec && n + 3 < n_end) {
-            i32x2_t w = {(int)pack_bf16x2(v0, v1), (int)pack_bf16x2(v2, v3)};
-            *(i32x2_t*)(drow + n) = w;
-          } else {
-            const float vv[4] = {v0, v1, v2, v3};
+        for (int r = 0; r < 16; ++r)
+          stage_quad(row, 4 * (8 * (r / 4) + 4 * elg + r % 4), acc[a][0][r], acc[a][1][r], acc[a][2][r],
+                     acc[a][3][r]);
+      } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (n + e < n_end) drow[n + e] = (uint16_t)(pack_bf16x2(vv[e], 0.0f) & 0xFFFF);
-          }
-        }
-        continue;
+        for (int b = 0; b < FN; ++b)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            stage_quad(row, 32 * b + 8 * q + 4 * elg, acc[a][b][4 * q], acc[a][b][4 * q + 1],
+                       acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]);
       }
+      // one fragment row at a time: the compiler would otherwise move every
+      // accumulator into VGPRs first and spill
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // (a wave reads back only what it wrote; its LDS accesses execute in order)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    constexpr int LPR = T::TN / 8;   // lanes per staged row, 16 bytes each
+    constexpr int RPI = 64 / LPR;    // rows per store instruction
+    const int rr = el / LPR, seg = el % LPR;
+    const int n = n0 + wn * T::TN + 8 * seg;
+    const bool vec = args.d_vec && n + 7 < n_end;
+    // Walked with running pointers and not unrolled: precomputed addresses for
+    // every row would not fit in registers alongside the next tile's state.
+    const uint8_t* src = stg + rr * T::EPI_ROW;
+    uint16_t* d = args.D + (int64_t)(m0 + wm * T::TM + rr) * args.ldd + n;
+    const int64_t dstep = (int64_t)RPI * args.ldd;
+#pragma unroll 1
+    for (int row0 = 0; row0 < rows_w; row0 += RPI) {
+      const int row = row0 + rr;
+      const i32x4_t v = *(const i32x4_t*)(src + 16 * (seg ^ T::epi_swz(row)));
+      if (row < rows_w) {
+        if (vec) {
+          *(i32x4_t*)d = v;
+        } else {
 #pragma unroll
-      for (int b = 0; b < FN; ++b) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n0 + wn * T::TN + 32 * b + 8 * q + 4 * lg;
-          const float v0 = acc[a][b][4 * q + 0], v1 = acc[a][b][4 * q + 1];
-          const float v2 = acc[a][b][4 * q + 2], v3 = acc[a][b][4 * q + 3];
-          if (args.d_vec && n + 3 < n_end) {
-            i32x2_t w = {(int)pack_bf16x2(v0, v1), (int)pack_bf16x2(v2, v3)};
-            *(i32x2_t*)(drow + n) = w;
-          } else {
-            const float vv[4] = {v0, v1, v2, v3};
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (n + e < n_end) drow[n + e] = (uint16_t)(pack_bf16x2(vv[e], 0.0f) & 0xFFFF);
-          }
+          for (int e = 0; e < 8; ++e)
+            if (n + e < n_end) d[e] = (uint16_t)(((uint32_t)v[e / 2] >> (16 * (e % 2))) & 0xFFFF);
         }
       }
+      src += RPI * T::EPI_ROW;
+      d += dstep;
     }
   }
 }
