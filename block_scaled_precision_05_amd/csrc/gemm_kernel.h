@@ -80,7 +80,7 @@ struct GemmArgs {
   int32_t tiles_m;          // dense: M tiles
   int32_t tiles_n;
   int32_t G;                // grouped: number of experts
-  int32_t d_vec;            // 1 when D rows allow 16-byte stores (D and ldd*2 16-aligned)
+  int32_t d_vec;            // widest D store: 2 = 16 bytes (D and ldd*2 16-aligned), 1 = 8, 0 = 2
   int32_t cap;              // grouped: 0 = contiguous experts, rows [offsets[g], offsets[g+1]);
                             // > 0 = masked layout, rows [g*cap, g*cap + min(offsets[g], cap))
 };
@@ -914,7 +914,7 @@ void gemm_kernel(const GemmArgs args) {
     constexpr int RPI = 64 / LPR;    // rows per store instruction
     const int rr = el / LPR, seg = el % LPR;
     const int n = n0 + wn * T::TN + 8 * seg;
-    const bool vec = args.d_vec && n + 7 < n_end;
+    const int vec = n + 7 < n_end ? args.d_vec : 0;
     // Walked with running pointers and not unrolled: precomputed addresses for
     // every row would not fit in registers alongside the next tile's state.
     const uint8_t* src = stg + rr * T::EPI_ROW;
@@ -925,8 +925,11 @@ void gemm_kernel(const GemmArgs args) {
       const int row = row0 + rr;
       const i32x4_t v = *(const i32x4_t*)(src + 16 * (seg ^ T::epi_swz(row)));
       if (row < rows_w) {
-        if (vec) {
+        if (vec == 2) {
           *(i32x4_t*)d = v;
+        } else if (vec == 1) {
+          *(i32x2_t*)d = (i32x2_t){v[0], v[1]};
+          *(i32x2_t*)(d + 4) = (i32x2_t){v[2], v[3]};
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e)

@@ -16,6 +16,9 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
+SENTINEL_BITS = 0x7FC1   # a bf16 NaN pattern no GEMM output has
+
+
 def _say(msg):
     print(f"[gpu-test] {msg}", flush=True)
 
@@ -32,20 +35,20 @@ def _u8(t):
 # runners
 # ---------------------------------------------------------------------------
 
-def run_gpu(kind, t, K=None):
+def run_gpu(kind, t, K=None, out=None):
     """t: device tensors with unpacked uint8 scales; packs them on the GPU."""
     if kind == "bf16":
-        return bsg.gemm_bf16(t["A"], t["B"])
+        return bsg.gemm_bf16(t["A"], t["B"], out=out)
     M, N = t["A"].shape[0], t["B"].shape[0]
     if kind == "fp8":
         K = t["A"].shape[1]
         sfa = bsg.ensure_packed(t["sfa"], M, K // 128)
         sfb = bsg.ensure_packed(t["sfb"], (N + 127) // 128, K // 128)
-        return bsg.gemm_fp8_blockscaled(t["A"], sfa, t["B"], sfb)
+        return bsg.gemm_fp8_blockscaled(t["A"], sfa, t["B"], sfb, out=out)
     K = K if K is not None else 2 * t["A"].shape[1]
     sfa = bsg.ensure_packed(t["sfa"], M, K // 32)
     sfb = bsg.ensure_packed(t["sfb"], N, K // 32)
-    return bsg.gemm_fp4_blockscaled(t["A"], sfa, t["B"], sfb, K=K)
+    return bsg.gemm_fp4_blockscaled(t["A"], sfa, t["B"], sfb, K=K, out=out)
 
 
 def run_oracle(kind, h, K, rows=None, cols=None):
@@ -263,6 +266,25 @@ def test_k_zero_writes_zeros_and_empty_is_noop():
     assert torch.all(out[:, :20] == 0) and torch.all(out[:, 20:] == 3.0)
     E = torch.zeros(0, 64, dtype=torch.bfloat16, device=DEV)
     assert bsg.gemm_bf16(E, torch.zeros(8, 64, dtype=torch.bfloat16, device=DEV)).shape == (0, 8)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8", "fp4"])
+@pytest.mark.parametrize("col0,pad", [(0, 0), (0, 4), (4, 4), (2, 6), (1, 3)])
+def test_output_alignment_and_stride(kind, col0, pad):
+    """D written into a wider buffer at column col0 with leading dimension N + pad:
+    16-byte, 8-byte and 2-byte stores of the staged rows give the same bits as a
+    contiguous D, and nothing outside the window is written."""
+    _say(f"output window {kind} col0={col0} pad={pad}")
+    M, N, K = 300, 264, 512
+    w = workloads.dense(kind, M, N, K, 77, device=DEV)
+    ref = run_gpu(kind, w.tensors, K=K)
+    buf = torch.full((M, N + pad), SENTINEL_BITS, dtype=torch.int16, device=DEV)
+    out = buf.view(torch.bfloat16)[:, col0:col0 + N]
+    run_gpu(kind, w.tensors, K=K, out=out)
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy()
+    assert np.array_equal(got[:, col0:col0 + N], ref.view(torch.int16).cpu().numpy())
+    assert np.all(got[:, :col0] == SENTINEL_BITS) and np.all(got[:, col0 + N:] == SENTINEL_BITS)
 
 
 @pytest.mark.parametrize("kind", ["bf16", "fp8", "fp4"])
