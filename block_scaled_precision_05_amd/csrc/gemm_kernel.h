@@ -1,7 +1,7 @@
 // gemm_kernel.h -- gfx950 GEMM kernel template for D = A * B^T (NT layout), BF16,
 // FP8 e4m3 and FP4 e2m1 operands, fp32 accumulation on MFMA, bf16 output.
 //
-// Data path of one workgroup (WM x WN waves, one wave per SIMD):
+// Data path of one workgroup (WM x WN waves; four waves: one per SIMD, eight: two):
 //   HBM/L2 --buffer_load ... lds (16 B per lane, no VGPR round trip)--> LDS
 //   LDS (a ring of NS stages of SB bytes of K per tile row, XOR-swizzled) --ds_read_b128--> VGPRs
 //   VGPRs --v_mfma_f32_32x32x16_bf16 / v_mfma_scale_f32_32x32x64_f8f6f4--> fp32 accumulators
@@ -434,7 +434,8 @@ __device__ __forceinline__ void ring_barrier() {
 }
 
 template <int KIND, int BM, int BN, int WM, int WN, int SB, int NS, int PR, bool GROUPED, int SV = 0>
-__global__ __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(WM* WN * 64)
+__attribute__((amdgpu_waves_per_eu((WM * WN + 3) / 4, (WM * WN + 3) / 4)))
 void gemm_kernel(const GemmArgs args) {
   using T = GemmTile<KIND, BM, BN, WM, WN, SB, NS, PR, SV>;
   constexpr int FM = T::FM, FN = T::FN, J = T::J, RPF = T::RPF, NC = T::NC, SW = T::SW;
