@@ -178,6 +178,10 @@ struct GemmTile {
   // FP8 B scales: one 128-row block per wave when the wave's TN rows stay inside
   // one block, else one word per 32-row fragment.
   static constexpr bool ONE_B_SCALE = TN <= 128 && 128 % TN == 0 && BN % 128 == 0;
+  // A fragments double-buffered in registers (the next k-step's read beside the
+  // current MFMAs) unless two waves share a SIMD on the halved register budget:
+  // then the MFMAs come first and the other wave covers the read's latency.
+  static constexpr bool DBA = NW <= 4 || KIND == KIND_BF16;
   static constexpr int NSB = KIND == KIND_FP8 ? (ONE_B_SCALE ? 1 : FN) : FN;
   // packed scale words per lane per fragment per stage: FP8 one (the K-block's
   // pair), FP4 NC/4 (lane group lg takes NC/2 K-blocks of 32)
@@ -681,7 +685,7 @@ void gemm_kernel(const GemmArgs args) {
 
     // Fragment registers, double-buffered across k-steps.
     typedef typename std::conditional<KIND == KIND_BF16, bf16x8_t, i32x8_t>::type frag_t;
-    frag_t fa[2][FM], fb[2][FN];
+    frag_t fa[T::DBA ? 2 : 1][FM], fb[2][FN];
     auto read_frags = [&](int buf, int j, frag_t (&xa)[FM], frag_t (&xb)[FN]) {
       const uint8_t* base = smem + buf * T::STAGE_BYTES;
 #pragma unroll
@@ -815,10 +819,17 @@ void gemm_kernel(const GemmArgs args) {
         // fragment register set of this k-step: k-steps alternate sets across
         // stage boundaries too (a round has an even number of them)
         constexpr int cu = (si * J + j) & 1, nx = cu ^ 1;
+        constexpr int ca = T::DBA ? cu : 0, na = T::DBA ? nx : 0;
         if constexpr (j + 1 < J) {
-          read_frags(buf, j + 1, fa[nx], fb[nx]);
-          if constexpr (PR) pair_chunk(std::integral_constant<int, g>{}, round);
-          mfmas(jc, fa[cu], fb[cu], sa_cur, sb_cur);
+          if constexpr (T::DBA) {
+            read_frags(buf, j + 1, fa[na], fb[nx]);
+            if constexpr (PR) pair_chunk(std::integral_constant<int, g>{}, round);
+            mfmas(jc, fa[ca], fb[cu], sa_cur, sb_cur);
+          } else {
+            if constexpr (PR) pair_chunk(std::integral_constant<int, g>{}, round);
+            mfmas(jc, fa[ca], fb[cu], sa_cur, sb_cur);
+            read_frags(buf, j + 1, fa[na], fb[nx]);
+          }
           interleave<FM * FN, (FM + FN) * RPF, nvm>();
           __builtin_amdgcn_sched_barrier(0);
         } else {
@@ -834,8 +845,13 @@ void gemm_kernel(const GemmArgs args) {
             load_scales(s + NS < nk ? s + NS : 0, std::integral_constant<int, buf>{});
             issue_stage(s + NS, buf);
           }
-          read_frags(nbuf, 0, fa[nx], fb[nx]);
-          mfmas(jc, fa[cu], fb[cu], sa_cur, sb_cur);
+          if constexpr (T::DBA) {
+            read_frags(nbuf, 0, fa[na], fb[nx]);
+            mfmas(jc, fa[ca], fb[cu], sa_cur, sb_cur);
+          } else {
+            mfmas(jc, fa[ca], fb[cu], sa_cur, sb_cur);
+            read_frags(nbuf, 0, fa[na], fb[nx]);
+          }
           interleave<FM * FN, (FM + FN) * RPF, nvm>();
           __builtin_amdgcn_sched_barrier(0);
           // (shared scales: stage s+1 reads the set of its pair's first stage)
