@@ -2,22 +2,21 @@
 // gemm_kernel: BM, BN, WM, WN, SB, NS, PR).
 #pragma once
 
-// Dense FP4: 256x256 workgroup tile, 2x2 waves of 128x128 (16 fragments of 32x32 per
-// wave, 256 fp32 accumulators per lane), a ring of five 64-byte stages (32 KiB
-// each) copied in pairs.  The copies are limited by the requests a CU keeps in
-// flight and by the issue cost of the copy instructions (spread over the MFMAs);
-// the MFMAs by the chip's power limit.  256x224 tiles (exactly two per CU at
-// 4096x7168) measured no faster: with the chip power-bound, the CUs left idle in
-// the last wave of 256x256 tiles let the others clock higher.
-#define BSG_FP4_CFG 256, 256, 2, 2, 64, 5, 1
-// BF16 and FP8: the same tile over eight waves (2x4 of 128x64, two per SIMD):
-// while one wave of a SIMD waits on a copy or an LDS read, the other issues
-// MFMAs.  The fragments fit the halved register budget (FP8 with its A fragments
-// single-buffered); FP4's row permutation needs 128x128 wave blocks, so FP4 stays
-// on four waves.  Alternating A/B, 8 against 4 waves: BF16 4096x7168x16384 717-719
-// against 734-741 us, grouped BF16 MoE shape 3430 against 3471 us; FP8
-// 4096x7168x16384 385 against 403 us, grouped FP8 MoE shape 1932 against 1957 us,
-// FFN down-projection 919 against 1007 us.
+// Dense: 256x256 workgroup tile over eight waves, 2x4 of 128x64 (8 fragments of
+// 32x32 per wave, 128 fp32 accumulators per lane), two waves per SIMD: while one
+// wave of a SIMD waits on a copy or an LDS read, the other issues MFMAs.  A ring
+// of five 64-byte stages (32 KiB each) copied in pairs.  The fragments fit the
+// halved register budget (FP8 and FP4 with their A fragments single-buffered; FP4
+// permutes B rows in 64-row blocks).  Alternating A/B, 8 against 4 waves of
+// 128x128: BF16 4096x7168x16384 717-719 against 734-741 us, FP8 385 against
+// 403 us, FP4 219-222 against 222-226 us; grouped BF16 MoE shape 3430 against
+// 3471 us, grouped FP8 1932 against 1957 us, FFN down-projection 919 against
+// 1007 us.  The copies are limited by the requests a CU keeps in flight and by
+// the issue cost of the copy instructions (spread over the MFMAs); the MFMAs by
+// the chip's power limit.  256x224 tiles (exactly two per CU at 4096x7168)
+// measured no faster: with the chip power-bound, the CUs left idle in the last
+// wave of 256x256 tiles let the others clock higher.
+#define BSG_FP4_CFG 256, 256, 2, 4, 64, 5, 1
 #define BSG_BF16_CFG 256, 256, 2, 4, 64, 5, 1
 #define BSG_FP8_CFG 256, 256, 2, 4, 64, 5, 1
 // Grouped: the dense FP8 tile and waves.  128x512 tiles (1x4 waves) waste no rows on
@@ -27,7 +26,7 @@
 #define BSG_GROUPED_CFG 256, 256, 2, 4, 64, 5, 1
 // Grouped BF16 and FP4: the dense tiles of their kind.
 #define BSG_GROUPED_BF16_CFG 256, 256, 2, 4, 64, 5, 1
-#define BSG_GROUPED_FP4_CFG 256, 256, 2, 2, 64, 5, 1
+#define BSG_GROUPED_FP4_CFG 256, 256, 2, 4, 64, 5, 1
 // Masked (decode-sized experts, tens of rows each): 128-row tiles, 1x4 waves of
 // 128x128 over 512 columns, four 40 KiB stages; 256-row tiles would multiply
 // mostly empty rows (measured 419 us against 340 us on the decode case).

@@ -31,9 +31,9 @@
 // 128-K block): the two 64-byte stages of a pair lie in one K-block and share
 // its scale word.  FP4 uses one byte per (row, 32-K block): each lane's 16-byte
 // operand is exactly one K-block and carries that block's byte.  Operands with a
-// scale per row permute the rows of each 128-row wave block (GemmTile::PERM_A,
-// PERM_B) so that a lane's four fragment rows, and their packed scale words, are
-// adjacent: one 8-byte load fetches all four.  Scale words are loaded together
+// scale per row permute the rows of each wave block (GemmTile::PERM_A, PERM_B)
+// so that a lane's fragment rows (four, or two for a 64-column B block), and
+// their packed scale words, are adjacent: one 8-byte (4-byte) load fetches them.  Scale words are loaded together
 // with the tile copy of their stage and only decoded after the barrier that
 // waits for that copy, so they never add a wait.
 #pragma once
@@ -187,25 +187,27 @@ struct GemmTile {
   // pair), FP4 NC/4 (lane group lg takes NC/2 K-blocks of 32)
   static constexpr int SW = KIND == KIND_BF16 ? 0 : (KIND == KIND_FP8 ? 1 : NC / 4);
   // Operands with one scale per row (A for FP8 and FP4, B for FP4) permute the
-  // rows of every 128-row wave block: LDS slot 32f + i (fragment f, lane row i)
-  // holds tile row 4i + f.  A lane's four fragment rows are then adjacent in
-  // memory, and so are their packed scale words: SV = 1 fetches them with one
-  // 8-byte load per operand (the packed arrays must be 8-byte aligned, with
-  // leading dimensions that are multiples of 4), SV = 0 with four 2-byte loads.
+  // rows of every wave block of n fragments (n = 4 for A; n = FN, 4 or 2, for
+  // B): LDS slot 32f + i (fragment f, lane row i) holds block row n*i + f.  A
+  // lane's n fragment rows are then adjacent in memory, and so are their packed
+  // scale words: SV = 1 fetches them with one 8-byte (n = 4) or 4-byte (n = 2)
+  // load per operand (the packed arrays must be 8-byte aligned, with leading
+  // dimensions that are multiples of 4), SV = 0 with n 2-byte loads.
   static constexpr bool PERM_A = KIND != KIND_BF16;
   static constexpr bool PERM_B = KIND == KIND_FP4;
   static constexpr bool PERM = PERM_B;   // FP4: both operands
   static_assert(!PERM_A || (FM == 4 && SW == 1),
                 "the row permutation needs 128-row wave blocks and one scale word per stage");
-  static_assert(!PERM_B || FN == 4, "the row permutation needs 128-row wave blocks");
-  static constexpr int perm_rows(bool on, int x) {
-    return on ? ((x & ~127) | ((x & 31) << 2) | ((x >> 5) & 3)) : x;
+  static_assert(!PERM_B || FN == 4 || FN == 2, "the B row permutation needs 128- or 64-row wave blocks");
+  // slot x -> row within blocks of 32n rows (n a power of two; n = 1: identity)
+  static constexpr int perm_rows(int n, int x) {
+    return n > 1 ? ((x & ~(32 * n - 1)) | ((x & 31) * n) | ((x >> 5) & (n - 1))) : x;
   }
-  static constexpr int perm_a(int x) { return perm_rows(PERM_A, x); }
+  static constexpr int perm_a(int x) { return perm_rows(PERM_A ? 4 : 1, x); }
   static constexpr int epi_swz(int row) {
     return (PERM_A ? (row >> 2) : row) & (EPI_CHUNKS - 1);
   }
-  static constexpr int perm_b(int x) { return perm_rows(PERM_B, x); }
+  static constexpr int perm_b(int x) { return perm_rows(PERM_B ? FN : 1, x); }
   static constexpr int NSC = SV ? (1 + (PERM_B ? 1 : NSB)) * SW : (FM + NSB) * SW;
   static constexpr int VMEM_PER_STAGE = N_DMA + NSC;
   static_assert(SB == 64 || SB == 128, "a stage is 64 or 128 bytes of K per row");
@@ -598,7 +600,7 @@ void gemm_kernel(const GemmArgs args) {
     uint32_t sa_voff = 2u * (uint32_t)(m0 + wm * T::TM + (T::PERM_A ? 4 * l32 : l32));
     asm volatile("" : "+v"(sa_voff));
     uint32_t sb_voff = KIND == KIND_FP8 ? 2u * (uint32_t)((n0 + wn * T::TN) / 128)
-                                        : 2u * (uint32_t)(n0 + wn * T::TN + (T::PERM_B ? 4 * l32 : l32));
+                                        : 2u * (uint32_t)(n0 + wn * T::TN + (T::PERM_B ? FN * l32 : l32));
     asm volatile("" : "+v"(sb_voff));
     // Raw scale words of stage kt (packed int16, not decoded yet).
     //   FP8: K-block kt*SB/128, held in packed row kb/2, byte kb%2.
@@ -630,10 +632,12 @@ void gemm_kernel(const GemmArgs args) {
             for (int f = 0; f < FM; ++f)
               rs_a[sl][f][w] = __builtin_amdgcn_raw_buffer_load_b16(rsa, va + fstep_a * f, 0, 0);
           }
-          if constexpr (SV && T::PERM_B) {
+          if constexpr (SV && T::PERM_B && FN == 4) {
             const u32x2_t db = __builtin_amdgcn_raw_buffer_load_b64(rsb, vb, 0, 0);
             rv_b[sl][0] = db[0];
             rv_b[sl][1] = db[1];
+          } else if constexpr (SV && T::PERM_B) {
+            rv_b[sl][0] = __builtin_amdgcn_raw_buffer_load_b32(rsb, vb, 0, 0);
           } else {
 #pragma unroll
             for (int f = 0; f < NSB; ++f) {
@@ -672,11 +676,13 @@ void gemm_kernel(const GemmArgs args) {
           sa[0] = rv_a[sl][0];
           sa[1] = rv_a[sl][1];
           sb[0] = rv_b[sl][0];
-          sb[1] = rv_b[sl][1];
+          if constexpr (FN > 2) sb[1] = rv_b[sl][1];
         } else {
 #pragma unroll
-          for (int i = 0; i < 2; ++i) {
+          for (int i = 0; i < 2; ++i)
             sa[i] = (uint32_t)rs_a[sl][2 * i][0] | ((uint32_t)rs_a[sl][2 * i + 1][0] << 16);
+#pragma unroll
+          for (int i = 0; i < FN / 2; ++i) {
             sb[i] = (uint32_t)rs_b[sl][2 * i][0] | ((uint32_t)rs_b[sl][2 * i + 1][0] << 16);
           }
         }
@@ -873,8 +879,8 @@ void gemm_kernel(const GemmArgs args) {
     // register r of lane l holds D[m][n] with m = l%32 and
     // n = 8*(r/4) + 4*(l/32) + r%4: four consecutive columns per register quad.
     // Permuted rows: fragment a's row l32 is tile row 4*l32 + a; with B permuted
-    // too (FP4), fragment b's column i is tile column 4*i + b, so the four
-    // fragments b hold four consecutive columns in the same register.
+    // too (FP4), fragment b's column i is tile column FN*i + b, so the FN
+    // fragments b hold FN consecutive columns in the same register.
     //
     // Stored straight from those registers, every store instruction would put 16
     // bytes into each of 32 rows, one L2 request per 16 bytes.  Instead each wave
@@ -908,11 +914,20 @@ void gemm_kernel(const GemmArgs args) {
 #pragma unroll
     for (int a = 0; a < FM; ++a) {
       const int row = T::PERM_A ? 4 * el32 + a : 32 * a + el32;
-      if constexpr (T::PERM) {
+      if constexpr (T::PERM && FN == 4) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           stage_quad(row, 4 * (8 * (r / 4) + 4 * elg + r % 4), acc[a][0][r], acc[a][1][r], acc[a][2][r],
                      acc[a][3][r]);
+      } else if constexpr (T::PERM) {
+        // two B fragments: the same register of both holds two consecutive columns
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int col = 2 * (8 * (r / 4) + 4 * elg + r % 4);
+          const int chunk = (col >> 3) ^ T::epi_swz(row);
+          *(uint32_t*)(stg + row * T::EPI_ROW + 16 * chunk + 2 * (col & 7)) =
+              pack_bf16x2(acc[a][0][r], acc[a][1][r]);
+        }
       } else {
 #pragma unroll
         for (int b = 0; b < FN; ++b)
