@@ -522,454 +522,475 @@ void gemm_kernel(const GemmArgs args) {
     m0 = __builtin_amdgcn_readfirstlane(m0);
     m_end = __builtin_amdgcn_readfirstlane(m_end);
     n0 = __builtin_amdgcn_readfirstlane(n0);
-    const int n_end = n0 + BN < args.N ? n0 + BN : args.N;
-    const int rows_a = m_end - m0, rows_b = n_end - n0;
 
-    // Buffer resources cover exactly the bytes of this tile's rows: rows past the
-    // end of the matrix (or of the expert) read as zero.
-    const __amdgpu_buffer_rsrc_t ra =
-        make_rsrc(args.A + (int64_t)m0 * args.lda, (uint32_t)((rows_a - 1) * args.lda + args.k_bytes));
-    const __amdgpu_buffer_rsrc_t rb =
-        make_rsrc(Bbase + (int64_t)n0 * args.ldb, (uint32_t)((rows_b - 1) * args.ldb + args.k_bytes));
-    // Copy q of a wave fills LDS rows (slots) (q*NW + wave) * ROWS_PER_COPY + cp_row
-    // from tile row perm(slot); the lane part and the q part of the slot occupy
-    // disjoint bits, so perm splits into a per-lane row and a per-q row.
-    uint32_t a_vbase = (uint32_t)(T::perm_a(T::ROWS_PER_COPY * wave + cp_row) * args.lda) + cp_c16;
-    uint32_t b_vbase = (uint32_t)(T::perm_b(T::ROWS_PER_COPY * wave + cp_row) * args.ldb) + cp_c16;
-    // Opaque per tile: otherwise the compiler hoists every copy offset of the
-    // prologue out of the tile loop and spills them all.
-    asm volatile("" : "+v"(a_vbase), "+v"(b_vbase));
+    // Waves whose rows all lie past the edge (the lower row of waves on an
+    // expert's last row tile when it holds at most BM/2 rows) run the tile without
+    // MFMAs, fragment reads or stores: they still issue their share of the copies
+    // and scale loads and meet every barrier, so the workgroup's schedule and the
+    // vmcnt arithmetic are unchanged, and the SIMD they share with a computing
+    // wave is left to it.
+    auto tile_body = [&](auto mm_c) __attribute__((always_inline)) {
+      constexpr bool MM = decltype(mm_c)::value;
+      const int n_end = n0 + BN < args.N ? n0 + BN : args.N;
+      const int rows_a = m_end - m0, rows_b = n_end - n0;
 
-    // Copy q of stage kt into LDS buffer `buf` (A copies first, then B); a stage
-    // past the end copies nothing (every lane's offset is out of range, so no
-    // memory is read).
-    auto copy_one = [&](int kt, int buf, int q) {
-      uint8_t* sA = smem + buf * T::STAGE_BYTES;
-      uint8_t* sB = sA + BM * SB;
-      const int kb = kt * SB;
-      const int k_lim = kt < nk ? args.k_bytes : 0;
-      // past the K extent the offset gets bit 31, which no record count reaches
-      const uint32_t oob = kb + cp_c16 < k_lim ? 0u : kOOB;
-      uint8_t* const spare = smem + NS * T::STAGE_BYTES;
-      if (q < T::A_LOADS) {
-        const int ci = q * T::NW + wave;
-        const bool dummy = T::DUMMY && ci >= T::A_COPIES;
-        const uint32_t qrow = (uint32_t)T::perm_a(q * T::NW * T::ROWS_PER_COPY);
-        const uint32_t off = (a_vbase + qrow * (uint32_t)args.lda + kb) | oob | (dummy ? kOOB : 0u);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ra, (__attribute__((address_space(3))) void*)(dummy ? spare : sA + T::ROWS_PER_COPY * ci * SB),
-            16, off, 0, 0, 0);
-      } else {
-        const int qb = q - T::A_LOADS;
-        const int ci = qb * T::NW + wave;
-        const bool dummy = T::DUMMY && ci >= T::B_COPIES;
-        const uint32_t qrow = (uint32_t)T::perm_b(qb * T::NW * T::ROWS_PER_COPY);
-        const uint32_t off = (b_vbase + qrow * (uint32_t)args.ldb + kb) | oob | (dummy ? kOOB : 0u);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rb, (__attribute__((address_space(3))) void*)(dummy ? spare : sB + T::ROWS_PER_COPY * ci * SB),
-            16, off, 0, 0, 0);
-      }
-    };
-    auto issue_stage = [&](int kt, int buf) {
-#pragma unroll
-      for (int q = 0; q < T::N_DMA; ++q) copy_one(kt, buf, q);
-    };
-    // Chunk c of pair (kt, kt+1): copies c*QPC .. (c+1)*QPC-1 of both stages, the
-    // two halves of every line back to back.
-    auto issue_chunk = [&](int kt, int buf0, int buf1, int c) {
-#pragma unroll
-      for (int q = 0; q < T::QPC; ++q) {
-        copy_one(kt, buf0, c * T::QPC + q);
-        copy_one(kt + 1, buf1, c * T::QPC + q);
-      }
-    };
+      // Buffer resources cover exactly the bytes of this tile's rows: rows past the
+      // end of the matrix (or of the expert) read as zero.
+      const __amdgpu_buffer_rsrc_t ra =
+          make_rsrc(args.A + (int64_t)m0 * args.lda, (uint32_t)((rows_a - 1) * args.lda + args.k_bytes));
+      const __amdgpu_buffer_rsrc_t rb =
+          make_rsrc(Bbase + (int64_t)n0 * args.ldb, (uint32_t)((rows_b - 1) * args.ldb + args.k_bytes));
+      // Copy q of a wave fills LDS rows (slots) (q*NW + wave) * ROWS_PER_COPY + cp_row
+      // from tile row perm(slot); the lane part and the q part of the slot occupy
+      // disjoint bits, so perm splits into a per-lane row and a per-q row.
+      uint32_t a_vbase = (uint32_t)(T::perm_a(T::ROWS_PER_COPY * wave + cp_row) * args.lda) + cp_c16;
+      uint32_t b_vbase = (uint32_t)(T::perm_b(T::ROWS_PER_COPY * wave + cp_row) * args.ldb) + cp_c16;
+      // Opaque per tile: otherwise the compiler hoists every copy offset of the
+      // prologue out of the tile loop and spills them all.
+      asm volatile("" : "+v"(a_vbase), "+v"(b_vbase));
 
-    // Scale loads.  Each lane reads the packed words of the rows it feeds to the
-    // MFMAs: A row m0 + wm*TM + 32f + l32 (f < FM), whose word sits 64f bytes after
-    // fragment 0's; for FP4 B row n likewise; for FP8 the 128-row block of B that
-    // holds the wave's rows (one block) or fragment f's 32 rows.  Rows past M or N
-    // read some other finite word or zero (out of range): they only meet zero
-    // operands and their outputs are never stored.
-    constexpr int NSB = T::NSB;   // B scale words per lane per packed row
-    const int nrow0 = n0 + wn * T::TN;   // first B row of this wave (uniform)
-    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(
-        args.sfa, (uint32_t)(2 * ((int64_t)(args.kp_count - 1) * args.ld_sfa + args.M)));
-    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(
-        sfb, (uint32_t)(2 * ((int64_t)(args.kp_count - 1) * args.ld_sfb + args.sfb_rows)));
-    // (FP4: the lane's fragment rows are 4*l32 .. 4*l32 + 3 of the wave block)
-    uint32_t sa_voff = 2u * (uint32_t)(m0 + wm * T::TM + (T::PERM_A ? 4 * l32 : l32));
-    asm volatile("" : "+v"(sa_voff));
-    uint32_t sb_voff = KIND == KIND_FP8 ? 2u * (uint32_t)((n0 + wn * T::TN) / 128)
-                                        : 2u * (uint32_t)(n0 + wn * T::TN + (T::PERM_B ? FN * l32 : l32));
-    asm volatile("" : "+v"(sb_voff));
-    // Raw scale words of stage kt (packed int16, not decoded yet).
-    //   FP8: K-block kt*SB/128, held in packed row kb/2, byte kb%2.
-    //   FP4: lane group lg needs K-blocks kt*NC + (NC/2)*lg + j (j < NC/2), the
-    //        packed rows kt*NC/2 + (NC/4)*lg + w for w < NC/4.
-    // Raw scale words, one register set per ring slot (the slot is a compile-time
-    // value at every call).  FP4 with SV: the two dwords of each operand's 8-byte
-    // load, fragments 2i and 2i+1 in the low and high halves of dword i.
-    uint16_t rs_a[NS][FM][SW > 0 ? SW : 1] = {}, rs_b[NS][NSB][SW > 0 ? SW : 1] = {};
-    uint32_t rv_a[SV ? NS : 1][2] = {}, rv_b[SV ? NS : 1][2] = {};
-    auto load_scales = [&](int kt, auto slot) {
-      constexpr int sl = decltype(slot)::value;
-      if constexpr (KIND != KIND_BF16) {
+      // Copy q of stage kt into LDS buffer `buf` (A copies first, then B); a stage
+      // past the end copies nothing (every lane's offset is out of range, so no
+      // memory is read).
+      auto copy_one = [&](int kt, int buf, int q) {
+        uint8_t* sA = smem + buf * T::STAGE_BYTES;
+        uint8_t* sB = sA + BM * SB;
+        const int kb = kt * SB;
+        const int k_lim = kt < nk ? args.k_bytes : 0;
+        // past the K extent the offset gets bit 31, which no record count reaches
+        const uint32_t oob = kb + cp_c16 < k_lim ? 0u : kOOB;
+        uint8_t* const spare = smem + NS * T::STAGE_BYTES;
+        if (q < T::A_LOADS) {
+          const int ci = q * T::NW + wave;
+          const bool dummy = T::DUMMY && ci >= T::A_COPIES;
+          const uint32_t qrow = (uint32_t)T::perm_a(q * T::NW * T::ROWS_PER_COPY);
+          const uint32_t off = (a_vbase + qrow * (uint32_t)args.lda + kb) | oob | (dummy ? kOOB : 0u);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              ra, (__attribute__((address_space(3))) void*)(dummy ? spare : sA + T::ROWS_PER_COPY * ci * SB),
+              16, off, 0, 0, 0);
+        } else {
+          const int qb = q - T::A_LOADS;
+          const int ci = qb * T::NW + wave;
+          const bool dummy = T::DUMMY && ci >= T::B_COPIES;
+          const uint32_t qrow = (uint32_t)T::perm_b(qb * T::NW * T::ROWS_PER_COPY);
+          const uint32_t off = (b_vbase + qrow * (uint32_t)args.ldb + kb) | oob | (dummy ? kOOB : 0u);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rb, (__attribute__((address_space(3))) void*)(dummy ? spare : sB + T::ROWS_PER_COPY * ci * SB),
+              16, off, 0, 0, 0);
+        }
+      };
+      auto issue_stage = [&](int kt, int buf) {
 #pragma unroll
-        for (int w = 0; w < SW; ++w) {
-          int kp = KIND == KIND_FP8 ? (kt * SB / 128) >> 1 : kt * (NC / 2) + (NC / 4) * lg + w;
-          kp = kp < args.kp_count ? kp : args.kp_count - 1;
-          const uint32_t va = sa_voff + 2u * (uint32_t)(kp * args.ld_sfa);
-          const uint32_t vb = sb_voff + 2u * (uint32_t)(kp * args.ld_sfb);
-          // fragment f's word: 2 bytes further on (permuted rows: adjacent) or
-          // 64 bytes (32 rows) further on
-          constexpr uint32_t fstep_a = T::PERM_A ? 2 : 64, fstep_b = T::PERM_B ? 2 : 64;
-          if constexpr (SV) {
-            const u32x2_t da = __builtin_amdgcn_raw_buffer_load_b64(rsa, va, 0, 0);
-            rv_a[sl][0] = da[0];
-            rv_a[sl][1] = da[1];
-          } else {
+        for (int q = 0; q < T::N_DMA; ++q) copy_one(kt, buf, q);
+      };
+      // Chunk c of pair (kt, kt+1): copies c*QPC .. (c+1)*QPC-1 of both stages, the
+      // two halves of every line back to back.
+      auto issue_chunk = [&](int kt, int buf0, int buf1, int c) {
 #pragma unroll
-            for (int f = 0; f < FM; ++f)
-              rs_a[sl][f][w] = __builtin_amdgcn_raw_buffer_load_b16(rsa, va + fstep_a * f, 0, 0);
-          }
-          if constexpr (SV && T::PERM_B && FN == 4) {
-            const u32x2_t db = __builtin_amdgcn_raw_buffer_load_b64(rsb, vb, 0, 0);
-            rv_b[sl][0] = db[0];
-            rv_b[sl][1] = db[1];
-          } else if constexpr (SV && T::PERM_B) {
-            rv_b[sl][0] = __builtin_amdgcn_raw_buffer_load_b32(rsb, vb, 0, 0);
-          } else {
+        for (int q = 0; q < T::QPC; ++q) {
+          copy_one(kt, buf0, c * T::QPC + q);
+          copy_one(kt + 1, buf1, c * T::QPC + q);
+        }
+      };
+
+      // Scale loads.  Each lane reads the packed words of the rows it feeds to the
+      // MFMAs: A row m0 + wm*TM + 32f + l32 (f < FM), whose word sits 64f bytes after
+      // fragment 0's; for FP4 B row n likewise; for FP8 the 128-row block of B that
+      // holds the wave's rows (one block) or fragment f's 32 rows.  Rows past M or N
+      // read some other finite word or zero (out of range): they only meet zero
+      // operands and their outputs are never stored.
+      constexpr int NSB = T::NSB;   // B scale words per lane per packed row
+      const int nrow0 = n0 + wn * T::TN;   // first B row of this wave (uniform)
+      const __amdgpu_buffer_rsrc_t rsa = make_rsrc(
+          args.sfa, (uint32_t)(2 * ((int64_t)(args.kp_count - 1) * args.ld_sfa + args.M)));
+      const __amdgpu_buffer_rsrc_t rsb = make_rsrc(
+          sfb, (uint32_t)(2 * ((int64_t)(args.kp_count - 1) * args.ld_sfb + args.sfb_rows)));
+      // (FP4: the lane's fragment rows are 4*l32 .. 4*l32 + 3 of the wave block)
+      uint32_t sa_voff = 2u * (uint32_t)(m0 + wm * T::TM + (T::PERM_A ? 4 * l32 : l32));
+      asm volatile("" : "+v"(sa_voff));
+      uint32_t sb_voff = KIND == KIND_FP8 ? 2u * (uint32_t)((n0 + wn * T::TN) / 128)
+                                          : 2u * (uint32_t)(n0 + wn * T::TN + (T::PERM_B ? FN * l32 : l32));
+      asm volatile("" : "+v"(sb_voff));
+      // Raw scale words of stage kt (packed int16, not decoded yet).
+      //   FP8: K-block kt*SB/128, held in packed row kb/2, byte kb%2.
+      //   FP4: lane group lg needs K-blocks kt*NC + (NC/2)*lg + j (j < NC/2), the
+      //        packed rows kt*NC/2 + (NC/4)*lg + w for w < NC/4.
+      // Raw scale words, one register set per ring slot (the slot is a compile-time
+      // value at every call).  FP4 with SV: the two dwords of each operand's 8-byte
+      // load, fragments 2i and 2i+1 in the low and high halves of dword i.
+      uint16_t rs_a[NS][FM][SW > 0 ? SW : 1] = {}, rs_b[NS][NSB][SW > 0 ? SW : 1] = {};
+      uint32_t rv_a[SV ? NS : 1][2] = {}, rv_b[SV ? NS : 1][2] = {};
+      auto load_scales = [&](int kt, auto slot) {
+        constexpr int sl = decltype(slot)::value;
+        if constexpr (KIND != KIND_BF16) {
 #pragma unroll
-            for (int f = 0; f < NSB; ++f) {
-              if constexpr (KIND == KIND_FP8 && !T::ONE_B_SCALE)
-                rs_b[sl][f][w] = __builtin_amdgcn_raw_buffer_load_b16(
-                    rsb, 2u * (uint32_t)(((nrow0 + 32 * f) >> 7) + kp * args.ld_sfb), 0, 0);
-              else
-                rs_b[sl][f][w] = __builtin_amdgcn_raw_buffer_load_b16(rsb, vb + fstep_b * f, 0, 0);
+          for (int w = 0; w < SW; ++w) {
+            int kp = KIND == KIND_FP8 ? (kt * SB / 128) >> 1 : kt * (NC / 2) + (NC / 4) * lg + w;
+            kp = kp < args.kp_count ? kp : args.kp_count - 1;
+            const uint32_t va = sa_voff + 2u * (uint32_t)(kp * args.ld_sfa);
+            const uint32_t vb = sb_voff + 2u * (uint32_t)(kp * args.ld_sfb);
+            // fragment f's word: 2 bytes further on (permuted rows: adjacent) or
+            // 64 bytes (32 rows) further on
+            constexpr uint32_t fstep_a = T::PERM_A ? 2 : 64, fstep_b = T::PERM_B ? 2 : 64;
+            if constexpr (SV) {
+              const u32x2_t da = __builtin_amdgcn_raw_buffer_load_b64(rsa, va, 0, 0);
+              rv_a[sl][0] = da[0];
+              rv_a[sl][1] = da[1];
+            } else {
+#pragma unroll
+              for (int f = 0; f < FM; ++f)
+                rs_a[sl][f][w] = __builtin_amdgcn_raw_buffer_load_b16(rsa, va + fstep_a * f, 0, 0);
+            }
+            if constexpr (SV && T::PERM_B && FN == 4) {
+              const u32x2_t db = __builtin_amdgcn_raw_buffer_load_b64(rsb, vb, 0, 0);
+              rv_b[sl][0] = db[0];
+              rv_b[sl][1] = db[1];
+            } else if constexpr (SV && T::PERM_B) {
+              rv_b[sl][0] = __builtin_amdgcn_raw_buffer_load_b32(rsb, vb, 0, 0);
+            } else {
+#pragma unroll
+              for (int f = 0; f < NSB; ++f) {
+                if constexpr (KIND == KIND_FP8 && !T::ONE_B_SCALE)
+                  rs_b[sl][f][w] = __builtin_amdgcn_raw_buffer_load_b16(
+                      rsb, 2u * (uint32_t)(((nrow0 + 32 * f) >> 7) + kp * args.ld_sfb), 0, 0);
+                else
+                  rs_b[sl][f][w] = __builtin_amdgcn_raw_buffer_load_b16(rsb, vb + fstep_b * f, 0, 0);
+              }
             }
           }
         }
-      }
-    };
-    // Decoded per-lane scale operand of stage kt.  FP8: the K-block's byte in
-    // bits 0..7.  FP4 (permuted rows): dword i holds fragment 2i's word in its low
-    // half and fragment 2i+1's in its high half; k-step j of fragment f uses byte
-    // 2*(f%2) + j of dword f/2, picked by the MFMA's byte select.  (The raw words
-    // stay untouched until here, so nothing uses a load's result before the
-    // barrier that waits for it.)
-    auto decode_scales = [&](int kt, auto slot, uint32_t (&sa)[FM], uint32_t (&sb)[FN]) {
-      constexpr int sl = decltype(slot)::value;
-      if constexpr (KIND == KIND_FP8) {
-        const int sh = ((kt * SB / 128) & 1) * 8;
-        if constexpr (SV) {
-          // the K-block's byte of fragments 2i and 2i+1 moves to bytes 0 and 2
-          sa[0] = rv_a[sl][0] >> sh;
-          sa[1] = rv_a[sl][1] >> sh;
-        } else {
-#pragma unroll
-          for (int f = 0; f < FM; ++f) sa[f] = ((uint32_t)rs_a[sl][f][0] >> sh) & 0xFF;
-        }
-#pragma unroll
-        for (int f = 0; f < FN; ++f) sb[f] = ((uint32_t)rs_b[sl][T::ONE_B_SCALE ? 0 : f][0] >> sh) & 0xFF;
-      } else if constexpr (KIND == KIND_FP4) {
-        if constexpr (SV) {
-          sa[0] = rv_a[sl][0];
-          sa[1] = rv_a[sl][1];
-          sb[0] = rv_b[sl][0];
-          if constexpr (FN > 2) sb[1] = rv_b[sl][1];
-        } else {
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-            sa[i] = (uint32_t)rs_a[sl][2 * i][0] | ((uint32_t)rs_a[sl][2 * i + 1][0] << 16);
-#pragma unroll
-          for (int i = 0; i < FN / 2; ++i) {
-            sb[i] = (uint32_t)rs_b[sl][2 * i][0] | ((uint32_t)rs_b[sl][2 * i + 1][0] << 16);
-          }
-        }
-      }
-    };
-
-    // Fragment registers, double-buffered across k-steps.
-    typedef typename std::conditional<KIND == KIND_BF16, bf16x8_t, i32x8_t>::type frag_t;
-    frag_t fa[T::DBA ? 2 : 1][FM], fb[2][FN];
-    auto read_frags = [&](int buf, int j, frag_t (&xa)[FM], frag_t (&xb)[FN]) {
-      const uint8_t* base = smem + buf * T::STAGE_BYTES;
-#pragma unroll
-      for (int f = 0; f < FM; ++f) {
-        const uint8_t* p0 = base + a_rd[j][0] + 32 * SB * f;
-        if constexpr (KIND == KIND_BF16) {
-          xa[f] = *(const bf16x8_t*)p0;
-        } else if constexpr (KIND == KIND_FP8) {
-          const i32x4_t lo = *(const i32x4_t*)p0;
-          const i32x4_t hi = *(const i32x4_t*)(base + a_rd[j][RPF - 1] + 32 * SB * f);
-          xa[f] = (i32x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        } else {
-          const i32x4_t v = *(const i32x4_t*)p0;
-          xa[f] = (i32x8_t){v[0], v[1], v[2], v[3], 0, 0, 0, 0};
-        }
-      }
-#pragma unroll
-      for (int f = 0; f < FN; ++f) {
-        const uint8_t* p0 = base + b_rd[j][0] + 32 * SB * f;
-        if constexpr (KIND == KIND_BF16) {
-          xb[f] = *(const bf16x8_t*)p0;
-        } else if constexpr (KIND == KIND_FP8) {
-          const i32x4_t lo = *(const i32x4_t*)p0;
-          const i32x4_t hi = *(const i32x4_t*)(base + b_rd[j][RPF - 1] + 32 * SB * f);
-          xb[f] = (i32x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        } else {
-          const i32x4_t v = *(const i32x4_t*)p0;
-          xb[f] = (i32x8_t){v[0], v[1], v[2], v[3], 0, 0, 0, 0};
-        }
-      }
-    };
-
-    f32x16_t acc[FM][FN];
-#pragma unroll
-    for (int a = 0; a < FM; ++a)
-#pragma unroll
-      for (int b = 0; b < FN; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
-
-    // One k-step's MFMAs: acc += A_frag x B_frag for every fragment pair.
-    auto mfmas = [&](auto jc, const frag_t (&xa)[FM], const frag_t (&xb)[FN], const uint32_t (&sa)[FM],
-                     const uint32_t (&sb)[FN]) {
-      constexpr int j = decltype(jc)::value;
-      if constexpr (KIND == KIND_FP8 && SV) {
-        // A fragment f's scale: byte 2*(f%2) of dword f/2 (decoded per K-block)
-        [&]<int... ab>(std::integer_sequence<int, ab...>) {
-          ((acc[ab / FN][ab % FN] = mfma_scaled2<0, 0, 2 * ((ab / FN) % 2)>(
-                xb[ab % FN], xa[ab / FN], acc[ab / FN][ab % FN], sb[ab % FN], sa[(ab / FN) / 2])),
-           ...);
-        }(std::make_integer_sequence<int, FM * FN>{});
-      } else if constexpr (T::PERM) {
-        // a-outer, b-inner as below; fragment f's scale is byte 2*(f%2) + j of
-        // dword f/2
-        [&]<int... ab>(std::integer_sequence<int, ab...>) {
-          ((acc[ab / FN][ab % FN] = mfma_scaled2<4, 2 * ((ab % FN) % 2) + j, 2 * ((ab / FN) % 2) + j>(
-                xb[ab % FN], xa[ab / FN], acc[ab / FN][ab % FN], sb[(ab % FN) / 2], sa[(ab / FN) / 2])),
-           ...);
-        }(std::make_integer_sequence<int, FM * FN>{});
-      } else {
-#pragma unroll
-        for (int a = 0; a < FM; ++a)
-#pragma unroll
-          for (int b = 0; b < FN; ++b) {
-            if constexpr (KIND == KIND_BF16)
-              acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb[b], xa[a], acc[a][b], 0, 0, 0);
-            else if constexpr (KIND == KIND_FP8)
-              acc[a][b] = mfma_scaled<0, 0>(xb[b], xa[a], acc[a][b], sb[b], sa[a]);
-            else
-              acc[a][b] = mfma_scaled<4, j>(xb[b], xa[a], acc[a][b], sb[b], sa[a]);
-          }
-      }
-    };
-
-    uint32_t sa_cur[FM] = {}, sb_cur[FN] = {};
-
-    // Prologue: the previous tile's LDS reads are over once every wave has
-    // drained its own and met the others here; then stages 0 .. T0-1 are put in
-    // flight and stage 0 is waited for.  The previous tile's D stores are not
-    // waited for (a __syncthreads would wait for every outstanding memory
-    // operation): their latency overlaps this tile's first copies, and since
-    // loads complete in order, the prologue's vmcnt wait below still covers
-    // stage 0 whatever the stores do.
-    wait_vm_lds<63>();
-    ring_barrier();
-    // Paired copies due at a k-step g: chunk chunk_at(g) of the pair started at
-    // the barrier of stage pair_start(g); chunk 0 also loads the first stage's
-    // scale words, chunk 1 the second's.
-    auto pair_chunk = [&](auto gc, int round) {
-      constexpr int g = decltype(gc)::value;
-      constexpr int c = T::chunk_at(g), tl = T::pair_start(g) + NS - 1;
-      constexpr int b0 = T::pmod(tl, NS), b1 = T::pmod(tl + 1, NS);
-      const int t = round + tl;
-      if constexpr (c == 0) load_scales(t < nk ? t : 0, std::integral_constant<int, b0>{});
-      if constexpr (c == 1 && !T::SHARED_SCALES)
-        load_scales(t + 1 < nk ? t + 1 : 0, std::integral_constant<int, b1>{});
-      issue_chunk(t, b0, b1, c);
-    };
-    if constexpr (PR) {
-      // every chunk due before k-step 0 (pairs with a first stage t >= 0)
-      [&]<int... gs>(std::integer_sequence<int, gs...>) {
-        ((T::pair_start(gs - (NS + 2) * J) + NS - 1 >= 0
-              ? pair_chunk(std::integral_constant<int, gs - (NS + 2) * J>{}, 0)
-              : void()),
-         ...);
-      }(std::make_integer_sequence<int, (NS + 2) * J>{});
-    } else {
-      [&]<int... bs>(std::integer_sequence<int, bs...>) {
-        ((load_scales(bs < nk ? bs : 0, std::integral_constant<int, bs>{}), issue_stage(bs, bs)), ...);
-      }(std::make_integer_sequence<int, NS>{});
-    }
-    wait_vm_lds<T::wait_prologue()>();
-    ring_barrier();
-    decode_scales(0, std::integral_constant<int, 0>{}, sa_cur, sb_cur);
-    read_frags(0, 0, fa[0], fb[0]);
-
-    // One stage.  Every stage runs the same code: after the last real one, the
-    // barrier, the copies (all out of range, so no memory traffic), the extra
-    // MFMAs on zero operands and the next-stage reads are dead work, which keeps
-    // the loop free of branches around the MFMAs.
-    auto stage = [&](auto ic, int s) {
-      constexpr int si = decltype(ic)::value;   // position of the stage in the round
-      constexpr int buf = si % NS;
-      constexpr int nbuf = (buf + 1) % NS;
-      static_assert(!PR || T::steady(si), "the copy schedule must repeat every round");
-      const int round = s - si;
-      auto body = [&](auto jc) {
-        constexpr int j = decltype(jc)::value;
-        constexpr int g = si * J + j;             // k-step index within the round
-        constexpr int nvm = PR ? T::chunk_vmem(g) : (j + 1 < J ? 0 : T::VMEM_PER_STAGE);
-        // fragment register set of this k-step: k-steps alternate sets across
-        // stage boundaries too (a round has an even number of them)
-        constexpr int cu = (si * J + j) & 1, nx = cu ^ 1;
-        constexpr int ca = T::DBA ? cu : 0, na = T::DBA ? nx : 0;
-        if constexpr (j + 1 < J) {
-          if constexpr (T::DBA) {
-            read_frags(buf, j + 1, fa[na], fb[nx]);
-            if constexpr (PR) pair_chunk(std::integral_constant<int, g>{}, round);
-            mfmas(jc, fa[ca], fb[cu], sa_cur, sb_cur);
+      };
+      // Decoded per-lane scale operand of stage kt.  FP8: the K-block's byte in
+      // bits 0..7.  FP4 (permuted rows): dword i holds fragment 2i's word in its low
+      // half and fragment 2i+1's in its high half; k-step j of fragment f uses byte
+      // 2*(f%2) + j of dword f/2, picked by the MFMA's byte select.  (The raw words
+      // stay untouched until here, so nothing uses a load's result before the
+      // barrier that waits for it.)
+      auto decode_scales = [&](int kt, auto slot, uint32_t (&sa)[FM], uint32_t (&sb)[FN]) {
+        if constexpr (!MM) return;
+        constexpr int sl = decltype(slot)::value;
+        if constexpr (KIND == KIND_FP8) {
+          const int sh = ((kt * SB / 128) & 1) * 8;
+          if constexpr (SV) {
+            // the K-block's byte of fragments 2i and 2i+1 moves to bytes 0 and 2
+            sa[0] = rv_a[sl][0] >> sh;
+            sa[1] = rv_a[sl][1] >> sh;
           } else {
-            if constexpr (PR) pair_chunk(std::integral_constant<int, g>{}, round);
-            mfmas(jc, fa[ca], fb[cu], sa_cur, sb_cur);
-            read_frags(buf, j + 1, fa[na], fb[nx]);
+#pragma unroll
+            for (int f = 0; f < FM; ++f) sa[f] = ((uint32_t)rs_a[sl][f][0] >> sh) & 0xFF;
           }
-          interleave<FM * FN, (FM + FN) * RPF, nvm>();
-          __builtin_amdgcn_sched_barrier(0);
-        } else {
-          // Stage s+1 has landed once no more than wait_at() of this wave's copies
-          // are outstanding and every wave has passed the barrier; every wave has
-          // also finished reading buffer `buf` (copies issued from here on go to
-          // the buffers of stages already consumed).
-          wait_vm_lds<T::wait_at(si)>();
-          ring_barrier();
-          if constexpr (PR) {
-            pair_chunk(std::integral_constant<int, g>{}, round);
+#pragma unroll
+          for (int f = 0; f < FN; ++f) sb[f] = ((uint32_t)rs_b[sl][T::ONE_B_SCALE ? 0 : f][0] >> sh) & 0xFF;
+        } else if constexpr (KIND == KIND_FP4) {
+          if constexpr (SV) {
+            sa[0] = rv_a[sl][0];
+            sa[1] = rv_a[sl][1];
+            sb[0] = rv_b[sl][0];
+            if constexpr (FN > 2) sb[1] = rv_b[sl][1];
           } else {
-            load_scales(s + NS < nk ? s + NS : 0, std::integral_constant<int, buf>{});
-            issue_stage(s + NS, buf);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+              sa[i] = (uint32_t)rs_a[sl][2 * i][0] | ((uint32_t)rs_a[sl][2 * i + 1][0] << 16);
+#pragma unroll
+            for (int i = 0; i < FN / 2; ++i) {
+              sb[i] = (uint32_t)rs_b[sl][2 * i][0] | ((uint32_t)rs_b[sl][2 * i + 1][0] << 16);
+            }
           }
-          if constexpr (T::DBA) {
-            read_frags(nbuf, 0, fa[na], fb[nx]);
-            mfmas(jc, fa[ca], fb[cu], sa_cur, sb_cur);
-          } else {
-            mfmas(jc, fa[ca], fb[cu], sa_cur, sb_cur);
-            read_frags(nbuf, 0, fa[na], fb[nx]);
-          }
-          interleave<FM * FN, (FM + FN) * RPF, nvm>();
-          __builtin_amdgcn_sched_barrier(0);
-          // (shared scales: stage s+1 reads the set of its pair's first stage)
-          constexpr int sbuf = T::SHARED_SCALES ? T::pmod(((si + 1) & ~1), NS) : nbuf;
-          decode_scales(s + 1, std::integral_constant<int, sbuf>{}, sa_cur, sb_cur);
         }
       };
-      [&]<int... js>(std::integer_sequence<int, js...>) {
-        (body(std::integral_constant<int, js>{}), ...);
-      }(std::make_integer_sequence<int, J>{});
-    };
-    for (int s = 0; s < nk_pad; s += T::U) {
-      [&]<int... is>(std::integer_sequence<int, is...>) {
-        (stage(std::integral_constant<int, is>{}, s + is), ...);
-      }(std::make_integer_sequence<int, T::U>{});
-    }
 
-    // Epilogue.  MFMA operands were (B fragment, A fragment), so accumulator
-    // register r of lane l holds D[m][n] with m = l%32 and
-    // n = 8*(r/4) + 4*(l/32) + r%4: four consecutive columns per register quad.
-    // Permuted rows: fragment a's row l32 is tile row 4*l32 + a; with B permuted
-    // too (FP4), fragment b's column i is tile column FN*i + b, so the FN
-    // fragments b hold FN consecutive columns in the same register.
-    //
-    // Stored straight from those registers, every store instruction would put 16
-    // bytes into each of 32 rows, one L2 request per 16 bytes.  Instead each wave
-    // converts its TM x TN block to bf16 into its own part of the idle LDS ring,
-    // row-major, then stores it row by row with 16 bytes per lane, so an
-    // instruction writes whole 2*TN-byte row segments.  The 16-byte chunks of a
-    // staged row are XOR-swizzled by the row (epi_swz) so that the 32 rows one
-    // write instruction touches spread over the banks.
-    //
-    // The ring is idle once no copy is in flight (the dead stages' out-of-range
-    // copies still write zeros into it) and every wave has passed the barrier.
-    wait_vm_lds<0>();
-    ring_barrier();
-    // rows of this wave's block that exist (an expert's last row tile, the
-    // matrix edge): a wave with none skips its part
-    const int rows_w = m_end - (m0 + wm * T::TM) < T::TM ? m_end - (m0 + wm * T::TM) : T::TM;
-    if (rows_w <= 0) continue;
-    uint8_t* const stg = smem + wave * T::EPI_WAVE_BYTES;
-    // The lane index, made opaque here: every staging address derives from it,
-    // and the compiler would otherwise hoist all of them out of the tile loop and
-    // spill them.
-    int el = lane;
-    asm volatile("" : "+v"(el));
-    const int el32 = el & 31, elg = el >> 5;
-    auto stage_quad = [&](int row, int col, float v0, float v1, float v2, float v3) {
-      // four consecutive columns col .. col+3 (col a multiple of 4) of `row`
-      const int chunk = (col >> 3) ^ T::epi_swz(row);
-      const i32x2_t w = {(int)pack_bf16x2(v0, v1), (int)pack_bf16x2(v2, v3)};
-      *(i32x2_t*)(stg + row * T::EPI_ROW + 16 * chunk + 2 * (col & 7)) = w;
-    };
+      // Fragment registers, double-buffered across k-steps.
+      typedef typename std::conditional<KIND == KIND_BF16, bf16x8_t, i32x8_t>::type frag_t;
+      frag_t fa[T::DBA ? 2 : 1][FM], fb[2][FN];
+      auto read_frags = [&](int buf, int j, frag_t (&xa)[FM], frag_t (&xb)[FN]) {
+        if constexpr (!MM) return;
+        const uint8_t* base = smem + buf * T::STAGE_BYTES;
 #pragma unroll
-    for (int a = 0; a < FM; ++a) {
-      const int row = T::PERM_A ? 4 * el32 + a : 32 * a + el32;
-      if constexpr (T::PERM && FN == 4) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          stage_quad(row, 4 * (8 * (r / 4) + 4 * elg + r % 4), acc[a][0][r], acc[a][1][r], acc[a][2][r],
-                     acc[a][3][r]);
-      } else if constexpr (T::PERM) {
-        // two B fragments: the same register of both holds two consecutive columns
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int col = 2 * (8 * (r / 4) + 4 * elg + r % 4);
-          const int chunk = (col >> 3) ^ T::epi_swz(row);
-          *(uint32_t*)(stg + row * T::EPI_ROW + 16 * chunk + 2 * (col & 7)) =
-              pack_bf16x2(acc[a][0][r], acc[a][1][r]);
+        for (int f = 0; f < FM; ++f) {
+          const uint8_t* p0 = base + a_rd[j][0] + 32 * SB * f;
+          if constexpr (KIND == KIND_BF16) {
+            xa[f] = *(const bf16x8_t*)p0;
+          } else if constexpr (KIND == KIND_FP8) {
+            const i32x4_t lo = *(const i32x4_t*)p0;
+            const i32x4_t hi = *(const i32x4_t*)(base + a_rd[j][RPF - 1] + 32 * SB * f);
+            xa[f] = (i32x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          } else {
+            const i32x4_t v = *(const i32x4_t*)p0;
+            xa[f] = (i32x8_t){v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+          }
         }
-      } else {
+#pragma unroll
+        for (int f = 0; f < FN; ++f) {
+          const uint8_t* p0 = base + b_rd[j][0] + 32 * SB * f;
+          if constexpr (KIND == KIND_BF16) {
+            xb[f] = *(const bf16x8_t*)p0;
+          } else if constexpr (KIND == KIND_FP8) {
+            const i32x4_t lo = *(const i32x4_t*)p0;
+            const i32x4_t hi = *(const i32x4_t*)(base + b_rd[j][RPF - 1] + 32 * SB * f);
+            xb[f] = (i32x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          } else {
+            const i32x4_t v = *(const i32x4_t*)p0;
+            xb[f] = (i32x8_t){v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+          }
+        }
+      };
+
+      f32x16_t acc[FM][FN];
+#pragma unroll
+      for (int a = 0; a < FM; ++a)
 #pragma unroll
         for (int b = 0; b < FN; ++b)
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            stage_quad(row, 32 * b + 8 * q + 4 * elg, acc[a][b][4 * q], acc[a][b][4 * q + 1],
-                       acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]);
-      }
-      // one fragment row at a time: the compiler would otherwise move every
-      // accumulator into VGPRs first and spill
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // (a wave reads back only what it wrote; its LDS accesses execute in order)
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    constexpr int LPR = T::TN / 8;   // lanes per staged row, 16 bytes each
-    constexpr int RPI = 64 / LPR;    // rows per store instruction
-    const int rr = el / LPR, seg = el % LPR;
-    const int n = n0 + wn * T::TN + 8 * seg;
-    const int vec = n + 7 < n_end ? args.d_vec : 0;
-    // Walked with running pointers and not unrolled: precomputed addresses for
-    // every row would not fit in registers alongside the next tile's state.
-    const uint8_t* src = stg + rr * T::EPI_ROW;
-    uint16_t* d = args.D + (int64_t)(m0 + wm * T::TM + rr) * args.ldd + n;
-    const int64_t dstep = (int64_t)RPI * args.ldd;
-#pragma unroll 1
-    for (int row0 = 0; row0 < rows_w; row0 += RPI) {
-      const int row = row0 + rr;
-      const i32x4_t v = *(const i32x4_t*)(src + 16 * (seg ^ T::epi_swz(row)));
-      if (row < rows_w) {
-        if (vec == 2) {
-          *(i32x4_t*)d = v;
-        } else if (vec == 1) {
-          *(i32x2_t*)d = (i32x2_t){v[0], v[1]};
-          *(i32x2_t*)(d + 4) = (i32x2_t){v[2], v[3]};
+          for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+      // One k-step's MFMAs: acc += A_frag x B_frag for every fragment pair.
+      auto mfmas = [&](auto jc, const frag_t (&xa)[FM], const frag_t (&xb)[FN], const uint32_t (&sa)[FM],
+                       const uint32_t (&sb)[FN]) {
+        constexpr int j = decltype(jc)::value;
+        if constexpr (!MM) return;
+        if constexpr (KIND == KIND_FP8 && SV) {
+          // A fragment f's scale: byte 2*(f%2) of dword f/2 (decoded per K-block)
+          [&]<int... ab>(std::integer_sequence<int, ab...>) {
+            ((acc[ab / FN][ab % FN] = mfma_scaled2<0, 0, 2 * ((ab / FN) % 2)>(
+                  xb[ab % FN], xa[ab / FN], acc[ab / FN][ab % FN], sb[ab % FN], sa[(ab / FN) / 2])),
+             ...);
+          }(std::make_integer_sequence<int, FM * FN>{});
+        } else if constexpr (T::PERM) {
+          // a-outer, b-inner as below; fragment f's scale is byte 2*(f%2) + j of
+          // dword f/2
+          [&]<int... ab>(std::integer_sequence<int, ab...>) {
+            ((acc[ab / FN][ab % FN] = mfma_scaled2<4, 2 * ((ab % FN) % 2) + j, 2 * ((ab / FN) % 2) + j>(
+                  xb[ab % FN], xa[ab / FN], acc[ab / FN][ab % FN], sb[(ab % FN) / 2], sa[(ab / FN) / 2])),
+             ...);
+          }(std::make_integer_sequence<int, FM * FN>{});
         } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (n + e < n_end) d[e] = (uint16_t)(((uint32_t)v[e / 2] >> (16 * (e % 2))) & 0xFFFF);
+          for (int a = 0; a < FM; ++a)
+#pragma unroll
+            for (int b = 0; b < FN; ++b) {
+              if constexpr (KIND == KIND_BF16)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb[b], xa[a], acc[a][b], 0, 0, 0);
+              else if constexpr (KIND == KIND_FP8)
+                acc[a][b] = mfma_scaled<0, 0>(xb[b], xa[a], acc[a][b], sb[b], sa[a]);
+              else
+                acc[a][b] = mfma_scaled<4, j>(xb[b], xa[a], acc[a][b], sb[b], sa[a]);
+            }
         }
+      };
+
+      uint32_t sa_cur[FM] = {}, sb_cur[FN] = {};
+
+      // Prologue: the previous tile's LDS reads are over once every wave has
+      // drained its own and met the others here; then stages 0 .. T0-1 are put in
+      // flight and stage 0 is waited for.  The previous tile's D stores are not
+      // waited for (a __syncthreads would wait for every outstanding memory
+      // operation): their latency overlaps this tile's first copies, and since
+      // loads complete in order, the prologue's vmcnt wait below still covers
+      // stage 0 whatever the stores do.
+      wait_vm_lds<63>();
+      ring_barrier();
+      // Paired copies due at a k-step g: chunk chunk_at(g) of the pair started at
+      // the barrier of stage pair_start(g); chunk 0 also loads the first stage's
+      // scale words, chunk 1 the second's.
+      auto pair_chunk = [&](auto gc, int round) {
+        constexpr int g = decltype(gc)::value;
+        constexpr int c = T::chunk_at(g), tl = T::pair_start(g) + NS - 1;
+        constexpr int b0 = T::pmod(tl, NS), b1 = T::pmod(tl + 1, NS);
+        const int t = round + tl;
+        if constexpr (c == 0) load_scales(t < nk ? t : 0, std::integral_constant<int, b0>{});
+        if constexpr (c == 1 && !T::SHARED_SCALES)
+          load_scales(t + 1 < nk ? t + 1 : 0, std::integral_constant<int, b1>{});
+        issue_chunk(t, b0, b1, c);
+      };
+      if constexpr (PR) {
+        // every chunk due before k-step 0 (pairs with a first stage t >= 0)
+        [&]<int... gs>(std::integer_sequence<int, gs...>) {
+          ((T::pair_start(gs - (NS + 2) * J) + NS - 1 >= 0
+                ? pair_chunk(std::integral_constant<int, gs - (NS + 2) * J>{}, 0)
+                : void()),
+           ...);
+        }(std::make_integer_sequence<int, (NS + 2) * J>{});
+      } else {
+        [&]<int... bs>(std::integer_sequence<int, bs...>) {
+          ((load_scales(bs < nk ? bs : 0, std::integral_constant<int, bs>{}), issue_stage(bs, bs)), ...);
+        }(std::make_integer_sequence<int, NS>{});
       }
-      src += RPI * T::EPI_ROW;
-      d += dstep;
+      wait_vm_lds<T::wait_prologue()>();
+      ring_barrier();
+      decode_scales(0, std::integral_constant<int, 0>{}, sa_cur, sb_cur);
+      read_frags(0, 0, fa[0], fb[0]);
+
+      // One stage.  Every stage runs the same code: after the last real one, the
+      // barrier, the copies (all out of range, so no memory traffic), the extra
+      // MFMAs on zero operands and the next-stage reads are dead work, which keeps
+      // the loop free of branches around the MFMAs.
+      auto stage = [&](auto ic, int s) {
+        constexpr int si = decltype(ic)::value;   // position of the stage in the round
+        constexpr int buf = si % NS;
+        constexpr int nbuf = (buf + 1) % NS;
+        static_assert(!PR || T::steady(si), "the copy schedule must repeat every round");
+        const int round = s - si;
+        auto body = [&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          constexpr int g = si * J + j;             // k-step index within the round
+          constexpr int nvm = PR ? T::chunk_vmem(g) : (j + 1 < J ? 0 : T::VMEM_PER_STAGE);
+          // fragment register set of this k-step: k-steps alternate sets across
+          // stage boundaries too (a round has an even number of them)
+          constexpr int cu = (si * J + j) & 1, nx = cu ^ 1;
+          constexpr int ca = T::DBA ? cu : 0, na = T::DBA ? nx : 0;
+          if constexpr (j + 1 < J) {
+            if constexpr (T::DBA) {
+              read_frags(buf, j + 1, fa[na], fb[nx]);
+              if constexpr (PR) pair_chunk(std::integral_constant<int, g>{}, round);
+              mfmas(jc, fa[ca], fb[cu], sa_cur, sb_cur);
+            } else {
+              if constexpr (PR) pair_chunk(std::integral_constant<int, g>{}, round);
+              mfmas(jc, fa[ca], fb[cu], sa_cur, sb_cur);
+              read_frags(buf, j + 1, fa[na], fb[nx]);
+            }
+            if constexpr (MM) interleave<FM * FN, (FM + FN) * RPF, nvm>();
+            __builtin_amdgcn_sched_barrier(0);
+          } else {
+            // Stage s+1 has landed once no more than wait_at() of this wave's copies
+            // are outstanding and every wave has passed the barrier; every wave has
+            // also finished reading buffer `buf` (copies issued from here on go to
+            // the buffers of stages already consumed).
+            wait_vm_lds<T::wait_at(si)>();
+            ring_barrier();
+            if constexpr (PR) {
+              pair_chunk(std::integral_constant<int, g>{}, round);
+            } else {
+              load_scales(s + NS < nk ? s + NS : 0, std::integral_constant<int, buf>{});
+              issue_stage(s + NS, buf);
+            }
+            if constexpr (T::DBA) {
+              read_frags(nbuf, 0, fa[na], fb[nx]);
+              mfmas(jc, fa[ca], fb[cu], sa_cur, sb_cur);
+            } else {
+              mfmas(jc, fa[ca], fb[cu], sa_cur, sb_cur);
+              read_frags(nbuf, 0, fa[na], fb[nx]);
+            }
+            if constexpr (MM) interleave<FM * FN, (FM + FN) * RPF, nvm>();
+            __builtin_amdgcn_sched_barrier(0);
+            // (shared scales: stage s+1 reads the set of its pair's first stage)
+            constexpr int sbuf = T::SHARED_SCALES ? T::pmod(((si + 1) & ~1), NS) : nbuf;
+            decode_scales(s + 1, std::integral_constant<int, sbuf>{}, sa_cur, sb_cur);
+          }
+        };
+        [&]<int... js>(std::integer_sequence<int, js...>) {
+          (body(std::integral_constant<int, js>{}), ...);
+        }(std::make_integer_sequence<int, J>{});
+      };
+      for (int s = 0; s < nk_pad; s += T::U) {
+        [&]<int... is>(std::integer_sequence<int, is...>) {
+          (stage(std::integral_constant<int, is>{}, s + is), ...);
+        }(std::make_integer_sequence<int, T::U>{});
+      }
+
+      // Epilogue.  MFMA operands were (B fragment, A fragment), so accumulator
+      // register r of lane l holds D[m][n] with m = l%32 and
+      // n = 8*(r/4) + 4*(l/32) + r%4: four consecutive columns per register quad.
+      // Permuted rows: fragment a's row l32 is tile row 4*l32 + a; with B permuted
+      // too (FP4), fragment b's column i is tile column FN*i + b, so the FN
+      // fragments b hold FN consecutive columns in the same register.
+      //
+      // Stored straight from those registers, every store instruction would put 16
+      // bytes into each of 32 rows, one L2 request per 16 bytes.  Instead each wave
+      // converts its TM x TN block to bf16 into its own part of the idle LDS ring,
+      // row-major, then stores it row by row with 16 bytes per lane, so an
+      // instruction writes whole 2*TN-byte row segments.  The 16-byte chunks of a
+      // staged row are XOR-swizzled by the row (epi_swz) so that the 32 rows one
+      // write instruction touches spread over the banks.
+      //
+      // The ring is idle once no copy is in flight (the dead stages' out-of-range
+      // copies still write zeros into it) and every wave has passed the barrier.
+      wait_vm_lds<0>();
+      ring_barrier();
+      // rows of this wave's block that exist (an expert's last row tile, the
+      // matrix edge): a wave with none skips its part
+      const int rows_w = m_end - (m0 + wm * T::TM) < T::TM ? m_end - (m0 + wm * T::TM) : T::TM;
+      if (rows_w <= 0) return;
+      uint8_t* const stg = smem + wave * T::EPI_WAVE_BYTES;
+      // The lane index, made opaque here: every staging address derives from it,
+      // and the compiler would otherwise hoist all of them out of the tile loop and
+      // spill them.
+      int el = lane;
+      asm volatile("" : "+v"(el));
+      const int el32 = el & 31, elg = el >> 5;
+      auto stage_quad = [&](int row, int col, float v0, float v1, float v2, float v3) {
+        // four consecutive columns col .. col+3 (col a multiple of 4) of `row`
+        const int chunk = (col >> 3) ^ T::epi_swz(row);
+        const i32x2_t w = {(int)pack_bf16x2(v0, v1), (int)pack_bf16x2(v2, v3)};
+        *(i32x2_t*)(stg + row * T::EPI_ROW + 16 * chunk + 2 * (col & 7)) = w;
+      };
+#pragma unroll
+      for (int a = 0; a < FM; ++a) {
+        const int row = T::PERM_A ? 4 * el32 + a : 32 * a + el32;
+        if constexpr (T::PERM && FN == 4) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            stage_quad(row, 4 * (8 * (r / 4) + 4 * elg + r % 4), acc[a][0][r], acc[a][1][r], acc[a][2][r],
+                       acc[a][3][r]);
+        } else if constexpr (T::PERM) {
+          // two B fragments: the same register of both holds two consecutive columns
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int col = 2 * (8 * (r / 4) + 4 * elg + r % 4);
+            const int chunk = (col >> 3) ^ T::epi_swz(row);
+            *(uint32_t*)(stg + row * T::EPI_ROW + 16 * chunk + 2 * (col & 7)) =
+                pack_bf16x2(acc[a][0][r], acc[a][1][r]);
+          }
+        } else {
+#pragma unroll
+          for (int b = 0; b < FN; ++b)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              stage_quad(row, 32 * b + 8 * q + 4 * elg, acc[a][b][4 * q], acc[a][b][4 * q + 1],
+                         acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]);
+        }
+        // one fragment row at a time: the compiler would otherwise move every
+        // accumulator into VGPRs first and spill
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // (a wave reads back only what it wrote; its LDS accesses execute in order)
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      constexpr int LPR = T::TN / 8;   // lanes per staged row, 16 bytes each
+      constexpr int RPI = 64 / LPR;    // rows per store instruction
+      const int rr = el / LPR, seg = el % LPR;
+      const int n = n0 + wn * T::TN + 8 * seg;
+      const int vec = n + 7 < n_end ? args.d_vec : 0;
+      // Walked with running pointers and not unrolled: precomputed addresses for
+      // every row would not fit in registers alongside the next tile's state.
+      const uint8_t* src = stg + rr * T::EPI_ROW;
+      uint16_t* d = args.D + (int64_t)(m0 + wm * T::TM + rr) * args.ldd + n;
+      const int64_t dstep = (int64_t)RPI * args.ldd;
+#pragma unroll 1
+      for (int row0 = 0; row0 < rows_w; row0 += RPI) {
+        const int row = row0 + rr;
+        const i32x4_t v = *(const i32x4_t*)(src + 16 * (seg ^ T::epi_swz(row)));
+        if (row < rows_w) {
+          if (vec == 2) {
+            *(i32x4_t*)d = v;
+          } else if (vec == 1) {
+            *(i32x2_t*)d = (i32x2_t){v[0], v[1]};
+            *(i32x2_t*)(d + 4) = (i32x2_t){v[2], v[3]};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (n + e < n_end) d[e] = (uint16_t)(((uint32_t)v[e / 2] >> (16 * (e % 2))) & 0xFFFF);
+          }
+        }
+        src += RPI * T::EPI_ROW;
+        d += dstep;
+      }
+    };
+    if constexpr (GROUPED && WM > 1 && T::NW > 4) {
+      if (m0 + wm * T::TM < m_end)
+        tile_body(std::true_type{});
+      else
+        tile_body(std::false_type{});
+    } else {
+      tile_body(std::true_type{});
     }
   }
 }
