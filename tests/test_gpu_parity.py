@@ -399,6 +399,34 @@ def test_grouped_half_and_full_row_tiles():
             assert_parity(Dh[lo:hi], ref[lo:hi], na[lo:hi], nb, what=f"half/full tiles expert {g}")
 
 
+def test_grouped_many_experts_mostly_empty():
+    """1024 experts (the most the library takes), all but four empty and the
+    non-empty ones far apart: the expert search walks sixteen 64-expert chunks."""
+    G, N, K = 1024, 256, 256
+    counts = [0] * G
+    counts[3], counts[200], counts[700], counts[1023] = 5, 130, 1, 64
+    w = workloads.grouped(G, N, K, seed=25, device=DEV, counts=counts, align=1)
+    D = run_grouped(w)
+    torch.cuda.synchronize()
+    t = w.tensors
+    off = t["offsets"].cpu().numpy()
+    rows = np.arange(off[-1])
+    A8, sfa = _u8(t["A"]), oracle.pack_scales(t["sfa"].cpu().numpy())
+    live = [g for g in range(G) if counts[g]]
+    Bh = np.zeros((G,) + tuple(t["B"].shape[1:]), dtype=np.uint8)
+    Sh = np.zeros((G,) + tuple(oracle.pack_scales(t["sfb"][0].cpu().numpy()).shape), dtype=np.int16)
+    for g in live:
+        Bh[g] = _u8(t["B"][g])
+        Sh[g] = oracle.pack_scales(t["sfb"][g].cpu().numpy())
+    ref = oracle.grouped_fp8(A8, sfa, Bh, Sh, off, rows=rows)
+    na = oracle.row_norms("e4m3", A8, sfa)
+    Dh = gpu_bits(D)
+    for g in live:
+        lo, hi = off[g], off[g + 1]
+        nb = oracle.row_norms("e4m3", Bh[g], Sh[g], gran_mn=128)
+        assert_parity(Dh[lo:hi], ref[lo:hi], na[lo:hi], nb, what=f"1024 experts, expert {g}")
+
+
 def test_grouped_unaligned_offsets_and_untouched_rows():
     """Offsets need no alignment; rows outside [off[0], off[G]) are not written."""
     G, N, K = 5, 256, 256
