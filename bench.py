@@ -65,17 +65,17 @@ QUANT_KINDS = ("quant_fp8", "quant_fp4", "quant_fp8_moe")
 PAGES_BF16_TFLOPS = 431.0
 
 KERNEL_NAME = {
-    "bf16": "gemm_kernel<0, 256, 256, 2, 4, 64, 5, 1, false, 0>",
-    "fp8": "gemm_kernel<1, 256, 256, 2, 4, 64, 5, 1, false, 1>",
-    "fp4": "gemm_kernel<2, 256, 256, 2, 4, 64, 5, 1, false, 1>",
-    "grouped": "gemm_kernel<1, 256, 256, 2, 4, 64, 5, 1, true, 1>",
+    "bf16": "gemm_kernel<0, 256, 256, 2, 4, 64, 5, 1, false, 0, 0>",
+    "fp8": "gemm_kernel<1, 256, 256, 2, 4, 64, 5, 1, false, 1, 0>",
+    "fp4": "gemm_kernel<2, 256, 256, 2, 4, 64, 5, 1, false, 1, 0>",
+    "grouped": "gemm_kernel<1, 256, 256, 2, 4, 64, 5, 1, true, 1, 8>",
     "quant_fp8": "quant_kernel<0, 0, 32, 2, 0>",
     "quant_fp4": "quant_kernel<1, 0, 32, 2, 0>",
     "quant_fp8_moe": "quant_kernel<0, 0, 32, 2, 0>",
-    "moe_ffn": "gemm_kernel<1, 256, 256, 2, 4, 64, 5, 1, true, 1> x2 + swiglu_quant_kernel<0>",
-    "masked": "gemm_kernel<1, 128, 512, 1, 4, 64, 4, 1, true, 1>",
-    "grouped_bf16": "gemm_kernel<0, 256, 256, 2, 4, 64, 5, 1, true, 0>",
-    "grouped_fp4": "gemm_kernel<2, 256, 256, 2, 4, 64, 5, 1, true, 1>",
+    "moe_ffn": "gemm_kernel<1, 256, 256, 2, 4, 64, 5, 1, true, 1, 8> x2 + swiglu_quant_kernel<0>",
+    "masked": "gemm_kernel<1, 128, 512, 1, 4, 64, 4, 1, true, 1, 0>",
+    "grouped_bf16": "gemm_kernel<0, 256, 256, 2, 4, 64, 5, 1, true, 0, 6>",
+    "grouped_fp4": "gemm_kernel<2, 256, 256, 2, 4, 64, 5, 1, true, 1, 4>",
 }
 
 

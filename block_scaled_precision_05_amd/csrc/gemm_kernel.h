@@ -427,6 +427,14 @@ __device__ __forceinline__ void wait_vm_lds() {
   __builtin_amdgcn_s_waitcnt(imm);
 }
 
+// The same without the LDS part: waits for the vector memory loads only.
+template <int VM>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(VM >= 0 && VM <= 63, "vmcnt is 6 bits");
+  constexpr int imm = (VM & 15) | (7 << 4) | (15 << 8) | ((VM >> 4) << 14);
+  __builtin_amdgcn_s_waitcnt(imm);
+}
+
 // Workgroup barrier of the LDS ring.  The caller waits for exactly the copies and
 // LDS reads it needs first (wait_vm_lds); a __syncthreads() would also wait for
 // every copy still in flight, which would empty the ring at each stage.  The
@@ -439,7 +447,8 @@ __device__ __forceinline__ void ring_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int KIND, int BM, int BN, int WM, int WN, int SB, int NS, int PR, bool GROUPED, int SV = 0>
+template <int KIND, int BM, int BN, int WM, int WN, int SB, int NS, int PR, bool GROUPED, int SV = 0,
+          int KOFF = 0>
 __global__ __launch_bounds__(WM* WN * 64)
 __attribute__((amdgpu_waves_per_eu((WM * WN + 3) / 4, (WM * WN + 3) / 4)))
 void gemm_kernel(const GemmArgs args) {
@@ -453,8 +462,16 @@ void gemm_kernel(const GemmArgs args) {
   const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31, lg = lane >> 5;
   const int nk = args.nk;
-  const int nk_pad = (nk + T::U - 1) / T::U * T::U;   // whole rounds of the ring; the
-                                                       // extra stages multiply zeros
+  // The stage loop runs whole rounds of U stages (buffer indices and register sets
+  // are compile-time).  When nk is not a multiple of U, the first round starts with
+  // KOFF stages that hold no data (the launcher picks KOFF = (U - nk % U) rounded
+  // down to even, so that paired stages stay the two halves of one 128-byte line);
+  // their copies read nothing and the first round, peeled off the loop, leaves out
+  // their MFMAs.  At most one stage (nk odd) is left over at the end, where it
+  // multiplies zeros.  Ring position p holds K stage p - KOFF.
+  static_assert(KOFF >= 0 && KOFF < T::U && KOFF % 2 == 0, "leading dead stages: even, under a round");
+  constexpr int koff = KOFF;
+  const int nk_pad = (nk + koff + T::U - 1) / T::U * T::U;
 
   int total_tiles;
   GroupCursor cur{0, 0};
@@ -549,16 +566,15 @@ void gemm_kernel(const GemmArgs args) {
       // prologue out of the tile loop and spills them all.
       asm volatile("" : "+v"(a_vbase), "+v"(b_vbase));
 
-      // Copy q of stage kt into LDS buffer `buf` (A copies first, then B); a stage
-      // past the end copies nothing (every lane's offset is out of range, so no
-      // memory is read).
+      // Copy q of K stage kt into LDS buffer `buf` (A copies first, then B); a stage
+      // before the start or past the end copies nothing (every lane's offset is out
+      // of range, so no memory is read, and the LDS receives zeros).
       auto copy_one = [&](int kt, int buf, int q) {
         uint8_t* sA = smem + buf * T::STAGE_BYTES;
         uint8_t* sB = sA + BM * SB;
         const int kb = kt * SB;
-        const int k_lim = kt < nk ? args.k_bytes : 0;
-        // past the K extent the offset gets bit 31, which no record count reaches
-        const uint32_t oob = kb + cp_c16 < k_lim ? 0u : kOOB;
+        // outside the K extent the offset gets bit 31, which no record count reaches
+        const uint32_t oob = (uint32_t)kt < (uint32_t)nk && kb + cp_c16 < args.k_bytes ? 0u : kOOB;
         uint8_t* const spare = smem + NS * T::STAGE_BYTES;
         if (q < T::A_LOADS) {
           const int ci = q * T::NW + wave;
@@ -796,10 +812,10 @@ void gemm_kernel(const GemmArgs args) {
         constexpr int g = decltype(gc)::value;
         constexpr int c = T::chunk_at(g), tl = T::pair_start(g) + NS - 1;
         constexpr int b0 = T::pmod(tl, NS), b1 = T::pmod(tl + 1, NS);
-        const int t = round + tl;
-        if constexpr (c == 0) load_scales(t < nk ? t : 0, std::integral_constant<int, b0>{});
+        const int t = round + tl - koff;   // K stage of the pair's first position
+        if constexpr (c == 0) load_scales(t >= 0 && t < nk ? t : 0, std::integral_constant<int, b0>{});
         if constexpr (c == 1 && !T::SHARED_SCALES)
-          load_scales(t + 1 < nk ? t + 1 : 0, std::integral_constant<int, b1>{});
+          load_scales(t + 1 >= 0 && t + 1 < nk ? t + 1 : 0, std::integral_constant<int, b1>{});
         issue_chunk(t, b0, b1, c);
       };
       if constexpr (PR) {
@@ -812,20 +828,25 @@ void gemm_kernel(const GemmArgs args) {
         }(std::make_integer_sequence<int, (NS + 2) * J>{});
       } else {
         [&]<int... bs>(std::integer_sequence<int, bs...>) {
-          ((load_scales(bs < nk ? bs : 0, std::integral_constant<int, bs>{}), issue_stage(bs, bs)), ...);
+          ((load_scales(bs - koff >= 0 && bs - koff < nk ? bs - koff : 0, std::integral_constant<int, bs>{}),
+            issue_stage(bs - koff, bs)),
+           ...);
         }(std::make_integer_sequence<int, NS>{});
       }
       wait_vm_lds<T::wait_prologue()>();
       ring_barrier();
-      decode_scales(0, std::integral_constant<int, 0>{}, sa_cur, sb_cur);
+      decode_scales(-koff, std::integral_constant<int, 0>{}, sa_cur, sb_cur);
       read_frags(0, 0, fa[0], fb[0]);
 
-      // One stage.  Every stage runs the same code: after the last real one, the
-      // barrier, the copies (all out of range, so no memory traffic), the extra
-      // MFMAs on zero operands and the next-stage reads are dead work, which keeps
-      // the loop free of branches around the MFMAs.
-      auto stage = [&](auto ic, int s) {
+      // One stage at ring position s.  Every stage of the steady loop runs the same
+      // code, free of branches around the MFMAs.  A DEAD stage (the first round's
+      // leading positions, which hold no data) keeps the barrier, the copies (all out
+      // of range, so no memory traffic), the scale loads and the fragment reads, so
+      // the copy schedule and its vmcnt arithmetic are those of every other round,
+      // and only leaves out the MFMAs, which would multiply zeros.
+      auto stage = [&](auto ic, auto deadc, int s) {
         constexpr int si = decltype(ic)::value;   // position of the stage in the round
+        constexpr bool DEAD = decltype(deadc)::value;
         constexpr int buf = si % NS;
         constexpr int nbuf = (buf + 1) % NS;
         static_assert(!PR || T::steady(si), "the copy schedule must repeat every round");
@@ -842,48 +863,68 @@ void gemm_kernel(const GemmArgs args) {
             if constexpr (T::DBA) {
               read_frags(buf, j + 1, fa[na], fb[nx]);
               if constexpr (PR) pair_chunk(std::integral_constant<int, g>{}, round);
-              mfmas(jc, fa[ca], fb[cu], sa_cur, sb_cur);
+              if constexpr (!DEAD) mfmas(jc, fa[ca], fb[cu], sa_cur, sb_cur);
             } else {
               if constexpr (PR) pair_chunk(std::integral_constant<int, g>{}, round);
-              mfmas(jc, fa[ca], fb[cu], sa_cur, sb_cur);
+              if constexpr (!DEAD) mfmas(jc, fa[ca], fb[cu], sa_cur, sb_cur);
               read_frags(buf, j + 1, fa[na], fb[nx]);
             }
-            if constexpr (MM) interleave<FM * FN, (FM + FN) * RPF, nvm>();
+            if constexpr (MM && !DEAD) interleave<FM * FN, (FM + FN) * RPF, nvm>();
             __builtin_amdgcn_sched_barrier(0);
           } else {
             // Stage s+1 has landed once no more than wait_at() of this wave's copies
-            // are outstanding and every wave has passed the barrier; every wave has
-            // also finished reading buffer `buf` (copies issued from here on go to
-            // the buffers of stages already consumed).
-            wait_vm_lds<T::wait_at(si)>();
+            // are outstanding and every wave has passed the barrier.  A barrier that
+            // starts a pair of copies also hands that pair the buffers read before
+            // it, so there every wave first waits for its own LDS reads; at the other
+            // barriers no copy targets a buffer just read, the reads stay in flight
+            // across the barrier, and the compiler waits for each one just before
+            // the first MFMA that uses its registers.
+            if constexpr (PR && T::chunk_at(g) != 0)
+              wait_vm<T::wait_at(si)>();
+            else
+              wait_vm_lds<T::wait_at(si)>();
             ring_barrier();
             if constexpr (PR) {
               pair_chunk(std::integral_constant<int, g>{}, round);
             } else {
-              load_scales(s + NS < nk ? s + NS : 0, std::integral_constant<int, buf>{});
-              issue_stage(s + NS, buf);
+              const int kt = s + NS - koff;
+              load_scales(kt >= 0 && kt < nk ? kt : 0, std::integral_constant<int, buf>{});
+              issue_stage(kt, buf);
             }
             if constexpr (T::DBA) {
               read_frags(nbuf, 0, fa[na], fb[nx]);
-              mfmas(jc, fa[ca], fb[cu], sa_cur, sb_cur);
+              if constexpr (!DEAD) mfmas(jc, fa[ca], fb[cu], sa_cur, sb_cur);
             } else {
-              mfmas(jc, fa[ca], fb[cu], sa_cur, sb_cur);
+              if constexpr (!DEAD) mfmas(jc, fa[ca], fb[cu], sa_cur, sb_cur);
               read_frags(nbuf, 0, fa[na], fb[nx]);
             }
-            if constexpr (MM) interleave<FM * FN, (FM + FN) * RPF, nvm>();
+            if constexpr (MM && !DEAD) interleave<FM * FN, (FM + FN) * RPF, nvm>();
             __builtin_amdgcn_sched_barrier(0);
             // (shared scales: stage s+1 reads the set of its pair's first stage)
             constexpr int sbuf = T::SHARED_SCALES ? T::pmod(((si + 1) & ~1), NS) : nbuf;
-            decode_scales(s + 1, std::integral_constant<int, sbuf>{}, sa_cur, sb_cur);
+            decode_scales(s + 1 - koff, std::integral_constant<int, sbuf>{}, sa_cur, sb_cur);
           }
         };
         [&]<int... js>(std::integer_sequence<int, js...>) {
           (body(std::integral_constant<int, js>{}), ...);
         }(std::make_integer_sequence<int, J>{});
       };
-      for (int s = 0; s < nk_pad; s += T::U) {
+      // With leading dead stages the first round is peeled off the loop.  (Its
+      // start is made opaque: known to be 0, it would let the compiler hoist that
+      // round's copy offsets out of the tile loop and spill them.)
+      if constexpr (koff > 0) {
+        if (nk_pad > 0) {
+          int s0 = 0;
+          asm volatile("" : "+s"(s0));
+          [&]<int... is>(std::integer_sequence<int, is...>) {
+            (stage(std::integral_constant<int, is>{}, std::integral_constant<bool, (is < koff)>{}, s0 + is),
+             ...);
+          }(std::make_integer_sequence<int, T::U>{});
+        }
+      }
+      for (int s = koff > 0 ? T::U : 0; s < nk_pad; s += T::U) {
         [&]<int... is>(std::integer_sequence<int, is...>) {
-          (stage(std::integral_constant<int, is>{}, s + is), ...);
+          (stage(std::integral_constant<int, is>{}, std::false_type{}, s + is), ...);
         }(std::make_integer_sequence<int, T::U>{});
       }
 

@@ -142,6 +142,22 @@ def test_dense_ragged(kind, M, N, K):
     dense_full(kind, M, N, K, 2000 + M)
 
 
+# The stage loop runs whole rounds of ten 64-byte stages; when the number of stages
+# nk is not a multiple of ten, the first round starts with an even number of stages
+# that hold no data (and an odd nk leaves one at the end).  These K values give every
+# remainder for every kind: nk = ceil(bytes of K per row / 64).
+@pytest.mark.parametrize("kind,K", [
+    ("fp8", 128), ("fp8", 256), ("fp8", 384), ("fp8", 512), ("fp8", 640), ("fp8", 6528),
+    ("fp4", 32), ("fp4", 160), ("fp4", 288), ("fp4", 544), ("fp4", 800), ("fp4", 1184),
+    ("fp4", 3264),
+    ("bf16", 8), ("bf16", 40), ("bf16", 104), ("bf16", 168), ("bf16", 232), ("bf16", 296),
+    ("bf16", 3272),
+])
+def test_every_stage_remainder(kind, K):
+    _say(f"stage remainder {kind} 300x260x{K}")
+    dense_full(kind, 300, 260, K, 3000 + K)
+
+
 def test_fp8_mid_workload():
     """FP8 1024x2048x4096 with 1x128 / 128x128 scales, compared in full."""
     _say("fp8 1024x2048x4096")
