@@ -73,7 +73,7 @@ KERNEL_NAME = {
     "quant_fp4": "quant_kernel<1, 0, 32, 2, 0>",
     "quant_fp8_moe": "quant_kernel<0, 0, 32, 2, 0>",
     "moe_ffn": "gemm_kernel<1, 256, 256, 2, 4, 64, 5, 1, true, 1, 8> x2 + swiglu_quant_kernel<0>",
-    "masked": "gemm_kernel<1, 128, 512, 1, 4, 64, 4, 1, true, 1, 0>",
+    "masked": "gemm_kernel<1, 128, 256, 1, 4, 64, 6, 1, true, 1, 0>",
     "grouped_bf16": "gemm_kernel<0, 256, 256, 2, 4, 64, 5, 1, true, 0, 6>",
     "grouped_fp4": "gemm_kernel<2, 256, 256, 2, 4, 64, 5, 1, true, 1, 4>",
 }

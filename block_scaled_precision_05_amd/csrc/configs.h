@@ -27,7 +27,11 @@
 // Grouped BF16 and FP4: the dense tiles of their kind.
 #define BSG_GROUPED_BF16_CFG 256, 256, 2, 4, 64, 5, 1
 #define BSG_GROUPED_FP4_CFG 256, 256, 2, 4, 64, 5, 1
-// Masked (decode-sized experts, tens of rows each): 128-row tiles, 1x4 waves of
-// 128x128 over 512 columns, four 40 KiB stages; 256-row tiles would multiply
-// mostly empty rows (measured 419 us against 340 us on the decode case).
-#define BSG_MASKED_CFG 128, 512, 1, 4, 64, 4, 1
+// Masked (decode-sized experts, tens of rows each): a stream of expert weights,
+// bound by HBM.  128-row tiles, 1x4 waves of 128x64 over 256 columns, a ring of six
+// 24 KiB stages (120 KiB of copies in flight per CU); on the decode case (48 experts,
+// N=4096, K=7168) 309 us against 318 us for 128x512 tiles with four 40 KiB stages
+// (the same bytes in flight, but 1.5 waves of workgroup tiles on 256 CUs), and 378 us
+// for 128x256 with four stages (72 KiB in flight).  256-row tiles would multiply
+// mostly empty rows (419 against 340 us).
+#define BSG_MASKED_CFG 128, 256, 1, 4, 64, 6, 1
