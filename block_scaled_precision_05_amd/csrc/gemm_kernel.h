@@ -463,12 +463,13 @@ void gemm_kernel(const GemmArgs args) {
   const int l32 = lane & 31, lg = lane >> 5;
   const int nk = args.nk;
   // The stage loop runs whole rounds of U stages (buffer indices and register sets
-  // are compile-time).  When nk is not a multiple of U, the first round starts with
-  // KOFF stages that hold no data (the launcher picks KOFF = (U - nk % U) rounded
-  // down to even, so that paired stages stay the two halves of one 128-byte line);
-  // their copies read nothing and the first round, peeled off the loop, leaves out
-  // their MFMAs.  At most one stage (nk odd) is left over at the end, where it
-  // multiplies zeros.  Ring position p holds K stage p - KOFF.
+  // are compile-time), so nk is padded up to whole rounds.  The padding either sits
+  // at the end, where those stages multiply zeros, or (KOFF > 0) at the start of the
+  // first round: KOFF stages that hold no data, an even count so that paired stages
+  // stay the two halves of one 128-byte line; their copies read nothing and the first
+  // round, peeled off the loop, leaves out their MFMAs.  The launcher picks KOFF =
+  // U - nk % U rounded down to even (one stage stays at the end when nk is odd), or 0
+  // when the padding is under 2% of the loop.  Ring position p holds K stage p - KOFF.
   static_assert(KOFF >= 0 && KOFF < T::U && KOFF % 2 == 0, "leading dead stages: even, under a round");
   constexpr int koff = KOFF;
   const int nk_pad = (nk + koff + T::U - 1) / T::U * T::U;
