@@ -386,8 +386,8 @@ __device__ __forceinline__ int xcd_remap(int i, int T) {
 }
 
 // Rasterisation: super-rows of GM M-tiles, N-major inside a super-row.
+template <int GM>
 __device__ __forceinline__ void raster(int p, int tiles_m, int tiles_n, int& tm, int& tn) {
-  constexpr int GM = 4;
   const int per_group = GM * tiles_n;
   const int grp = p / per_group;
   const int first_m = grp * GM;
@@ -517,14 +517,15 @@ void gemm_kernel(const GemmArgs args) {
     const int16_t* sfb = args.sfb;
     if constexpr (GROUPED) {
       // An expert's tiles form a contiguous range of the order; inside it they
-      // are rasterised like a dense matrix (super-rows of row tiles, N-major), so
-      // the tiles an XCD runs together share expert weights as well as rows.
+      // are rasterised like a dense matrix (super-rows of two row tiles, N-major),
+      // so the tiles an XCD runs together share expert weights as well as rows.
+      // (Two-row super-rows measured 1% faster than four on the MoE shapes.)
       int g, tile0, ntl, row_lo, row_hi;
       if (!grouped_find<BM>(args.offsets, args.G, args.cap, p / args.tiles_n, cur, g, tile0, ntl,
                             row_lo, row_hi))
         break;
       int tm, tn;
-      raster(p - tile0 * args.tiles_n, ntl, args.tiles_n, tm, tn);
+      raster<2>(p - tile0 * args.tiles_n, ntl, args.tiles_n, tm, tn);
       m0 = row_lo + tm * BM;
       m_end = m0 + BM < row_hi ? m0 + BM : row_hi;
       n0 = tn * BN;
@@ -532,7 +533,7 @@ void gemm_kernel(const GemmArgs args) {
       sfb += (int64_t)g * args.stride_sfb;
     } else {
       int tm, tn;
-      raster(p, args.tiles_m, args.tiles_n, tm, tn);
+      raster<4>(p, args.tiles_m, args.tiles_n, tm, tn);
       m0 = tm * BM;
       m_end = m0 + BM < args.M ? m0 + BM : args.M;
       n0 = tn * BN;
