@@ -1004,6 +1004,10 @@ void gemm_kernel(const GemmArgs args) {
       const int vec = n + 7 < n_end ? args.d_vec : 0;
       // Walked with running pointers and not unrolled: precomputed addresses for
       // every row would not fit in registers alongside the next tile's state.
+      // The stores carry the non-temporal hint: D is written once and never read
+      // here, and a tile-wave of workgroups writes about 4 MB per XCD at once, as much
+      // as its L2, which would otherwise evict the operand lines the next tiles read
+      // (alternating A/B: 0.3-1.9% faster on every shape).
       const uint8_t* src = stg + rr * T::EPI_ROW;
       uint16_t* d = args.D + (int64_t)(m0 + wm * T::TM + rr) * args.ldd + n;
       const int64_t dstep = (int64_t)RPI * args.ldd;
@@ -1013,10 +1017,10 @@ void gemm_kernel(const GemmArgs args) {
         const i32x4_t v = *(const i32x4_t*)(src + 16 * (seg ^ T::epi_swz(row)));
         if (row < rows_w) {
           if (vec == 2) {
-            *(i32x4_t*)d = v;
+            __builtin_nontemporal_store(v, (i32x4_t*)d);
           } else if (vec == 1) {
-            *(i32x2_t*)d = (i32x2_t){v[0], v[1]};
-            *(i32x2_t*)(d + 4) = (i32x2_t){v[2], v[3]};
+            __builtin_nontemporal_store((i32x2_t){v[0], v[1]}, (i32x2_t*)d);
+            __builtin_nontemporal_store((i32x2_t){v[2], v[3]}, (i32x2_t*)(d + 4));
           } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
