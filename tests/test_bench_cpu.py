@@ -1,0 +1,71 @@
+"""bench.py's host logic, without a GPU: the one-GPU contract, the lookup of the
+committed HBM counters, and the kernel names it reports for each timed case."""
+import json
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""
+
+
+def test_traffic_is_read_only_for_the_sources_it_was_taken_on():
+    with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+        tab = json.load(f)
+    ent = tab["bf16"]
+    assert bench.load_traffic("bf16", ent["src_sha"]) == ent["bytes_per_launch"]
+    assert bench.load_traffic("bf16", "0" * 16) is None
+    assert bench.load_traffic("no_such_case", ent["src_sha"]) is None
+
+
+def test_source_hash_ignores_comments_and_layout(tmp_path, monkeypatch):
+    csrc = tmp_path / "block_scaled_precision_05_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    for name in ("gemm_kernel.h", "configs.h"):
+        (csrc / name).write_text("int a; // one\n/* two */ int b;\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0 = bench.kernel_sources_sha("gemm")
+    (csrc / "gemm_kernel.h").write_text("int a;   // changed comment\n\n/* other */  int b;\n")
+    assert bench.kernel_sources_sha("gemm") == h0
+    (csrc / "gemm_kernel.h").write_text("int a; int c;\n")
+    assert bench.kernel_sources_sha("gemm") != h0
+
+
+def _stages(kind, K):
+    """K stages of 64 bytes per row, as the launcher counts them."""
+    row_bytes = {"bf16": 2 * K, "fp8": K, "fp4": K // 2}[kind]
+    return (row_bytes + 63) // 64
+
+
+def _leading_dead(nk, ns):
+    """The launcher's rule: pad nk to whole rounds of U stages (U = 2*NS for an odd
+    ring, else NS); the padding goes first, rounded down to even, unless it is under
+    2% of the loop."""
+    u = 2 * ns if ns % 2 else ns
+    koff = (u - nk % u) & ~1 if nk % u else 0
+    return 0 if koff * 50 <= nk + koff else koff
+
+
+@pytest.mark.parametrize("case,kind,K", [
+    ("bf16", "bf16", 16384), ("fp8", "fp8", 16384), ("fp4", "fp4", 16384),
+    ("grouped", "fp8", 7168), ("grouped_bf16", "bf16", 7168), ("grouped_fp4", "fp4", 7168),
+    ("masked", "fp8", 7168), ("moe_ffn", "fp8", 7168), ("moe_ffn", "fp8", 2048),
+])
+def test_reported_kernel_names_match_the_launch(case, kind, K):
+    name = bench.KERNEL_NAME[case]
+    args = [a.strip() for a in re.match(r"gemm_kernel<([^>]*)>", name).group(1).split(",")]
+    kind_id, ns, koff = int(args[0]), int(args[6]), int(args[10])
+    assert kind_id == {"bf16": 0, "fp8": 1, "fp4": 2}[kind]
+    assert koff == _leading_dead(_stages(kind, K), ns)
