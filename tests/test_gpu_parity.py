@@ -158,6 +158,16 @@ def test_every_stage_remainder(kind, K):
     dense_full(kind, 300, 260, K, 3000 + K)
 
 
+# The dense grid gives every workgroup the same number of tiles where it can: 300
+# tiles run as 152 workgroups (two tiles each, the last four with one), 520 tiles as
+# 176 (three each, the last eight with two); every output tile must still be
+# computed exactly once.
+@pytest.mark.parametrize("M,N", [(20 * 256, 15 * 256), (26 * 256 - 37, 20 * 256 - 5)])
+def test_dense_grid_with_uneven_tiles_per_workgroup(M, N):
+    _say(f"dense grid fp8 {M}x{N}x256")
+    dense_full("fp8", M, N, 256, 4000 + M)
+
+
 def test_fp8_mid_workload():
     """FP8 1024x2048x4096 with 1x128 / 128x128 scales, compared in full."""
     _say("fp8 1024x2048x4096")
