@@ -95,11 +95,14 @@ static int launch(GemmArgs a, hipStream_t stream) {
   int koff = a.nk % U ? (U - a.nk % U) & ~1 : 0;
   if (koff * 50 <= a.nk + koff) koff = 0;
   (void)hipGetLastError();
+  int st = BSG_OK;
   auto go = [&](auto kc) {
     constexpr int KO = decltype(kc)::value;
     if constexpr (KO < U)
       hipLaunchKernelGGL((gemm_kernel<KIND, BM, BN, WM, WN, SB, NS, PR, GROUPED, SV, KO>), dim3(grid),
                          dim3(T::NT), 0, stream, a);
+    else
+      st = BSG_ERR_UNSUPPORTED_SHAPE;   // not reached: koff < U by construction
   };
   static_assert(U <= 16, "leading dead stages are instantiated up to 14");
   switch (koff) {
@@ -113,6 +116,7 @@ static int launch(GemmArgs a, hipStream_t stream) {
     case 14: go(std::integral_constant<int, 14>{}); break;
     default: return BSG_ERR_UNSUPPORTED_SHAPE;
   }
+  if (st != BSG_OK) return st;
   return hipGetLastError() == hipSuccess ? BSG_OK : BSG_ERR_HIP;
 }
 
