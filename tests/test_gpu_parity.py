@@ -399,6 +399,30 @@ def test_grouped_small_full():
             assert_parity(Dh[lo:hi], ref[lo:hi], na[lo:hi], nb, what=f"grouped small expert {g}")
 
 
+# Every remainder of the grouped stage loop: K = 128, 256, 640 and 2048 give 2, 4,
+# 10 and 32 stages of 64 bytes, i.e. 8, 6, 0 and 8 leading dead stages.
+@pytest.mark.parametrize("K", [128, 256, 640, 2048])
+def test_grouped_every_stage_remainder(K):
+    _say(f"grouped stage remainder K={K}")
+    w = workloads.grouped(5, 384, K, seed=30 + K, device=DEV, counts=[256, 0, 384, 128, 0])
+    D = run_grouped(w)
+    torch.cuda.synchronize()
+    t = w.tensors
+    off = t["offsets"].cpu().numpy()
+    A8, sfa = _u8(t["A"]), oracle.pack_scales(t["sfa"].cpu().numpy())
+    ref = oracle.grouped_fp8(A8, sfa, np.stack([_u8(b) for b in t["B"]]),
+                             np.stack([oracle.pack_scales(x.cpu().numpy()) for x in t["sfb"]]),
+                             off, rows=np.arange(off[-1]))
+    na = oracle.row_norms("e4m3", A8, sfa)
+    Dh = gpu_bits(D)
+    for g in range(5):
+        lo, hi = off[g], off[g + 1]
+        if hi > lo:
+            nb = oracle.row_norms("e4m3", _u8(t["B"][g]), oracle.pack_scales(t["sfb"][g].cpu().numpy()),
+                                  gran_mn=128)
+            assert_parity(Dh[lo:hi], ref[lo:hi], na[lo:hi], nb, what=f"grouped K={K} expert {g}")
+
+
 def test_grouped_half_and_full_row_tiles():
     """Experts whose last row tile holds at most half a tile's rows (129 = one
     full-height tile, 128 and 1 = half tiles, 257 = a full tile then one row)
