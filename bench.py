@@ -65,17 +65,17 @@ QUANT_KINDS = ("quant_fp8", "quant_fp4", "quant_fp8_moe")
 PAGES_BF16_TFLOPS = 431.0
 
 KERNEL_NAME = {
-    "bf16": "gemm_kernel<0, 256, 256, 2, 4, 64, 5, 1, false, 0, 0>",
-    "fp8": "gemm_kernel<1, 256, 256, 2, 4, 64, 5, 1, false, 1, 0>",
-    "fp4": "gemm_kernel<2, 256, 256, 2, 4, 64, 5, 1, false, 1, 0>",
-    "grouped": "gemm_kernel<1, 256, 256, 2, 4, 64, 5, 1, true, 1, 8>",
+    "bf16": "gemm_kernel<0, 256, 256, 2, 4, 64, 5, 1, false, 0, 0, 0>",
+    "fp8": "gemm_kernel<1, 256, 256, 2, 4, 64, 5, 1, false, 1, 0, 0>",
+    "fp4": "gemm_kernel<2, 256, 256, 2, 4, 64, 5, 1, false, 1, 0, 0>",
+    "grouped": "gemm_kernel<1, 256, 256, 2, 4, 64, 5, 1, true, 1, 8, 0>",
     "quant_fp8": "quant_kernel<0, 0, 32, 2, 0>",
     "quant_fp4": "quant_kernel<1, 0, 32, 2, 0>",
     "quant_fp8_moe": "quant_kernel<0, 0, 32, 2, 0>",
-    "moe_ffn": "gemm_kernel<1, 256, 256, 2, 4, 64, 5, 1, true, 1, 8> x2 + swiglu_quant_kernel<0>",
-    "masked": "gemm_kernel<1, 128, 256, 1, 4, 64, 6, 1, true, 1, 0>",
-    "grouped_bf16": "gemm_kernel<0, 256, 256, 2, 4, 64, 5, 1, true, 0, 6>",
-    "grouped_fp4": "gemm_kernel<2, 256, 256, 2, 4, 64, 5, 1, true, 1, 4>",
+    "moe_ffn": "gemm_kernel<1, 256, 256, 2, 4, 64, 5, 1, true, 1, 8, 1> (up, SwiGLU epilogue) + gemm_kernel<1, 256, 256, 2, 4, 64, 5, 1, true, 1, 8, 0> (down)",
+    "masked": "gemm_kernel<1, 128, 256, 1, 4, 64, 6, 1, true, 1, 0, 0>",
+    "grouped_bf16": "gemm_kernel<0, 256, 256, 2, 4, 64, 5, 1, true, 0, 6, 0>",
+    "grouped_fp4": "gemm_kernel<2, 256, 256, 2, 4, 64, 5, 1, true, 1, 4, 0>",
 }
 
 
@@ -86,8 +86,8 @@ def log(msg):
 # Kernel sources behind each measured kind: a change to any of them detaches the
 # committed rocprofv3 counters from the kernel.
 SOURCES = {
-    "gemm": ("gemm_kernel.h", "configs.h"),
-    "quant": ("quant.hip",),
+    "gemm": ("gemm_kernel.h", "configs.h", "quant_math.h"),
+    "quant": ("quant.hip", "quant_math.h"),
 }
 
 

@@ -62,7 +62,8 @@ static int num_cus() {
   return g_num_cus[dev];
 }
 
-template <int KIND, int BM, int BN, int WM, int WN, int SB, int NS, int PR, bool GROUPED, int SV = 0>
+template <int KIND, int BM, int BN, int WM, int WN, int SB, int NS, int PR, bool GROUPED, int SV = 0,
+          int EPI = 0>
 static int launch(GemmArgs a, hipStream_t stream) {
   using T = GemmTile<KIND, BM, BN, WM, WN, SB, NS, PR, SV>;
   a.d_vec = (((uintptr_t)a.D & 15) == 0 && (a.ldd % 8) == 0) ? 2
@@ -99,7 +100,7 @@ static int launch(GemmArgs a, hipStream_t stream) {
   auto go = [&](auto kc) {
     constexpr int KO = decltype(kc)::value;
     if constexpr (KO < U)
-      hipLaunchKernelGGL((gemm_kernel<KIND, BM, BN, WM, WN, SB, NS, PR, GROUPED, SV, KO>), dim3(grid),
+      hipLaunchKernelGGL((gemm_kernel<KIND, BM, BN, WM, WN, SB, NS, PR, GROUPED, SV, KO, EPI>), dim3(grid),
                          dim3(T::NT), 0, stream, a);
     else
       st = BSG_ERR_UNSUPPORTED_SHAPE;   // not reached: koff < U by construction
@@ -322,6 +323,56 @@ int m_grouped_gemm_fp8(const void* A, int64_t lda, const int16_t* sfa, int64_t l
   if (sv_ok(sfa, ld_sfa)) return launch<KIND_FP8, BSG_GROUPED_CFG, true, 1>(a, (hipStream_t)stream);
   return launch<KIND_FP8, BSG_GROUPED_CFG, true, 0>(a, (hipStream_t)stream);
 }
+
+}  // extern "C"
+
+namespace bsg {
+
+// The FFN core's up-projection with the SwiGLU epilogue: Y = fp8(silu(gate) * up)
+// and its packed 1x128 scales straight from the grouped FP8 GEMM over W13 = [gate;
+// up] (2*inter rows per expert); H is never formed.  Arguments were checked by the
+// caller; inter is a multiple of 128, Y 8-byte aligned with ldy a multiple of 8.
+int grouped_fp8_swiglu(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa, const void* W13,
+                       int64_t ldw, int64_t stride_w, const int16_t* sfw, int64_t ld_sfw,
+                       int64_t stride_sfw, const int32_t* group_offsets, int32_t G, int64_t M_total,
+                       int64_t hidden, int64_t inter, void* Y, int64_t ldy, int16_t* sfy, int64_t ld_sfy,
+                       int32_t rule, void* stream) {
+  const int64_t K = hidden, N = 2 * inter;
+  GemmArgs a = {};
+  a.A = (const uint8_t*)A;
+  a.B = (const uint8_t*)W13;
+  a.sfa = sfa;
+  a.sfb = sfw;
+  a.offsets = group_offsets;
+  a.lda = lda;
+  a.ldb = ldw;
+  a.ld_sfa = ld_sfa;
+  a.ld_sfb = ld_sfw;
+  a.stride_b = stride_w;
+  a.stride_sfb = stride_sfw;
+  a.M = (int32_t)M_total;
+  a.N = (int32_t)N;
+  a.K = (int32_t)K;
+  a.k_bytes = (int32_t)K;
+  a.kp_count = (int32_t)((K / 128 + 1) / 2);
+  a.sfb_rows = (int32_t)((N + 127) / 128);
+  a.G = G;
+  a.Y = (uint8_t*)Y;
+  a.sfy = sfy;
+  a.ldy = ldy;
+  a.ld_sfy = ld_sfy;
+  a.inter = (int32_t)inter;
+  const bool sv = sv_ok(sfa, ld_sfa);
+  if (rule == BSG_SCALE_CEIL)
+    return sv ? launch<KIND_FP8, BSG_GROUPED_CFG, true, 1, 1>(a, (hipStream_t)stream)
+              : launch<KIND_FP8, BSG_GROUPED_CFG, true, 0, 1>(a, (hipStream_t)stream);
+  return sv ? launch<KIND_FP8, BSG_GROUPED_CFG, true, 1, 2>(a, (hipStream_t)stream)
+            : launch<KIND_FP8, BSG_GROUPED_CFG, true, 0, 2>(a, (hipStream_t)stream);
+}
+
+}  // namespace bsg
+
+extern "C" {
 
 int m_grouped_gemm_fp8_masked(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
                               const void* B, int64_t ldb, int64_t stride_b,

@@ -42,6 +42,8 @@
 #include <stdint.h>
 
 #include <type_traits>
+
+#include "quant_math.h"
 #include <utility>
 
 namespace bsg {
@@ -83,6 +85,16 @@ struct GemmArgs {
   int32_t d_vec;            // widest D store: 2 = 16 bytes (D and ldd*2 16-aligned), 1 = 8, 0 = 2
   int32_t cap;              // grouped: 0 = contiguous experts, rows [offsets[g], offsets[g+1]);
                             // > 0 = masked layout, rows [g*cap, g*cap + min(offsets[g], cap))
+  // SwiGLU epilogue (up-projection of an FFN, EPI > 0): B holds [gate; up] rows of
+  // each expert, gate in rows [0, inter), up in [inter, 2*inter); a tile of BN B
+  // rows takes BN/2 gate and the matching BN/2 up rows; instead of D the tile writes
+  // Y = fp8(silu(gate) * up) [M][ldy bytes] and its 1x128 UE8M0 scales, packed int16
+  // MN-major sfy [ceil(inter/256)][ld_sfy].
+  uint8_t* Y;
+  int16_t* sfy;
+  int64_t ldy;
+  int64_t ld_sfy;
+  int32_t inter;
 };
 
 // Buffer resource word 3 for raw (unswizzled, stride 0) byte-addressed buffers on
@@ -448,12 +460,16 @@ __device__ __forceinline__ void ring_barrier() {
 }
 
 template <int KIND, int BM, int BN, int WM, int WN, int SB, int NS, int PR, bool GROUPED, int SV = 0,
-          int KOFF = 0>
+          int KOFF = 0, int EPI = 0>
 __global__ __launch_bounds__(WM* WN * 64)
 __attribute__((amdgpu_waves_per_eu((WM * WN + 3) / 4, (WM * WN + 3) / 4)))
 void gemm_kernel(const GemmArgs args) {
   using T = GemmTile<KIND, BM, BN, WM, WN, SB, NS, PR, SV>;
   constexpr int FM = T::FM, FN = T::FN, J = T::J, RPF = T::RPF, NC = T::NC, SW = T::SW;
+  // EPI: 0 = bf16 D; 1 + rule = SwiGLU and FP8 1x128 requantisation (rule CEIL / OCP_MX)
+  static_assert(EPI == 0 || (KIND == KIND_FP8 && GROUPED && !T::PERM_B && T::ONE_B_SCALE &&
+                             T::NW * T::ROWS_PER_COPY == BN / 2 && BN / 2 == 128 && T::TN <= 64),
+                "the SwiGLU epilogue: FP8 grouped tiles whose B copies and scale blocks stay in one half");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
 
   const int tid = threadIdx.x;
@@ -528,7 +544,7 @@ void gemm_kernel(const GemmArgs args) {
       raster<2>(p - tile0 * args.tiles_n, ntl, args.tiles_n, tm, tn);
       m0 = row_lo + tm * BM;
       m_end = m0 + BM < row_hi ? m0 + BM : row_hi;
-      n0 = tn * BN;
+      n0 = tn * (EPI ? BN / 2 : BN);
       Bbase += (int64_t)g * args.stride_b;
       sfb += (int64_t)g * args.stride_sfb;
     } else {
@@ -557,8 +573,9 @@ void gemm_kernel(const GemmArgs args) {
       // end of the matrix (or of the expert) read as zero.
       const __amdgpu_buffer_rsrc_t ra =
           make_rsrc(args.A + (int64_t)m0 * args.lda, (uint32_t)((rows_a - 1) * args.lda + args.k_bytes));
-      const __amdgpu_buffer_rsrc_t rb =
-          make_rsrc(Bbase + (int64_t)n0 * args.ldb, (uint32_t)((rows_b - 1) * args.ldb + args.k_bytes));
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(
+          Bbase + (int64_t)n0 * args.ldb,
+          (uint32_t)(((EPI ? args.inter + BN / 2 : rows_b) - 1) * args.ldb + args.k_bytes));
       // Copy q of a wave fills LDS rows (slots) (q*NW + wave) * ROWS_PER_COPY + cp_row
       // from tile row perm(slot); the lane part and the q part of the slot occupy
       // disjoint bits, so perm splits into a per-lane row and a per-q row.
@@ -590,7 +607,9 @@ void gemm_kernel(const GemmArgs args) {
           const int qb = q - T::A_LOADS;
           const int ci = qb * T::NW + wave;
           const bool dummy = T::DUMMY && ci >= T::B_COPIES;
-          const uint32_t qrow = (uint32_t)T::perm_b(qb * T::NW * T::ROWS_PER_COPY);
+          const uint32_t qrow0 = (uint32_t)T::perm_b(qb * T::NW * T::ROWS_PER_COPY);
+          // (SwiGLU epilogue: tile rows past BN/2 are up rows, inter rows further on)
+          const uint32_t qrow = EPI && qrow0 >= (uint32_t)(BN / 2) ? qrow0 - BN / 2 + (uint32_t)args.inter : qrow0;
           const uint32_t off = (b_vbase + qrow * (uint32_t)args.ldb + kb) | oob | (dummy ? kOOB : 0u);
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
               rb, (__attribute__((address_space(3))) void*)(dummy ? spare : sB + T::ROWS_PER_COPY * ci * SB),
@@ -626,7 +645,8 @@ void gemm_kernel(const GemmArgs args) {
       // (FP4: the lane's fragment rows are 4*l32 .. 4*l32 + 3 of the wave block)
       uint32_t sa_voff = 2u * (uint32_t)(m0 + wm * T::TM + (T::PERM_A ? 4 * l32 : l32));
       asm volatile("" : "+v"(sa_voff));
-      uint32_t sb_voff = KIND == KIND_FP8 ? 2u * (uint32_t)((n0 + wn * T::TN) / 128)
+      const int brow0 = EPI && wn * T::TN >= BN / 2 ? args.inter + n0 + wn * T::TN - BN / 2 : n0 + wn * T::TN;
+      uint32_t sb_voff = KIND == KIND_FP8 ? 2u * (uint32_t)(brow0 / 128)
                                           : 2u * (uint32_t)(n0 + wn * T::TN + (T::PERM_B ? FN * l32 : l32));
       asm volatile("" : "+v"(sb_voff));
       // Raw scale words of stage kt (packed int16, not decoded yet).
@@ -952,7 +972,8 @@ void gemm_kernel(const GemmArgs args) {
       // rows of this wave's block that exist (an expert's last row tile, the
       // matrix edge): a wave with none skips its part
       const int rows_w = m_end - (m0 + wm * T::TM) < T::TM ? m_end - (m0 + wm * T::TM) : T::TM;
-      if (rows_w <= 0) return;
+      // (the SwiGLU epilogue has every wave meet one more barrier: no early exit)
+      if (EPI == 0 && rows_w <= 0) return;
       uint8_t* const stg = smem + wave * T::EPI_WAVE_BYTES;
       // The lane index, made opaque here: every staging address derives from it,
       // and the compiler would otherwise hoist all of them out of the tile loop and
@@ -994,6 +1015,44 @@ void gemm_kernel(const GemmArgs args) {
         // one fragment row at a time: the compiler would otherwise move every
         // accumulator into VGPRs first and spill
         __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (EPI > 0) {
+        // SwiGLU and FP8 1x128 requantisation.  Tile row r's gate values (tile columns
+        // 0 .. BN/2-1) and up values (BN/2 .. BN-1) lie in the staged blocks of other
+        // waves, so every wave's block must be in place first.  Wave w then takes
+        // rows 32w .. 32w+31, four rows a pass, 16 lanes a row, 8 outputs a lane:
+        // exactly the arithmetic of the SwiGLU quantiser, on the same bf16 values.
+        wait_vm_lds<63>();
+        ring_barrier();
+        constexpr int RULE = EPI - 1;
+        const int seg = el & 15, rsub = el >> 4;
+        const int blk = n0 / 128, kb_total = args.inter / 128;
+        const int gcol = 8 * seg, ucol = BN / 2 + 8 * seg;
+#pragma unroll 1
+        for (int it = 0; it < 8; ++it) {
+          const int row = 32 * wave + 4 * it + rsub;
+          const int wmr = row / T::TM, r_in = row - wmr * T::TM;
+          const int sw = T::epi_swz(r_in);
+          const uint8_t* gp = smem + (wmr * WN + gcol / T::TN) * T::EPI_WAVE_BYTES + r_in * T::EPI_ROW +
+                              16 * (((gcol % T::TN) / 8) ^ sw);
+          const uint8_t* upp = smem + (wmr * WN + ucol / T::TN) * T::EPI_WAVE_BYTES + r_in * T::EPI_ROW +
+                               16 * (((ucol % T::TN) / 8) ^ sw);
+          const bsg_qm::qm_u32x4_t g = *(const bsg_qm::qm_u32x4_t*)gp;
+          const bsg_qm::qm_u32x4_t u = *(const bsg_qm::qm_u32x4_t*)upp;
+          bsg_qm::qm_u32x2_t codes;
+          int byte;
+          bsg_qm::swiglu_fp8x8<RULE>(g, u, codes, byte);
+          if (m0 + row < m_end) {
+            *(bsg_qm::qm_u32x2_t*)(args.Y + (int64_t)(m0 + row) * args.ldy + n0 + 8 * seg) = codes;
+            if (seg == 0) {
+              uint8_t* sp = (uint8_t*)args.sfy + 2 * ((int64_t)(blk >> 1) * args.ld_sfy + m0 + row);
+              sp[blk & 1] = (uint8_t)byte;
+              // an odd number of 128-blocks: the last pair's high byte is the neutral 1.0
+              if ((blk & 1) == 0 && blk + 1 == kb_total) sp[1] = 0x7F;
+            }
+          }
+        }
+        return;
       }
       // (a wave reads back only what it wrote; its LDS accesses execute in order)
       __atomic_signal_fence(__ATOMIC_SEQ_CST);

@@ -21,4 +21,12 @@ int grouped_fp8_check(const void* A, int64_t lda, const int16_t* sfa, int64_t ld
                       const int32_t* group_offsets, int32_t G, int64_t M_total, int64_t N,
                       int64_t K);
 
+// The FFN core's up-projection with the SwiGLU epilogue (Y codes and packed 1x128
+// scales instead of H); arguments already checked.
+int grouped_fp8_swiglu(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa, const void* W13,
+                       int64_t ldw, int64_t stride_w, const int16_t* sfw, int64_t ld_sfw,
+                       int64_t stride_sfw, const int32_t* group_offsets, int32_t G, int64_t M_total,
+                       int64_t hidden, int64_t inter, void* Y, int64_t ldy, int16_t* sfy, int64_t ld_sfy,
+                       int32_t rule, void* stream);
+
 }  // namespace bsg

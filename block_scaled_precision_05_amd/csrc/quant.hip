@@ -31,8 +31,11 @@
 
 #include "../../include/bsg.h"
 #include "internal.h"
+#include "quant_math.h"
 
 namespace bsg_quant {
+
+using namespace bsg_qm;
 
 constexpr int kRows = 32;        // rows per workgroup
 constexpr int kCols = 512;       // elements per workgroup row
@@ -45,50 +48,7 @@ constexpr int kThreads = 64 * kWaves;
 // workgroups.
 constexpr int kLoadAux = 2;
 
-enum { FMT_E4M3 = 0, FMT_E2M1 = 1 };
 
-template <int FMT>
-struct Fmt;
-template <>
-struct Fmt<FMT_E4M3> {
-  static constexpr int GK = 128;        // elements per block
-  static constexpr int LANES = GK / 8;  // lanes per block
-  static constexpr int QX = 9;          // 448 = 0.875 * 2^9
-  static constexpr int QT = 224;        // 0.875 * 256
-  static constexpr int EMAX = 8;
-};
-template <>
-struct Fmt<FMT_E2M1> {
-  static constexpr int GK = 32;
-  static constexpr int LANES = GK / 8;
-  static constexpr int QX = 3;          // 6 = 0.75 * 2^3
-  static constexpr int QT = 192;        // 0.75 * 256
-  static constexpr int EMAX = 2;
-};
-
-// Scale byte of a block from its largest magnitude, given as fp32 bits a (sign
-// bit clear; a bf16 magnitude h is a = h << 16).  The magnitude is sig * 2^ex
-// with sig the 24-bit significand (hidden bit included) or, below the normal
-// range, the 23-bit fraction at ex = -149.  Normalising sig to sn in [2^23,
-// 2^24) gives floor(log2) p, and amax = sn/2^24 * 2^(p+1); with qmax = qt/256 *
-// 2^qx the smallest e with amax <= qmax * 2^e is p + 1 - qx, plus one when
-// sn > qt * 2^16.  a == 0 needs no branch: clz gives 32, p = -150 and the byte
-// clamps to 0.
-template <int FMT, int RULE>
-__device__ __forceinline__ int scale_byte(uint32_t a) {
-  using F = Fmt<FMT>;
-  const uint32_t E = a >> 23;
-  const uint32_t sig = E ? (0x800000u | (a & 0x7FFFFFu)) : (a & 0x7FFFFFu);
-  const int ex = E ? (int)E - 150 : -149;
-  const int lz = __clz(sig) - 8;
-  const uint32_t sn = sig << lz;
-  const int p = 23 - lz + ex;
-  const int e = RULE == BSG_SCALE_CEIL
-                    ? p + 1 - F::QX + (sn > ((uint32_t)F::QT << 16) ? 1 : 0)
-                    : p - F::EMAX;
-  const int b = e + 127;
-  return b < 0 ? 0 : (b > 254 ? 254 : b);
-}
 
 typedef __attribute__((ext_vector_type(2))) short short2_t;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
@@ -105,10 +65,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(2))) unsigned short ushort2_t;
 
-// 2^(byte-127) as an fp32 (byte 0 is the subnormal 2^-127).
-__device__ __forceinline__ float scale_f32(int byte) {
-  return __uint_as_float(byte ? ((uint32_t)byte << 23) : 0x00400000u);
-}
 
 __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(ushort2_t, a),
@@ -120,19 +76,6 @@ __device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
                                                                 __builtin_bit_cast(ushort2_t, b)));
 }
 
-// Max over the lanes of one block: 16 lanes (e4m3) or 4 (e2m1), all DPP moves.
-// quad_perm [1,0,3,2] and [2,3,0,1] make a quad uniform; row_ror 4 and 8 then
-// combine the four quads of a 16-lane row.
-template <int LANES>
-__device__ __forceinline__ uint32_t block_max(uint32_t h) {
-  h = max(h, (uint32_t)__builtin_amdgcn_mov_dpp((int)h, 0xB1, 0xF, 0xF, false));
-  h = max(h, (uint32_t)__builtin_amdgcn_mov_dpp((int)h, 0x4E, 0xF, 0xF, false));
-  if (LANES == 16) {
-    h = max(h, (uint32_t)__builtin_amdgcn_mov_dpp((int)h, 0x124, 0xF, 0xF, false));
-    h = max(h, (uint32_t)__builtin_amdgcn_mov_dpp((int)h, 0x128, 0xF, 0xF, false));
-  }
-  return h;
-}
 
 // ROWS: rows per workgroup (at most 64); LAUX / SAUX: cache-policy bits of
 // the operand loads and the code stores.
@@ -232,9 +175,6 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
 // SiLU in fp32: g / (1 + e^-g) with the accurate expf and a reciprocal (about 3
 // ulp in all).  For g below about -88 e^-g is +inf, the reciprocal 0 and the
 // result a zero with g's sign, the limit.
-__device__ __forceinline__ float silu_f32(float g) {
-  return g * __builtin_amdgcn_rcpf(1.0f + expf(-g));
-}
 
 // SwiGLU of an up-projection output followed by FP8 1x128 quantisation.  H is
 // bf16 [M][ldh] with the gate in columns [0, I) and the up projection in
@@ -282,32 +222,9 @@ __global__ __launch_bounds__(kThreads) void swiglu_quant_kernel(
 #pragma unroll
   for (int i = 0; i < kRowsPerWave; ++i) {
     const int rl = wave + i * kWaves;
-    float y[8];
-    uint32_t a = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t g = gr[i][j], u = ur[i][j];
-      y[2 * j] = silu_f32(__uint_as_float(g << 16)) * __uint_as_float(u << 16);
-      y[2 * j + 1] = silu_f32(__uint_as_float(g & 0xFFFF0000u)) * __uint_as_float(u & 0xFFFF0000u);
-      a = max(a, __float_as_uint(y[2 * j]) & 0x7FFFFFFFu);
-      a = max(a, __float_as_uint(y[2 * j + 1]) & 0x7FFFFFFFu);
-    }
-    a = block_max<F::LANES>(a);
-    const int byte = scale_byte<FMT_E4M3, RULE>(a);
-    const float sc = scale_f32(byte);
-    if (RULE == BSG_SCALE_OCP_MX) {
-      // saturate at 448 * sc before the conversion (which would give NaN)
-      const float lim = 448.0f * sc;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        y[j] = __builtin_copysignf(fminf(fabsf(y[j]), lim), y[j]);
-    }
-    short2_t lo = {0, 0}, hi = {0, 0};
-    lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, y[0], y[1], sc, false);
-    lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, y[2], y[3], sc, true);
-    hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, y[4], y[5], sc, false);
-    hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, y[6], y[7], sc, true);
-    const u32x2_t v = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+    u32x2_t v;
+    int byte;
+    swiglu_fp8x8<RULE>(gr[i], ur[i], v, byte);
     __builtin_amdgcn_raw_buffer_store_b64(v, qr, qoff, rl * (int)ldq, 0);
     const int hb = __shfl_down(byte, F::LANES);
     if ((lane % (2 * F::LANES)) == 0) {
@@ -432,11 +349,19 @@ int moe_ffn_fp8(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
                               D, ldd, group_offsets, G, M_total, hidden, inter);
   if (st != BSG_OK) return st;
   if (M_total == 0 || G == 0 || hidden == 0 || inter == 0) return BSG_OK;
-  st = m_grouped_gemm_fp8(A, lda, sfa, ld_sfa, W13, ldw13, stride_w13, sfw13, ld_sfw13,
-                          stride_sfw13, H, ldh, group_offsets, G, M_total, 2 * inter, hidden,
-                          stream);
-  if (st != BSG_OK) return st;
-  st = swiglu_launch(H, ldh, Y, ldy, sfy, ld_sfy, M_total, inter, rule, (hipStream_t)stream);
+  if (inter % 128 == 0 && ((uintptr_t)Y & 7) == 0 && ldy % 8 == 0) {
+    // the up-projection applies SwiGLU and the requantisation in its epilogue; H is
+    // not written
+    st = bsg::grouped_fp8_swiglu(A, lda, sfa, ld_sfa, W13, ldw13, stride_w13, sfw13, ld_sfw13,
+                                 stride_sfw13, group_offsets, G, M_total, hidden, inter, Y, ldy,
+                                 sfy, ld_sfy, rule, stream);
+  } else {
+    st = m_grouped_gemm_fp8(A, lda, sfa, ld_sfa, W13, ldw13, stride_w13, sfw13, ld_sfw13,
+                            stride_sfw13, H, ldh, group_offsets, G, M_total, 2 * inter, hidden,
+                            stream);
+    if (st != BSG_OK) return st;
+    st = swiglu_launch(H, ldh, Y, ldy, sfy, ld_sfy, M_total, inter, rule, (hipStream_t)stream);
+  }
   if (st != BSG_OK) return st;
   return m_grouped_gemm_fp8(Y, ldy, sfy, ld_sfy, W2, ldw2, stride_w2, sfw2, ld_sfw2, stride_sfw2,
                             D, ldd, group_offsets, G, M_total, hidden, inter, stream);

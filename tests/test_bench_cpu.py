@@ -33,7 +33,7 @@ def test_traffic_is_read_only_for_the_sources_it_was_taken_on():
 def test_source_hash_ignores_comments_and_layout(tmp_path, monkeypatch):
     csrc = tmp_path / "block_scaled_precision_05_amd" / "csrc"
     csrc.mkdir(parents=True)
-    for name in ("gemm_kernel.h", "configs.h"):
+    for name in bench.SOURCES["gemm"]:
         (csrc / name).write_text("int a; // one\n/* two */ int b;\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     h0 = bench.kernel_sources_sha("gemm")

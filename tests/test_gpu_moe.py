@@ -91,7 +91,20 @@ def _ffn_gpu(w):
     sfy = torch.empty((inter // 128 + 1) // 2, M, dtype=torch.int16, device=DEV)
     D = bsg.moe_ffn_fp8(t["A"], sfa, t["W13"], sfw13, t["W2"], sfw2, t["offsets"],
                         workspace=(H, Y, sfy))
+    # With inter a multiple of 128 the up-projection applies SwiGLU and the FP8
+    # requantisation in its epilogue and H stays unwritten.  The same GEMM run on its
+    # own gives H; quantising that H must reproduce the call's Y and scales bit for bit.
+    H = bsg.m_grouped_gemm_fp8(t["A"], sfa, t["W13"], sfw13, t["offsets"])
+    Yq, sfq = bsg.swiglu_quantize_fp8(H, inter)
     torch.cuda.synchronize()
+    off = t["offsets"].cpu().numpy()
+    rows = np.concatenate([np.arange(off[g], off[g + 1]) for g in range(len(off) - 1)])
+    y_got = Y.view(torch.uint8).cpu().numpy()[rows]
+    y_want = Yq.view(torch.uint8).cpu().numpy()[rows]
+    assert np.array_equal(y_got, y_want), "moe_ffn: Y differs from quantising H"
+    s_got = sfy.cpu().numpy()[:, rows]
+    s_want = sfq.cpu().numpy()[:, rows]
+    assert np.array_equal(s_got, s_want), "moe_ffn: Y scales differ from quantising H"
     return D, H
 
 
@@ -171,6 +184,16 @@ def test_moe_ffn_small_full():
     off = w.tensors["offsets"].cpu().numpy()
     rows = np.concatenate([np.arange(off[g], off[g + 1]) for g in range(len(off) - 1)])
     _check_ffn(w, rows, "moe_ffn small")
+
+
+def test_moe_ffn_odd_number_of_scale_blocks():
+    """inter = 384: three 128-wide blocks, so the last packed scale word of every row
+    holds one block and the neutral padding byte."""
+    _say("moe_ffn: 3 experts, hidden 512, inter 384")
+    w = workloads.moe_ffn(33, device=DEV, hidden=512, inter=384, counts=[200, 128, 0])
+    off = w.tensors["offsets"].cpu().numpy()
+    rows = np.concatenate([np.arange(off[g], off[g + 1]) for g in range(len(off) - 1)])
+    _check_ffn(w, rows, "moe_ffn inter 384")
 
 
 def test_moe_ffn_workload_sampled_rows():
