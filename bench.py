@@ -26,8 +26,8 @@ packed UE8M0 scales) are timed the same way on the dense shape's A (4096x16384)
 and on the MoE tokens (16384x7168), reported in GB/s of algorithmic traffic
 against the 8 TB/s HBM peak.
 
-The MoE FFN core (grouped up-projection, SwiGLU + FP8 requantisation, grouped
-down-projection) runs on one GPU's share of the pages' fused MoE case: 48 of 384
+The MoE FFN core (grouped up-projection with SwiGLU + FP8 requantisation in its
+epilogue, grouped down-projection) runs on one GPU's share of the pages' fused MoE case: 48 of 384
 experts (EP8) plus the shared expert, 16384 tokens top-6, hidden 7168,
 intermediate 2048; TFLOPS count useful (unpadded) rows.
 
@@ -334,7 +334,7 @@ def summarize(kind, r, steps):
     if kind == "masked":
         out["gb_per_s"] = r["min_bytes"] * steps / r["wall_s"] / 1e9
         out["frac_of_hbm_peak"] = out["gb_per_s"] / HBM_PEAK_GBS
-    # per-launch roofline of the case's GEMM kernel (the FFN core: its three
+    # per-launch roofline of the case's GEMM kernel (the FFN core: its two
     # kernels together, against the FP8 peak)
     sha = kernel_sources_sha()
     if kind == "masked":
