@@ -233,11 +233,10 @@ int swiglu_quantize_fp8(const void* H, int64_t ldh, void* Q, int64_t ldq, int16_
  *   H = m_grouped_gemm_fp8(A, W13)          bf16 [M_total][2*inter]
  *   (Y, sfy) = swiglu_quantize_fp8(H)       e4m3 [M_total][inter] + packed 1x128 scales
  *   D = m_grouped_gemm_fp8(Y, W2)           bf16 [M_total][hidden]
- * on `stream`, with the same expert row ranges (group_offsets, device int32 [G+1])
- * in both GEMMs.  When Y is 8-byte aligned and ldy a multiple of 8, the first two
- * steps are one launch: the up-projection applies SwiGLU and the requantisation to
- * each tile in its epilogue, with the same bits as the two calls, and H is not
- * written (it is still checked); otherwise three launches.
+ * as two launches on `stream`, with the same expert row ranges (group_offsets,
+ * device int32 [G+1]) in both GEMMs: the up-projection applies SwiGLU and the
+ * requantisation to each tile in its epilogue, with the same bits as the first two
+ * calls above, so H is not written (it stays in the signature and is still checked).
  *   A: e4m3 [M_total][lda] tokens, hidden wide; sfa packed [ceil(hidden/256)][ld_sfa].
  *   W13: e4m3 [G][2*inter][ldw13] (expert g at W13 + g*stride_w13 bytes; gate
  *        rows [0, inter), up rows [inter, 2*inter)); sfw13 packed int16
