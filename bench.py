@@ -343,9 +343,15 @@ def summarize(kind, r, steps):
     else:
         ach = r["flops"] / (mean_us * 1e-6) / 1e12
         out["roofline"] = {"bound": "mfma", "achieved": ach, "peak": PEAK[kind], "unit": "TFLOP/s"}
+    if kind == "moe_ffn":
+        # the call's two kernels: the up-projection (with its SwiGLU epilogue) and the
+        # down-projection
+        parts = [load_traffic(k, sha) for k in ("moe_ffn_up", "moe_ffn_down")]
+        traffic = None if None in parts else sum(parts)
+    else:
+        traffic = load_traffic(kind, sha)
     out["roofline"].update(kernel=KERNEL_NAME[kind], frac=ach / out["roofline"]["peak"],
-                           traffic=None if kind == "moe_ffn" else load_traffic(kind, sha),
-                           src_sha=sha)
+                           traffic=traffic, src_sha=sha)
     if "cold_us" in r:
         c = sorted(r["cold_us"])
         out["cold_l2_us_median"] = statistics.median(c)

@@ -30,6 +30,19 @@ def test_traffic_is_read_only_for_the_sources_it_was_taken_on():
     assert bench.load_traffic("no_such_case", ent["src_sha"]) is None
 
 
+def test_ffn_roofline_traffic_is_the_sum_of_its_two_kernels():
+    with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+        tab = json.load(f)
+    want = tab["moe_ffn_up"]["bytes_per_launch"] + tab["moe_ffn_down"]["bytes_per_launch"]
+    r = {"per_launch_us": [1400.0, 1410.0], "wall_s": 2.9e-3, "flops": 2.2e12,
+         "min_bytes": 3.4e9, "meta": {}}
+    out = bench.summarize("moe_ffn", r, 2)
+    if tab["moe_ffn_up"]["src_sha"] == bench.kernel_sources_sha():
+        assert out["roofline"]["traffic"] == want
+    else:
+        assert out["roofline"]["traffic"] is None
+
+
 def test_source_hash_ignores_comments_and_layout(tmp_path, monkeypatch):
     csrc = tmp_path / "block_scaled_precision_05_amd" / "csrc"
     csrc.mkdir(parents=True)
