@@ -196,6 +196,37 @@ def test_moe_ffn_odd_number_of_scale_blocks():
     _check_ffn(w, rows, "moe_ffn inter 384")
 
 
+def test_moe_ffn_ocp_mx_rule_matches_the_separate_steps():
+    """Both scale rules have their own fused epilogue: with rule ocp_mx the call's Y,
+    its scales and D must equal, bit for bit, the up-projection, swiglu_quantize_fp8
+    and the down-projection run one by one (each pinned to the oracle elsewhere)."""
+    _say("moe_ffn rule ocp_mx against the separate steps")
+    w = workloads.moe_ffn(35, device=DEV, hidden=512, inter=384, counts=[130, 0, 256, 37])
+    t = w.tensors
+    G, two_i, hidden = t["W13"].shape
+    inter = two_i // 2
+    M = t["A"].shape[0]
+    sfa = bsg.ensure_packed(t["sfa"], M, hidden // 128)
+    sfw13 = torch.stack([bsg.ensure_packed(x, (two_i + 127) // 128, hidden // 128) for x in t["sfw13"]])
+    sfw2 = torch.stack([bsg.ensure_packed(x, (hidden + 127) // 128, inter // 128) for x in t["sfw2"]])
+    H = torch.empty(M, two_i, dtype=torch.bfloat16, device=DEV)
+    Y = torch.empty(M, inter, dtype=torch.uint8, device=DEV)
+    sfy = torch.empty((inter // 128 + 1) // 2, M, dtype=torch.int16, device=DEV)
+    D = bsg.moe_ffn_fp8(t["A"], sfa, t["W13"], sfw13, t["W2"], sfw2, t["offsets"], rule="ocp_mx",
+                        workspace=(H, Y, sfy))
+    H1 = bsg.m_grouped_gemm_fp8(t["A"], sfa, t["W13"], sfw13, t["offsets"])
+    Y1, sf1 = bsg.swiglu_quantize_fp8(H1, inter, rule="ocp_mx")
+    D1 = bsg.m_grouped_gemm_fp8(Y1, sf1, t["W2"], sfw2, t["offsets"])
+    torch.cuda.synchronize()
+    off = t["offsets"].cpu().numpy()
+    rows = np.concatenate([np.arange(off[g], off[g + 1]) for g in range(len(off) - 1)])
+    assert np.array_equal(Y.cpu().numpy()[rows], Y1.view(torch.uint8).cpu().numpy()[rows])
+    assert np.array_equal(sfy.cpu().numpy()[:, rows], sf1.cpu().numpy()[:, rows])
+    got = D.view(torch.int16).cpu().numpy()[rows]
+    want = D1.view(torch.int16).cpu().numpy()[rows]
+    assert np.array_equal(got, want), f"{int((got != want).sum())} outputs of D differ"
+
+
 def test_moe_ffn_workload_sampled_rows():
     """The benchmark's FFN share (48 + 1 experts, hidden 7168, inter 2048) in the
     launch the benchmark times; the oracle computes 24 sampled rows in full."""
