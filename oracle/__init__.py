@@ -8,8 +8,8 @@ other; the only thing both sides see is the seeded input bytes.
 The arithmetic lives in ``oracle.c`` (plain C, fp64, no fast-math): exact decode
 of every element, exact scaling by powers of two, one fp64 dot product per output
 in plain k order.  This module only marshals numpy arrays into it and builds it
-with gcc.  ``oracle.exact`` holds an independent exact-rational brute force for
-tiny shapes.
+with gcc.  An independent exact-rational brute force for tiny shapes lives with
+the tests (``tests/exact.py``), which pin this package against it.
 
 ``oracle.quantize`` (numpy, fp64) holds the per-token quantiser: bf16 rows to
 e4m3 or e2m1 codes with UE8M0 block scales.
@@ -17,7 +17,7 @@ e4m3 or e2m1 codes with UE8M0 block scales.
 Parity status of each function (what pins it is in ``tests/test_oracle_pins.py``
 and ``tests/test_quantize_pins.py``):
   decoders, bf16 rounding, pack/unpack, dense BF16/FP8/FP4, grouped BF16/FP8/FP4,
-  masked grouped FP8, per-token quantisation: pinned.
+  masked grouped FP8, per-token quantisation, row norms (bf16, e4m3, e2m1): pinned.
 """
 from __future__ import annotations
 

@@ -382,6 +382,66 @@ def test_library_dgemm_special_case(orc):
 
 
 # ---------------------------------------------------------------------------
+# row norms: the denominators of every parity comparison
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("K", [8, 70, 1000])
+def test_row_norms_bf16_match_library_norm(orc, K):
+    """BF16 rows decoded by torch, normed by numpy; K need not be a multiple of
+    anything.  A padded row stride (lda > K) must not leak into the norm."""
+    r = _rng(41)
+    A = _bf16(r.standard_normal((37, K + 6)) * 2.0 ** r.integers(-20, 20, (37, 1)))
+    a = A[:, :K]
+    ref = np.linalg.norm(exact.dequant_bf16(a), axis=1)
+    assert np.allclose(orc.row_norms("bf16", a), ref, rtol=1e-13, atol=0)
+    rows = np.array([36, 0, 5])
+    assert np.allclose(orc.row_norms("bf16", a, rows=rows), ref[rows], rtol=1e-13, atol=0)
+
+
+def test_row_norms_bf16_closed_form(orc):
+    """All-ones rows have norm sqrt(K); a row of v's scaled by 2^s has |v| 2^s sqrt(K);
+    a zero row has norm 0."""
+    K = 1024
+    A = np.zeros((3, K), dtype=np.uint16)
+    A[0] = exact.bf16_bits(1.0)
+    A[1] = exact.bf16_bits(-0.75 * 2.0 ** -30)
+    n = orc.row_norms("bf16", A)
+    assert n[0] == 32.0 and n[1] == 0.75 * 2.0 ** -30 * 32.0 and n[2] == 0.0
+
+
+@pytest.mark.parametrize("K", [32, 96, 160, 224, 1056])
+def test_row_norms_e2m1_match_library_norm(orc, K):
+    """E2M1 rows with scale bytes spread far from 127, K a multiple of 32 but not of
+    64 (odd K-block count, so the last packed word has the 0x7F filler), and rows
+    stored wider than K/2 bytes: the K inference and the 32-element scale
+    granularity are both exercised."""
+    r = _rng(42)
+    rows, width = 23, K // 2 + 16
+    A = r.integers(0, 256, (rows, width), dtype=np.uint8)
+    sf = r.integers(100, 150, (rows, K // 32), dtype=np.uint8)
+    ref = np.linalg.norm(exact.dequant_e2m1(A[:, :K // 2], sf, K), axis=1)
+    got = orc.row_norms("e2m1", A, orc.pack_scales(sf), K=K)
+    assert np.allclose(got, ref, rtol=1e-13, atol=0)
+    # K inferred from the operand width when the stored row is exactly K/2 bytes
+    a = np.ascontiguousarray(A[:, :K // 2])
+    assert np.allclose(orc.row_norms("e2m1", a, orc.pack_scales(sf)), ref, rtol=1e-13, atol=0)
+
+
+def test_row_norms_e2m1_closed_form(orc):
+    """Code 0x2 (1.0) everywhere with one scale byte 127 + s per 32-block: the
+    squared norm is 32 * sum_b 4^s_b, exact in fp64.  Sign codes do not change it."""
+    K = 32 * 7
+    s = np.array([[0, 1, -1, 3, -4, 2, 0], [5, 5, 5, 5, 5, 5, 5]], dtype=np.int64)
+    codes = np.full((2, K), 0x2, dtype=np.uint8)
+    codes[1, 1::3] = 0xA                    # -1.0
+    A = _e2m1_pack(codes)
+    sf = (127 + s).astype(np.uint8)
+    n = orc.row_norms("e2m1", A, orc.pack_scales(sf), K=K)
+    want = np.sqrt(32.0 * np.sum(4.0 ** s, axis=1))
+    assert np.array_equal(n, want)
+
+
+# ---------------------------------------------------------------------------
 # invariants
 # ---------------------------------------------------------------------------
 
