@@ -35,6 +35,9 @@ Value recipes:
   * FP4: per 32-wide K-block, e = floor(log2(amax)) - 2 (the OCP MX rule, e2m1's
     largest exponent is 2); x / 2^e is rounded to nearest (ties to the even code)
     onto the e2m1 grid, saturating at 6.  An all-zero block gets e = 0.
+  * Expert weights are drawn a few experts at a time (one operand of c*N rows per
+    batch, cut into experts), so a workload costs a handful of device dispatches
+    rather than several per expert.
   * MoE routing: 16384 tokens x top-6 = 98304 assignments drawn multinomially
     over 256 experts with popularity p_r ~ r^-1.1 (rank r = 1..256), ranks mapped
     to expert ids by a seeded permutation; every count is padded up to a multiple
@@ -159,6 +162,44 @@ def pad_offsets(counts: torch.Tensor, align: int = 128) -> torch.Tensor:
     return off.to(torch.int32)
 
 
+def expert_weights(kind: str, G: int, N: int, K: int, g: torch.Generator, device,
+                   gran_mn: int = 128, max_elems: int = 1 << 31):
+    """G experts' operands [G][N][..] (and UE8M0 bytes [G][..][..]) drawn a few
+    experts at a time: each batch is one operand of c*N rows, cut into experts.
+    FP8 batches need N % gran_mn == 0 so that no scale block straddles two experts
+    (otherwise experts are drawn one by one)."""
+    per = max(1, min(G, max_elems // max(1, N * K)))
+    if kind == "fp8" and N % gran_mn:
+        per = 1
+    qs, sfs = [], []
+    for e0 in range(0, G, per):
+        c = min(per, G - e0)
+        if kind == "fp8":
+            q, sf = fp8_operand(c * N, K, gran_mn, g, device)
+            qs.append(q.view(c, N, K))
+            sfs.append(sf.view(c, -1, K // 128))
+        elif kind == "fp4":
+            q, sf = fp4_operand(c * N, K, g, device)
+            qs.append(q.view(c, N, K // 2))
+            sfs.append(sf.view(c, N, K // 32))
+        elif kind == "bf16":
+            qs.append(bf16_normal(c * N, K, g, device).view(c, N, K))
+        else:
+            raise ValueError(kind)
+    B = torch.cat(qs) if len(qs) > 1 else qs[0]
+    return B, (torch.cat(sfs) if len(sfs) > 1 else sfs[0]) if sfs else None
+
+
+def padded_rows_mask(offsets: torch.Tensor, counts: torch.Tensor, m_total: int) -> torch.Tensor:
+    """bool [m_total]: True for the first counts[g] rows of every expert's range
+    [off[g], off[g+1]), False for its padding rows."""
+    r = torch.arange(m_total, device=offsets.device, dtype=torch.int64)
+    off = offsets.to(torch.int64)
+    e = torch.searchsorted(off, r, right=True) - 1
+    e = e.clamp(0, counts.numel() - 1)
+    return (r - off[e]) < counts.to(off.device)[e]
+
+
 @dataclass
 class Workload:
     name: str
@@ -241,31 +282,16 @@ def grouped(G: int, N: int, K: int, seed: int, device="cpu", counts=None, name="
         raise ValueError(kind)
     A = A[:m_total]
     # zero the padding rows of every expert
-    valid = torch.zeros(m_total, dtype=torch.bool, device=device)
-    starts = off[:-1].to(torch.int64)
-    for e in range(G):
-        s = int(starts[e])
-        c = int(counts[e])
-        if c:
-            valid[s:s + c] = True
+    valid = padded_rows_mask(off, counts, m_total)
     A[~valid] = 0
     if sfa is not None:
         sfa = sfa[:m_total]
         sfa[~valid] = 127
-    Bs, sfbs = [], []
-    for _ in range(G):
-        if kind == "fp8":
-            b, sb = fp8_operand(N, K, 128, g, device)
-        elif kind == "fp4":
-            b, sb = fp4_operand(N, K, g, device)
-        else:
-            b, sb = bf16_normal(N, K, g, device), None
-        Bs.append(b)
-        sfbs.append(sb)
+    B, sfb = expert_weights(kind, G, N, K, g, device)
     w = Workload(name, "grouped_" + kind, m_total, N, K)
-    w.tensors.update(A=A.contiguous(), B=torch.stack(Bs), offsets=off, counts=counts)
+    w.tensors.update(A=A.contiguous(), B=B, offsets=off, counts=counts)
     if sfa is not None:
-        w.tensors.update(sfa=sfa.contiguous(), sfb=torch.stack(sfbs))
+        w.tensors.update(sfa=sfa.contiguous(), sfb=sfb)
     w.meta.update(seed=seed, G=G, useful_rows=int(counts.sum().item()), m_total=m_total,
                   routing=f"multinomial({tokens}x{topk}), zipf {zipf}, pad {align}")
     return w
@@ -282,13 +308,9 @@ def masked(seed: int, device="cpu", G: int = 48, cap: int = 512, N: int = 4096, 
     else:
         counts = torch.as_tensor(list(counts), dtype=torch.int64, device=device)
     A, sfa = fp8_operand(G * cap, K, 1, g, device)
-    Bs, sfbs = [], []
-    for _ in range(G):
-        b, sb = fp8_operand(N, K, 128, g, device)
-        Bs.append(b)
-        sfbs.append(sb)
+    B, sfb = expert_weights("fp8", G, N, K, g, device)
     w = Workload(name, "masked_fp8", G * cap, N, K)
-    w.tensors.update(A=A.view(G, cap, K), sfa=sfa, B=torch.stack(Bs), sfb=torch.stack(sfbs),
+    w.tensors.update(A=A.view(G, cap, K), sfa=sfa, B=B, sfb=sfb,
                      masked_m=counts.to(torch.int32))
     useful = int(counts.clamp(min=0, max=cap).sum().item())
     w.meta.update(seed=seed, G=G, cap=cap, useful_rows=useful,
@@ -316,25 +338,14 @@ def moe_ffn(seed: int, device="cpu", hidden: int = 7168, inter: int = 2048, expe
     m_total = int(off[-1].item())
     A, sfa = fp8_operand(max(m_total, 1), hidden, 1, g, device)
     A, sfa = A[:m_total], sfa[:m_total]
-    valid = torch.zeros(m_total, dtype=torch.bool, device=device)
-    for e in range(G):
-        s0, c = int(off[e]), int(counts[e])
-        if c:
-            valid[s0:s0 + c] = True
+    valid = padded_rows_mask(off, counts, m_total)
     A[~valid] = 0
     sfa[~valid] = 127
-    W13, s13, W2, s2 = [], [], [], []
-    for _ in range(G):
-        w, sw = fp8_operand(2 * inter, hidden, 128, g, device)
-        W13.append(w)
-        s13.append(sw)
-        w, sw = fp8_operand(hidden, inter, 128, g, device)
-        W2.append(w)
-        s2.append(sw)
+    W13, s13 = expert_weights("fp8", G, 2 * inter, hidden, g, device)
+    W2, s2 = expert_weights("fp8", G, hidden, inter, g, device)
     w = Workload(name, "moe_ffn", m_total, hidden, hidden)
-    w.tensors.update(A=A.contiguous(), sfa=sfa.contiguous(), W13=torch.stack(W13),
-                     sfw13=torch.stack(s13), W2=torch.stack(W2), sfw2=torch.stack(s2),
-                     offsets=off, counts=counts)
+    w.tensors.update(A=A.contiguous(), sfa=sfa.contiguous(), W13=W13, sfw13=s13, W2=W2,
+                     sfw2=s2, offsets=off, counts=counts)
     useful = int(counts.sum().item())
     w.meta.update(seed=seed, G=G, hidden=hidden, inter=inter, useful_rows=useful,
                   m_total=m_total,
