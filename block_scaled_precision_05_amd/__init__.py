@@ -312,28 +312,49 @@ def m_grouped_gemm_fp8_masked(A, sfa, B, sfb, masked_m, out=None, stream=None):
     return out
 
 
+# hipStreamLegacy: the legacy default stream as a non-NULL handle (the pack and
+# unpack entry points read a NULL stream as "host pointers").
+_HIP_STREAM_LEGACY = 1
+
+
+def _pack_stream(tensors, stream) -> int:
+    """NULL (host path) when every tensor lives in host memory; otherwise the
+    device stream, with the default stream passed as hipStreamLegacy."""
+    on_gpu = [t.is_cuda for t in tensors if t is not None]
+    if not any(on_gpu):
+        if stream is not None:
+            raise ValueError("host tensors are packed synchronously: pass no stream")
+        return 0
+    if not all(on_gpu):
+        raise ValueError("sf and the packed array must both live on the GPU or both on the host")
+    s = _stream(stream)
+    return s if s else _HIP_STREAM_LEGACY
+
+
 def pack_ue8m0_scales(sf: torch.Tensor, ld_packed: int | None = None, out=None, stream=None):
-    """uint8 (or float8_e8m0fnu) [mn, kb] -> packed int16 [ceil(kb/2), ld_packed]."""
-    _dev(sf, out)
+    """uint8 (or float8_e8m0fnu) [mn, kb] -> packed int16 [ceil(kb/2), ld_packed].
+    GPU tensors are packed by a kernel on ``stream``; host tensors on the calling
+    thread (the C entry point's NULL-stream path)."""
     sf = _bytes_u8(sf)
     mn, kb = sf.shape
     ldp = mn if ld_packed is None else int(ld_packed)
     if out is None:
         out = torch.empty(((kb + 1) // 2, ldp), dtype=torch.int16, device=sf.device)
+    st = _pack_stream((sf, out), stream)
     _check("pack_ue8m0_scales", lib().pack_ue8m0_scales(_ptr(sf), mn, kb, _mat(sf, "sf"),
-                                                        _ptr(out), _mat(out, "out"),
-                                                        _stream(stream)))
+                                                        _ptr(out), _mat(out, "out"), st))
     return out
 
 
 def unpack_ue8m0_scales(packed: torch.Tensor, mn: int, kb: int, out=None, stream=None):
-    """packed int16 [ceil(kb/2), >=mn] -> uint8 [mn, kb]."""
-    _dev(packed, out)
+    """packed int16 [ceil(kb/2), >=mn] -> uint8 [mn, kb] (on the GPU or, for host
+    tensors, on the calling thread)."""
     if out is None:
         out = torch.empty((mn, kb), dtype=torch.uint8, device=packed.device)
+    st = _pack_stream((packed, out), stream)
     _check("unpack_ue8m0_scales", lib().unpack_ue8m0_scales(_ptr(packed), mn, kb,
                                                             _packed(packed, "packed"), _ptr(out),
-                                                            _mat(out, "out"), _stream(stream)))
+                                                            _mat(out, "out"), st))
     return out
 
 
@@ -354,7 +375,7 @@ def ensure_packed(sf: torch.Tensor, mn: int, kb: int, stream=None) -> torch.Tens
         return sf
     if sf.dtype in (torch.uint8, torch.float8_e8m0fnu) and sf.dim() == 2 and \
             tuple(sf.shape) == (mn, kb):
-        return pack_ue8m0_scales(sf, stream=stream)
+        return pack_ue8m0_scales(sf, stream=stream if sf.is_cuda else None)
     raise TypeError(
         f"scales must be packed int16 [{(kb + 1) // 2}, >={mn}] or UE8M0 bytes [{mn}, {kb}]; "
         f"got {sf.dtype} {tuple(sf.shape)}")
@@ -420,8 +441,9 @@ def moe_ffn_fp8(A, sfa, W13, sfw13, W2, sfw2, offsets, rule: str = "ceil", out=N
     """MoE FFN core: grouped up-projection (W13 [G, 2*inter, hidden]), SwiGLU + FP8
     requantisation, grouped down-projection (W2 [G, hidden, inter]); A e4m3
     [M_total, hidden] with packed scales; offsets int32 [G+1] on the GPU.  Returns
-    D bf16 [M_total, hidden].  ``workspace`` may pass (H, Y, sfy) buffers; they are
-    allocated here otherwise."""
+    D bf16 [M_total, hidden].  ``workspace`` may pass the (Y, sfy) buffers (e4m3
+    uint8 [M_total, >=inter] and packed int16 [ceil(inter/256), >=M_total]); they
+    are allocated here otherwise.  The bf16 up-projection output H is never formed."""
     _dev(A, sfa, W13, sfw13, W2, sfw2, offsets, out)
     A, W13, W2 = _bytes_u8(A), _bytes_u8(W13), _bytes_u8(W2)
     if W13.dim() != 3 or W2.dim() != 3 or sfw13.dim() != 3 or sfw2.dim() != 3:
@@ -434,11 +456,10 @@ def moe_ffn_fp8(A, sfa, W13, sfw13, W2, sfw2, offsets, rule: str = "ceil", out=N
         raise ValueError("W2 must be [G, hidden, inter] for W13 [G, 2*inter, hidden]")
     M = A.shape[0]
     if workspace is None:
-        H = torch.empty((M, 2 * inter), dtype=torch.bfloat16, device=A.device)
         Y = torch.empty((M, inter), dtype=torch.uint8, device=A.device)
         sfy = torch.empty(((inter // 128 + 1) // 2, M), dtype=torch.int16, device=A.device)
     else:
-        H, Y, sfy = workspace
+        Y, sfy = workspace
     D = _out(out, M, hidden, A.device)
     for t, n in ((W13, "W13"), (W2, "W2"), (sfw13, "sfw13"), (sfw2, "sfw2")):
         if t.stride(2) != 1:
@@ -448,6 +469,6 @@ def moe_ffn_fp8(A, sfa, W13, sfw13, W2, sfw2, offsets, rule: str = "ceil", out=N
         _ptr(W13), W13.stride(1), W13.stride(0), _ptr(sfw13), sfw13.stride(1), sfw13.stride(0),
         _ptr(W2), W2.stride(1), W2.stride(0), _ptr(sfw2), sfw2.stride(1), sfw2.stride(0),
         _ptr(offsets), G, M, hidden, inter,
-        _ptr(H), _mat(H, "H"), _ptr(Y), _mat(_bytes_u8(Y), "Y"), _ptr(sfy), _packed(sfy, "sfy"),
+        0, 0, _ptr(Y), _mat(_bytes_u8(Y), "Y"), _ptr(sfy), _packed(sfy, "sfy"),
         _ptr(D), _mat(D, "out"), SCALE_RULES[rule], _stream(stream)))
     return D

@@ -486,12 +486,39 @@ static int launch_pack(bool unpack, const void* src, int64_t mn, int64_t kb, int
   return hipGetLastError() == hipSuccess ? BSG_OK : BSG_ERR_HIP;
 }
 
+// Host forms of the two kernels (stream == NULL: the caller's pointers are host
+// memory and the call returns when the work is done).  No HIP call is made, so
+// they also run where no GPU is present.  Same layout rule as the kernels.
+static void pack_host(const uint8_t* sf, int64_t mn, int64_t kb, int64_t ld_sf, int16_t* packed,
+                      int64_t ld_packed) {
+  for (int64_t kp = 0; kp < (kb + 1) / 2; ++kp)
+    for (int64_t r = 0; r < mn; ++r) {
+      const uint32_t lo = sf[r * ld_sf + 2 * kp];
+      const uint32_t hi = 2 * kp + 1 < kb ? sf[r * ld_sf + 2 * kp + 1] : 0x7Fu;
+      packed[kp * ld_packed + r] = (int16_t)(uint16_t)(lo | (hi << 8));
+    }
+}
+
+static void unpack_host(const int16_t* packed, int64_t mn, int64_t kb, int64_t ld_packed,
+                        uint8_t* sf, int64_t ld_sf) {
+  for (int64_t kp = 0; kp < (kb + 1) / 2; ++kp)
+    for (int64_t r = 0; r < mn; ++r) {
+      const uint32_t w = (uint16_t)packed[kp * ld_packed + r];
+      sf[r * ld_sf + 2 * kp] = (uint8_t)(w & 0xFF);
+      if (2 * kp + 1 < kb) sf[r * ld_sf + 2 * kp + 1] = (uint8_t)(w >> 8);
+    }
+}
+
 int pack_ue8m0_scales(const uint8_t* sf, int64_t mn, int64_t kb, int64_t ld_sf, int16_t* packed,
                       int64_t ld_packed, void* stream) {
   if (mn < 0 || kb < 0) return BSG_ERR_INVALID_ARG;
   if (mn == 0 || kb == 0) return BSG_OK;
   if (!sf || !packed || ld_sf < kb || ld_packed < mn) return BSG_ERR_INVALID_ARG;
   if ((uintptr_t)packed & 1) return BSG_ERR_MISALIGNED;
+  if (!stream) {
+    pack_host(sf, mn, kb, ld_sf, packed, ld_packed);
+    return BSG_OK;
+  }
   return launch_pack(false, sf, mn, kb, ld_sf, packed, ld_packed, stream);
 }
 
@@ -501,6 +528,10 @@ int unpack_ue8m0_scales(const int16_t* packed, int64_t mn, int64_t kb, int64_t l
   if (mn == 0 || kb == 0) return BSG_OK;
   if (!sf || !packed || ld_sf < kb || ld_packed < mn) return BSG_ERR_INVALID_ARG;
   if ((uintptr_t)packed & 1) return BSG_ERR_MISALIGNED;
+  if (!stream) {
+    unpack_host(packed, mn, kb, ld_packed, sf, ld_sf);
+    return BSG_OK;
+  }
   return launch_pack(true, packed, mn, kb, ld_packed, sf, ld_sf, stream);
 }
 

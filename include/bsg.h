@@ -32,9 +32,11 @@
  *    element (kp, mn) sits at kp*ld_sf + mn, its low byte is K-block 2kp and its
  *    high byte K-block 2kp+1 (0x7F when Kb is odd).  "Scale rows" (mn) are the
  *    rows of A, the 128-row blocks of B (FP8) or the rows of B (FP4).
- *  - Every pointer is a device pointer owned by the caller; the library allocates nothing, keeps no state between
- *    calls and never synchronises.  Work is enqueued on `stream` (a hipStream_t;
- *    NULL is the default stream) and is complete when the stream says so.
+ *  - Every pointer is a device pointer owned by the caller; the library allocates
+ *    nothing, keeps no state between calls and never synchronises.  Work is
+ *    enqueued on `stream` (a hipStream_t; NULL is the default stream) and is
+ *    complete when the stream says so.  The one exception is the scale
+ *    pack/unpack pair: there NULL means host pointers and a synchronous call.
  *  - Every call validates its arguments on the host before touching the GPU and
  *    returns a status code; nothing is launched when the status is not BSG_OK.
  *    A launch failure reported by the runtime returns BSG_ERR_HIP.
@@ -166,14 +168,30 @@ int m_grouped_gemm_fp8_masked(const void* A, int64_t lda, const int16_t* sfa, in
                               void* D, int64_t ldd, const int32_t* masked_m, int32_t G,
                               int64_t max_m, int64_t N, int64_t K, void* stream);
 
-/* Pack UE8M0 scales (device kernel on `stream`):
+/* Pack UE8M0 scales: the conversion half of the pages' reuse-or-convert scale
+ * helper, which passes scales through when they already have the packed layout
+ * and converts them otherwise (first page, "DeepGEMM-Ascend cobre quantas
+ * operacoes no Ascend 950?", section "Fatores de escala FP8 e o formato UE8M0
+ * no Ascend"):
  *   sf: uint8 [mn][ld_sf], K-blocks contiguous (kb of them per scale row)
- *   -> packed: int16 [ceil(kb/2)][ld_packed], MN-major, as described above.
- *   Requires ld_sf >= kb, ld_packed >= mn; device pointers. */
+ *   -> packed: int16 [ceil(kb/2)][ld_packed], MN-major, as described above
+ *      (columns mn .. ld_packed-1 are not written).
+ *   stream == NULL: sf and packed are HOST pointers; the work is done on the
+ *     calling thread before the call returns (no HIP call is made, so this also
+ *     works on a machine without a GPU).
+ *   stream != NULL: sf and packed are DEVICE pointers; a kernel is enqueued on
+ *     that hipStream_t.  To use the legacy default stream pass hipStreamLegacy
+ *     ((void*)1), since NULL selects the host path.
+ *   Requires ld_sf >= kb, ld_packed >= mn, packed 2-byte aligned; mn == 0 or
+ *   kb == 0 is a no-op.  Errors: BSG_ERR_INVALID_ARG (null pointer, negative size,
+ *   leading dimension too small), BSG_ERR_MISALIGNED, BSG_ERR_HIP (launch). */
 int pack_ue8m0_scales(const uint8_t* sf, int64_t mn, int64_t kb, int64_t ld_sf,
                       int16_t* packed, int64_t ld_packed, void* stream);
 
-/* Inverse of pack_ue8m0_scales (device kernel on `stream`). */
+/* Inverse of pack_ue8m0_scales, with the same stream rule (NULL: host pointers,
+ * synchronous; otherwise device pointers and a kernel on `stream`): packed int16
+ * [ceil(kb/2)][ld_packed] -> sf uint8 [mn][ld_sf]; the 0x7F filler byte of an odd
+ * kb is not written back.  Columns kb .. ld_sf-1 of sf are not written. */
 int unpack_ue8m0_scales(const int16_t* packed, int64_t mn, int64_t kb, int64_t ld_packed,
                         uint8_t* sf, int64_t ld_sf, void* stream);
 
@@ -236,19 +254,22 @@ int swiglu_quantize_fp8(const void* H, int64_t ldh, void* Q, int64_t ldq, int16_
  * as two launches on `stream`, with the same expert row ranges (group_offsets,
  * device int32 [G+1]) in both GEMMs: the up-projection applies SwiGLU and the
  * requantisation to each tile in its epilogue, with the same bits as the first two
- * calls above, so H is not written (it stays in the signature and is still checked).
+ * calls above, so H is never formed.  H may be NULL (then ldh is ignored); a
+ * non-NULL H is checked as that output would be but is not written.
  *   A: e4m3 [M_total][lda] tokens, hidden wide; sfa packed [ceil(hidden/256)][ld_sfa].
  *   W13: e4m3 [G][2*inter][ldw13] (expert g at W13 + g*stride_w13 bytes; gate
  *        rows [0, inter), up rows [inter, 2*inter)); sfw13 packed int16
  *        [G][ceil(hidden/256)][ld_sfw13 >= ceil(2*inter/128)], expert stride
  *        stride_sfw13 elements.
  *   W2: e4m3 [G][hidden][ldw2] (K = inter); sfw2 packed [G][ceil(inter/256)][ld_sfw2].
- *   H, Y, sfy: caller-owned workspace (the library allocates nothing), with
- *        ldh >= 2*inter, ldy >= inter, ld_sfy >= M_total.
+ *   Y, sfy: caller-owned workspace (the library allocates nothing), with
+ *        ldy >= inter, ld_sfy >= M_total (H: see above, ldh >= 2*inter).
  *   D: bf16 [M_total][ldd].  Rows outside [off[0], off[G]) of H, Y and D are not
  *   meaningful.  Every argument of all three steps is checked before the first
  *   launch; the requirements are those of the three calls above (hidden and inter
- *   multiples of 128). */
+ *   multiples of 128), and (inter + 128) * ldw13 < 2^31 (the up-projection reads a
+ *   tile's gate rows and the matching up rows through one record of 32-bit byte
+ *   offsets); larger shapes return BSG_ERR_UNSUPPORTED_SHAPE. */
 int moe_ffn_fp8(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
                 const void* W13, int64_t ldw13, int64_t stride_w13, const int16_t* sfw13,
                 int64_t ld_sfw13, int64_t stride_sfw13,

@@ -269,3 +269,91 @@ def test_binding_refuses_cpu_tensors():
     a = torch.zeros(4, 8, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         bsg.gemm_bf16(a, a)
+
+
+# ---------------------------------------------------------------------------
+# scale pack / unpack on the host (stream == NULL): no GPU involved
+# ---------------------------------------------------------------------------
+
+def _np_ptr(a):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+@pytest.mark.parametrize("mn,kb,ld_sf,ldp", [(1, 1, 1, 1), (5, 3, 3, 5), (7, 3, 8, 12),
+                                             (300, 57, 60, 320), (1024, 32, 32, 1024),
+                                             (33, 1, 4, 33)])
+def test_host_pack_unpack_match_oracle_bit_for_bit(mn, kb, ld_sf, ldp):
+    """pack_ue8m0_scales(..., NULL) packs host memory on the calling thread: every
+    byte value, odd kb (0x7F filler), ld_sf > kb and ld_packed > mn; the padding
+    columns of both arrays stay untouched.  unpack inverts it."""
+    import numpy as np
+    import oracle
+    L = bsg.lib()
+    r = np.random.default_rng(mn * 1000 + kb)
+    sf = r.integers(0, 256, (mn, ld_sf), dtype=np.uint8)
+    sf[0, :min(kb, 256)] = np.arange(min(kb, 256), dtype=np.uint8)
+    packed = np.full(((kb + 1) // 2, ldp), 0x5A5A, dtype=np.int16)
+    assert L.pack_ue8m0_scales(_np_ptr(sf), mn, kb, ld_sf, _np_ptr(packed), ldp, None) == bsg.BSG_OK
+    want = oracle.pack_scales(np.ascontiguousarray(sf[:, :kb]), ld_packed=ldp)
+    assert np.array_equal(packed[:, :mn], want[:, :mn])
+    assert np.all(packed[:, mn:] == 0x5A5A)
+    back = np.full((mn, kb + 3), 0xEE, dtype=np.uint8)
+    assert L.unpack_ue8m0_scales(_np_ptr(packed), mn, kb, ldp, _np_ptr(back), kb + 3,
+                                 None) == bsg.BSG_OK
+    assert np.array_equal(back[:, :kb], sf[:, :kb])
+    assert np.all(back[:, kb:] == 0xEE)
+    assert np.array_equal(back[:, :kb], oracle.unpack_scales(packed, mn, kb))
+
+
+def test_host_pack_worked_example():
+    """The worked example of the packed layout (tests/golden/pack_example.txt)."""
+    import numpy as np
+    L = bsg.lib()
+    sf = np.array([[0x77, 0x83], [0x7F, 0x80]], dtype=np.uint8)
+    packed = np.zeros((1, 2), dtype=np.int16)
+    assert L.pack_ue8m0_scales(_np_ptr(sf), 2, 2, 2, _np_ptr(packed), 2, None) == bsg.BSG_OK
+    assert packed.view(np.uint16).tolist() == [[0x8377, 0x807F]]
+
+
+def test_binding_packs_host_tensors_on_the_host():
+    import numpy as np
+    import torch
+    import oracle
+    sf = torch.randint(0, 256, (40, 7), dtype=torch.uint8)
+    p = bsg.pack_ue8m0_scales(sf)
+    assert not p.is_cuda and p.shape == (4, 40)
+    assert np.array_equal(p.numpy(), oracle.pack_scales(sf.numpy()))
+    assert torch.equal(bsg.unpack_ue8m0_scales(p, 40, 7), sf)
+    assert bsg.ensure_packed(sf, 40, 7).shape == (4, 40)
+    with pytest.raises(ValueError):
+        bsg.pack_ue8m0_scales(sf, stream=5)
+
+
+def test_moe_ffn_accepts_no_h_and_bounds_the_w13_record():
+    """H may be NULL (it is never written); (inter + 128) * ldw13 >= 2^31 is refused
+    before anything is launched (fake, never dereferenced pointers)."""
+    f = bsg.lib().moe_ffn_fp8
+    hidden, inter, G, M = 512, 256, 4, 256
+    args = [P, hidden, P2, M, 0x100000, hidden, 2 * inter * hidden, P2, 4, 4 * 2,
+            0x400000, inter, hidden * inter, P2, 4, 4, P2, G, M, hidden, inter,
+            0, 0, 0x900000, inter, 0xA00000, M, 0xB00001, hidden, 0, None]
+    # H = NULL passes every check up to the last one (an odd D address)
+    assert f(*args) == bsg.BSG_ERR_MISALIGNED
+    bad = list(args); bad[21] = 0x800000; bad[22] = 2 * inter - 8   # given H: checked
+    assert f(*bad) == bsg.BSG_ERR_INVALID_ARG
+    bad = list(args); bad[21] = 0x800001; bad[22] = 2 * inter       # odd H address
+    assert f(*bad) == bsg.BSG_ERR_MISALIGNED
+    empty = list(args); empty[18] = 0                               # M_total = 0: no-op
+    assert f(*empty) == bsg.BSG_OK
+    # hidden 16384, inter 131072: 131200 rows of 16384 bytes pass 2^31
+    big = list(args)
+    big[1] = big[5] = big[19] = 16384
+    big[20] = big[11] = big[24] = 131072
+    big[6] = 2 * 131072 * 16384
+    big[12] = 16384 * 131072
+    big[26] = 256
+    big[27], big[28] = 0xB00000, 16384
+    big[8], big[9] = 2048, 2048 * 64
+    big[14], big[15] = 128, 128 * 512
+    assert f(*big) == bsg.BSG_ERR_UNSUPPORTED_SHAPE
+
