@@ -302,6 +302,57 @@ static int swiglu_launch(const void* H, int64_t ldh, void* Q, int64_t ldq, int16
   return hipGetLastError() == hipSuccess ? BSG_OK : BSG_ERR_HIP;
 }
 
+// ---------------------------------------------------------------------------
+// MoE FFN core: argument checks and the two launches, shared by moe_ffn_fp8
+// (its workspace comes from the caller).
+// ---------------------------------------------------------------------------
+static int ffn_check(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
+                     const void* W13, int64_t ldw13, int64_t stride_w13, const int16_t* sfw13,
+                     int64_t ld_sfw13, int64_t stride_sfw13, const void* W2, int64_t ldw2,
+                     int64_t stride_w2, const int16_t* sfw2, int64_t ld_sfw2, int64_t stride_sfw2,
+                     const int32_t* group_offsets, int32_t G, int64_t M_total, int64_t hidden,
+                     int64_t inter, const void* H, int64_t ldh, const void* Y, int64_t ldy,
+                     const int16_t* sfy, int64_t ld_sfy, const void* D, int64_t ldd, int32_t rule) {
+  if (inter < 0 || hidden < 0) return BSG_ERR_INVALID_ARG;
+  // H is never written (the up-projection's epilogue forms Y directly), so it may be
+  // NULL; when given it is checked as the up-projection's output would be.  The
+  // checks below take a stand-in that is never dereferenced: a 16-byte aligned
+  // non-null address with the smallest valid leading dimension.
+  const void* Hc = H ? H : (const void*)(uintptr_t)256;
+  const int64_t ldhc = H ? ldh : 2 * inter;
+  int st = bsg::grouped_fp8_check(A, lda, sfa, ld_sfa, W13, ldw13, stride_w13, sfw13, ld_sfw13,
+                                  stride_sfw13, Hc, ldhc, group_offsets, G, M_total, 2 * inter,
+                                  hidden);
+  if (st != BSG_OK) return st;
+  st = swiglu_check(Hc, ldhc, Y, ldy, sfy, ld_sfy, M_total, inter, rule);
+  if (st != BSG_OK) return st;
+  // The up-projection tile reads gate rows n0 .. n0+127 and the matching up rows
+  // inter + n0 .. of W13 through one buffer record of 32-bit byte offsets, so
+  // inter + 128 rows of W13 must stay below 2^31 bytes.
+  if ((inter + 128) * ldw13 >= (int64_t(1) << 31)) return BSG_ERR_UNSUPPORTED_SHAPE;
+  return bsg::grouped_fp8_check(Y, ldy, sfy, ld_sfy, W2, ldw2, stride_w2, sfw2, ld_sfw2,
+                                stride_sfw2, D, ldd, group_offsets, G, M_total, hidden, inter);
+}
+
+// Arguments checked; M_total, G, hidden and inter all positive.
+static int ffn_launch(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
+                      const void* W13, int64_t ldw13, int64_t stride_w13, const int16_t* sfw13,
+                      int64_t ld_sfw13, int64_t stride_sfw13, const void* W2, int64_t ldw2,
+                      int64_t stride_w2, const int16_t* sfw2, int64_t ld_sfw2, int64_t stride_sfw2,
+                      const int32_t* group_offsets, int32_t G, int64_t M_total, int64_t hidden,
+                      int64_t inter, void* Y, int64_t ldy, int16_t* sfy, int64_t ld_sfy, void* D,
+                      int64_t ldd, int32_t rule, void* stream) {
+  // The up-projection applies SwiGLU and the requantisation in its epilogue (the
+  // checks guarantee what that needs: inter a multiple of 128, Y 8-byte aligned
+  // with ldy a multiple of 8); H is not formed.
+  int st = bsg::grouped_fp8_swiglu(A, lda, sfa, ld_sfa, W13, ldw13, stride_w13, sfw13, ld_sfw13,
+                                   stride_sfw13, group_offsets, G, M_total, hidden, inter, Y, ldy,
+                                   sfy, ld_sfy, rule, stream);
+  if (st != BSG_OK) return st;
+  return m_grouped_gemm_fp8(Y, ldy, sfy, ld_sfy, W2, ldw2, stride_w2, sfw2, ld_sfw2, stride_sfw2,
+                            D, ldd, group_offsets, G, M_total, hidden, inter, stream);
+}
+
 }  // namespace bsg_quant
 
 using namespace bsg_quant;
@@ -337,27 +388,15 @@ int moe_ffn_fp8(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
                 const int32_t* group_offsets, int32_t G, int64_t M_total, int64_t hidden,
                 int64_t inter, void* H, int64_t ldh, void* Y, int64_t ldy, int16_t* sfy,
                 int64_t ld_sfy, void* D, int64_t ldd, int32_t rule, void* stream) {
-  if (inter < 0 || hidden < 0) return BSG_ERR_INVALID_ARG;
   // every check before the first launch, so a bad argument launches nothing
-  int st = bsg::grouped_fp8_check(A, lda, sfa, ld_sfa, W13, ldw13, stride_w13, sfw13, ld_sfw13,
-                                  stride_sfw13, H, ldh, group_offsets, G, M_total, 2 * inter,
-                                  hidden);
-  if (st != BSG_OK) return st;
-  st = swiglu_check(H, ldh, Y, ldy, sfy, ld_sfy, M_total, inter, rule);
-  if (st != BSG_OK) return st;
-  st = bsg::grouped_fp8_check(Y, ldy, sfy, ld_sfy, W2, ldw2, stride_w2, sfw2, ld_sfw2, stride_sfw2,
-                              D, ldd, group_offsets, G, M_total, hidden, inter);
-  if (st != BSG_OK) return st;
-  if (M_total == 0 || G == 0 || hidden == 0 || inter == 0) return BSG_OK;
-  // The up-projection applies SwiGLU and the requantisation in its epilogue (the
-  // checks above guarantee what that needs: inter a multiple of 128, Y 8-byte aligned
-  // with ldy a multiple of 8); H is not written.
-  st = bsg::grouped_fp8_swiglu(A, lda, sfa, ld_sfa, W13, ldw13, stride_w13, sfw13, ld_sfw13,
-                               stride_sfw13, group_offsets, G, M_total, hidden, inter, Y, ldy, sfy,
-                               ld_sfy, rule, stream);
-  if (st != BSG_OK) return st;
-  return m_grouped_gemm_fp8(Y, ldy, sfy, ld_sfy, W2, ldw2, stride_w2, sfw2, ld_sfw2, stride_sfw2,
-                            D, ldd, group_offsets, G, M_total, hidden, inter, stream);
+  const int st = ffn_check(A, lda, sfa, ld_sfa, W13, ldw13, stride_w13, sfw13, ld_sfw13,
+                           stride_sfw13, W2, ldw2, stride_w2, sfw2, ld_sfw2, stride_sfw2,
+                           group_offsets, G, M_total, hidden, inter, H, ldh, Y, ldy, sfy, ld_sfy,
+                           D, ldd, rule);
+  if (st != BSG_OK || M_total == 0 || G == 0 || hidden == 0 || inter == 0) return st;
+  return ffn_launch(A, lda, sfa, ld_sfa, W13, ldw13, stride_w13, sfw13, ld_sfw13, stride_sfw13,
+                    W2, ldw2, stride_w2, sfw2, ld_sfw2, stride_sfw2, group_offsets, G, M_total,
+                    hidden, inter, Y, ldy, sfy, ld_sfy, D, ldd, rule, stream);
 }
 
 }  // extern "C"
