@@ -638,10 +638,19 @@ void gemm_kernel(const GemmArgs args) {
       // operands and their outputs are never stored.
       constexpr int NSB = T::NSB;   // B scale words per lane per packed row
       const int nrow0 = n0 + wn * T::TN;   // first B row of this wave (uniform)
+      // The records end after the last packed row's scale rows; with the wide scale
+      // loads (SV) they extend to the next multiple of four rows, which a wide load
+      // of the last row group reads whole (the launcher takes SV only when the
+      // leading dimension is a multiple of 4, so those words lie inside the array):
+      // a record ending at row M would drop the valid words of a dword that
+      // straddles it.
+      constexpr bool SV_B = SV && T::PERM_B;
+      const int a_rows = SV ? (args.M + 3) & ~3 : args.M;
+      const int b_rows = SV_B ? (args.sfb_rows + 3) & ~3 : args.sfb_rows;
       const __amdgpu_buffer_rsrc_t rsa = make_rsrc(
-          args.sfa, (uint32_t)(2 * ((int64_t)(args.kp_count - 1) * args.ld_sfa + args.M)));
+          args.sfa, (uint32_t)(2 * ((int64_t)(args.kp_count - 1) * args.ld_sfa + a_rows)));
       const __amdgpu_buffer_rsrc_t rsb = make_rsrc(
-          sfb, (uint32_t)(2 * ((int64_t)(args.kp_count - 1) * args.ld_sfb + args.sfb_rows)));
+          sfb, (uint32_t)(2 * ((int64_t)(args.kp_count - 1) * args.ld_sfb + b_rows)));
       // (FP4: the lane's fragment rows are 4*l32 .. 4*l32 + 3 of the wave block)
       uint32_t sa_voff = 2u * (uint32_t)(m0 + wm * T::TM + (T::PERM_A ? 4 * l32 : l32));
       asm volatile("" : "+v"(sa_voff));

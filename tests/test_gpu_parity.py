@@ -549,6 +549,31 @@ def test_fp4_scale_load_variants_agree():
     assert_parity(outs[0], ref, na, nb, what="fp4 512x384x1024 (8-byte scale loads)")
 
 
+@pytest.mark.parametrize("kind,M,N", [("fp8", 423, 300), ("fp8", 421, 256),
+                                      ("fp4", 423, 301), ("fp4", 512, 302), ("fp4", 257, 255)])
+def test_wide_scale_loads_with_rows_not_a_multiple_of_four(kind, M, N):
+    """Packed scale arrays whose leading dimension is a multiple of 4 (so the wide
+    8- and 4-byte scale loads are taken) while the scale rows are not: the last
+    row group's load must still deliver the words of the rows that exist, in every
+    packed row including the last one."""
+    K = 1024 if kind == "fp8" else 448
+    _say(f"{kind} {M}x{N}x{K} with wide scale loads over ragged scale rows")
+    w = workloads.dense(kind, M, N, K, 81 + M + N, device="cpu")
+    t = {k: v.to(DEV) for k, v in w.tensors.items()}
+    pad = lambda n: (n + 3) // 4 * 4
+    if kind == "fp8":
+        sfa = bsg.pack_ue8m0_scales(t["sfa"], ld_packed=pad(M))[:, :M]
+        sfb = bsg.ensure_packed(t["sfb"], (N + 127) // 128, K // 128)
+        D = bsg.gemm_fp8_blockscaled(t["A"], sfa, t["B"], sfb)
+    else:
+        sfa = bsg.pack_ue8m0_scales(t["sfa"], ld_packed=pad(M))[:, :M]
+        sfb = bsg.pack_ue8m0_scales(t["sfb"], ld_packed=pad(N))[:, :N]
+        D = bsg.gemm_fp4_blockscaled(t["A"], sfa, t["B"], sfb, K=K)
+    torch.cuda.synchronize()
+    ref, na, nb = run_oracle(kind, host(w.tensors), K)
+    assert_parity(gpu_bits(D), ref, na, nb, what=f"{kind} {M}x{N}x{K}, scale rows padded to 4")
+
+
 def test_fp8_scale_load_variants_agree():
     """FP8 fetches a lane's four A scale words with one 8-byte load when sfa
     allows it and with 2-byte loads otherwise: same bits, dense and grouped."""
