@@ -5,14 +5,17 @@
 * The whole FFN (grouped up-projection, SwiGLU + requantisation, grouped
   down-projection) on the structured case of moe_cases, where every step is
   exact: D bit-exact against the closed form and the oracle.
-* The whole FFN on random data against the oracle's chain.  Y is not unique: a
-  code whose exact value sits at a rounding boundary (of y, or of the bf16 H it
-  comes from) may round either way, and each such code moves D[i][j] by at most
-  one e4m3 step of y_k (<= 2^-3 |y_k|) times |w_jk|.  So an output passes when its
-  normalised error is within the GEMM bound 1e-3, or within 1e-3 plus the effect
-  of two such steps at the row's largest |y_k w_jk|.  One flip reaches every output
-  of its row, so it is the rows that need the allowance that must stay rare (at
-  most 5%).  H is checked to the GEMM bound as well."""
+* The whole FFN on random data against the oracle's chain.  Y is not unique: the
+  GPU's H is an fp32 sum rounded to bf16, and where it lands one bf16 step away
+  from the oracle's H (allowed by the GEMM bound, which H is checked to), y moves
+  by about 2^-8 relative and a Y code near a rounding boundary goes to its
+  neighbour.  So Y is compared with the oracle's element by element: every
+  difference must be at most one e4m3 step of the two values (or the smallest
+  step of the larger block scale), and few elements may differ (under 1%).  Each
+  output D[i][j] then passes when its normalised error is within the GEMM bound
+  1e-3 plus the effect of those differences, sum_k |dY_ik| |w_jk| / (|y_i| |w_j|),
+  plus one bf16 step of the output (each side rounds once to bf16).
+  H is checked to the GEMM bound as well."""
 import numpy as np
 import pytest
 import torch
@@ -86,11 +89,10 @@ def _ffn_gpu(w):
     sfa = bsg.ensure_packed(t["sfa"], M, hidden // 128)
     sfw13 = torch.stack([bsg.ensure_packed(x, (two_i + 127) // 128, hidden // 128) for x in t["sfw13"]])
     sfw2 = torch.stack([bsg.ensure_packed(x, (hidden + 127) // 128, inter // 128) for x in t["sfw2"]])
-    H = torch.empty(M, two_i, dtype=torch.bfloat16, device=DEV)
     Y = torch.empty(M, inter, dtype=torch.uint8, device=DEV)
     sfy = torch.empty((inter // 128 + 1) // 2, M, dtype=torch.int16, device=DEV)
     D = bsg.moe_ffn_fp8(t["A"], sfa, t["W13"], sfw13, t["W2"], sfw2, t["offsets"],
-                        workspace=(H, Y, sfy))
+                        workspace=(Y, sfy))
     # With inter a multiple of 128 the up-projection applies SwiGLU and the FP8
     # requantisation in its epilogue and H stays unwritten.  The same GEMM run on its
     # own gives H; quantising that H must reproduce the call's Y and scales bit for bit.
@@ -105,36 +107,48 @@ def _ffn_gpu(w):
     s_got = sfy.cpu().numpy()[:, rows]
     s_want = sfq.cpu().numpy()[:, rows]
     assert np.array_equal(s_got, s_want), "moe_ffn: Y scales differ from quantising H"
-    return D, H
+    return D, H, Y, sfy
 
 
-def _ffn_compare(got_bits, ref, y_deq, w_deq, what):
-    """Normalised error with the requantisation allowance (module docstring)."""
+def _ffn_compare(got_bits, ref, y_orc, y_gpu, s_max, w_deq, what):
+    """D against the oracle, with the allowance that the actual differences between
+    the GPU's Y and the oracle's Y (dequantised, rows x inter) explain."""
     from parity import bf16_bits_to_f64
     got = bf16_bits_to_f64(got_bits)
     ref_b = bf16_bits_to_f64(oracle.bf16_rne(ref))
-    na = np.linalg.norm(y_deq, axis=1)
+    dy = np.abs(y_gpu - y_orc)
+    step = 2.0 ** -3 * np.maximum(np.abs(y_gpu), np.abs(y_orc)) + 2.0 ** -9 * s_max
+    assert np.all(dy <= step), f"{what}: a Y element differs by more than one e4m3 step"
+    n_diff = int(np.count_nonzero(dy))
+    assert n_diff <= max(2, dy.size // 100), f"{what}: {n_diff} of {dy.size} Y elements differ"
+    na = np.linalg.norm(y_orc, axis=1)
     nb = np.linalg.norm(w_deq, axis=1)
     den = na[:, None] * nb[None, :]
+    allow = (dy @ np.abs(w_deq).T) / np.where(den == 0, 1.0, den)
     with np.errstate(divide="ignore", invalid="ignore"):
         err = np.abs(got - ref_b) / den
     err = np.where(den == 0, np.where(got == ref_b, 0.0, np.inf), err)
-    over = np.argwhere(err > 1e-3)
-    for i, j in over:
-        allow = 2 * 2.0 ** -3 * np.max(np.abs(y_deq[i]) * np.abs(w_deq[j])) / den[i, j]
-        assert err[i, j] <= 1e-3 + allow, f"{what}: ({i},{j}) err {err[i, j]:.3e} > {1e-3 + allow:.3e}"
-    rows_allow = np.unique(over[:, 0]).size if over.size else 0
+    # both sides end in one bf16 rounding: up to one bf16 step of the larger value
+    mag = np.maximum(np.abs(got), np.abs(ref_b))
+    ulp = np.where(mag > 0, 2.0 ** (np.floor(np.log2(np.where(mag > 0, mag, 1.0))) - 7), 0.0)
+    allow = allow + ulp / np.where(den == 0, 1.0, den)
+    over = err > 1e-3 + allow
+    if np.any(over):
+        i, j = np.argwhere(over)[0]
+        raise AssertionError(f"{what}: {int(over.sum())} outputs beyond 1e-3 + allowance, e.g. "
+                             f"({i},{j}) err {err[i, j]:.3e} allowance {allow[i, j]:.3e} "
+                             f"got {got[i, j]!r} want {ref_b[i, j]!r}")
+    need = int(np.sum(err > 1e-3))
     print(f"[parity] {what}: max normalised error {float(np.max(err)):.3e} over {err.size}, "
-          f"{len(over)} outputs in {rows_allow} rows within the requantisation allowance", flush=True)
-    # a requantisation flip touches every output of its row; flips themselves are rare
-    assert rows_allow <= max(2, err.shape[0] // 20)
+          f"{n_diff} of {dy.size} Y elements one step off the oracle's, {need} outputs "
+          f"within the allowance they explain", flush=True)
 
 
 def _check_ffn(w, rows, what):
     t = {k: v.cpu() if torch.is_tensor(v) else v for k, v in w.tensors.items()}
     G, two_i, hidden = t["W13"].shape
     inter = two_i // 2
-    D, H = _ffn_gpu(w)
+    D, H, Y, sfy = _ffn_gpu(w)
     A = t["A"].numpy()
     sfa = oracle.pack_scales(t["sfa"].numpy())
     W13 = t["W13"].numpy()
@@ -144,11 +158,15 @@ def _check_ffn(w, rows, what):
     off = t["offsets"].numpy()
     res = moe.moe_ffn(A, sfa, W13, sfw13, W2, sfw2, off, rows)
     got = gpu_bits(D)[rows]
-    y_deq = exact.dequant_e4m3(res["Y"], res["sfy"], 1, 128)
+    y_orc = exact.dequant_e4m3(res["Y"], res["sfy"], 1, 128)
+    sf_gpu = oracle.unpack_scales(sfy.cpu().numpy(), sfy.shape[1], inter // 128)[rows]
+    y_gpu = exact.dequant_e4m3(Y.view(torch.uint8).cpu().numpy()[rows], sf_gpu, 1, 128)
+    s_max = np.repeat(2.0 ** (np.maximum(res["sfy"], sf_gpu).astype(np.float64) - 127), 128, axis=1)
     for g in np.unique(res["expert"]):
         sel = np.nonzero(res["expert"] == g)[0]
         w_deq = exact.dequant_e4m3(W2[g], t["sfw2"].numpy()[g], 128, 128)
-        _ffn_compare(got[sel], res["D"][sel], y_deq[sel], w_deq, f"{what} D expert {g}")
+        _ffn_compare(got[sel], res["D"][sel], y_orc[sel], y_gpu[sel], s_max[sel], w_deq,
+                     f"{what} D expert {g}")
     # the up-projection, to the GEMM bound
     na_h = oracle.row_norms("e4m3", A, sfa, rows=rows)
     h_gpu = gpu_bits(H)[rows]
@@ -168,7 +186,7 @@ def test_moe_ffn_structured_exact():
 
     class W:
         tensors = tens
-    D, H = _ffn_gpu(W)
+    D, H, _, _ = _ffn_gpu(W)
     got = gpu_bits(D)
     want = oracle.bf16_rne(c["D"])
     assert np.array_equal(got, want), f"{int((got != want).sum())} outputs differ"
@@ -196,12 +214,17 @@ def test_moe_ffn_odd_number_of_scale_blocks():
     _check_ffn(w, rows, "moe_ffn inter 384")
 
 
-def test_moe_ffn_ocp_mx_rule_matches_the_separate_steps():
+@pytest.mark.parametrize("align", [128, 1])
+def test_moe_ffn_ocp_mx_rule_matches_the_separate_steps(align):
     """Both scale rules have their own fused epilogue: with rule ocp_mx the call's Y,
     its scales and D must equal, bit for bit, the up-projection, swiglu_quantize_fp8
-    and the down-projection run one by one (each pinned to the oracle elsewhere)."""
-    _say("moe_ffn rule ocp_mx against the separate steps")
-    w = workloads.moe_ffn(35, device=DEV, hidden=512, inter=384, counts=[130, 0, 256, 37])
+    and the down-projection run one by one (each pinned to the oracle elsewhere).
+    Rows padded to 128 give M_total = 640, a multiple of 4, so the packed A scales
+    take the 8-byte load variant of the fused kernel; unpadded rows give 423 and
+    the 2-byte variant."""
+    _say(f"moe_ffn rule ocp_mx against the separate steps, row alignment {align}")
+    w = workloads.moe_ffn(35, device=DEV, hidden=512, inter=384, counts=[130, 0, 256, 37],
+                          align=align)
     t = w.tensors
     G, two_i, hidden = t["W13"].shape
     inter = two_i // 2
@@ -209,11 +232,11 @@ def test_moe_ffn_ocp_mx_rule_matches_the_separate_steps():
     sfa = bsg.ensure_packed(t["sfa"], M, hidden // 128)
     sfw13 = torch.stack([bsg.ensure_packed(x, (two_i + 127) // 128, hidden // 128) for x in t["sfw13"]])
     sfw2 = torch.stack([bsg.ensure_packed(x, (hidden + 127) // 128, inter // 128) for x in t["sfw2"]])
-    H = torch.empty(M, two_i, dtype=torch.bfloat16, device=DEV)
+    assert M == (640 if align == 128 else 423)
     Y = torch.empty(M, inter, dtype=torch.uint8, device=DEV)
     sfy = torch.empty((inter // 128 + 1) // 2, M, dtype=torch.int16, device=DEV)
     D = bsg.moe_ffn_fp8(t["A"], sfa, t["W13"], sfw13, t["W2"], sfw2, t["offsets"], rule="ocp_mx",
-                        workspace=(H, Y, sfy))
+                        workspace=(Y, sfy))
     H1 = bsg.m_grouped_gemm_fp8(t["A"], sfa, t["W13"], sfw13, t["offsets"])
     Y1, sf1 = bsg.swiglu_quantize_fp8(H1, inter, rule="ocp_mx")
     D1 = bsg.m_grouped_gemm_fp8(Y1, sf1, t["W2"], sfw2, t["offsets"])
