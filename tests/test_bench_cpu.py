@@ -82,3 +82,35 @@ def test_reported_kernel_names_match_the_launch(case, kind, K):
     kind_id, ns, koff = int(args[0]), int(args[6]), int(args[10])
     assert kind_id == {"bf16": 0, "fp8": 1, "fp4": 2}[kind]
     assert koff == _leading_dead(_stages(kind, K), ns)
+
+
+def test_headline_is_the_cold_median_and_warm_is_reported_beside():
+    r = {"per_launch_us": [900.0, 1000.0, 1100.0], "wall_s": 4e-3,
+         "warm_us": [700.0, 800.0, 750.0], "warm_wall_s": 2.3e-3,
+         "flops": 1e12, "min_bytes": 4e8, "meta": {}}
+    out = bench.summarize("bf16", r, 3)
+    assert out["tflops"] == pytest.approx(1e12 / 1000e-6 / 1e12)
+    assert out["ms_per_call"] == pytest.approx(1.0)
+    assert out["warm"]["tflops"] == pytest.approx(1e12 / 750e-6 / 1e12)
+    # the roofline takes the mean cold launch
+    assert out["roofline"]["achieved"] == pytest.approx(1e12 / 1000e-6 / 1e12)
+    assert out["roofline"]["frac"] == pytest.approx(out["roofline"]["achieved"] / 2500.0)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8", "fp4", "grouped"])
+def test_cpu_sample_times_the_oracle_on_the_case_inputs(kind):
+    from block_scaled_precision_05_amd import workloads
+    if kind == "grouped":
+        w = workloads.grouped(4, 256, 256, 7, device="cpu", counts=[40, 0, 300, 5])
+    else:
+        w = workloads.dense(kind, 64, 256, 256, 7, device="cpu")
+    r = bench.cpu_sample(kind, w, 0.2)
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOPS" and r["value"] > 0
+    assert r["cores"] >= 1 and "rows 0.." in r["sample"]
+    if kind == "grouped":
+        assert "expert 2 (300 rows)" in r["sample"]
+
+
+def test_host_info_names_cores_and_model():
+    h = bench.host_info()
+    assert h["nproc"] >= 1 and h["usable_cpus"] >= 1
