@@ -18,6 +18,7 @@ if ``libbsg.so`` is missing or cannot be loaded, every call raises.
     Q, P = quantize_fp4_per_token(X)            # bf16 [M,K] -> e2m1 (2/byte) + packed 1x32 scales
     Q, P = swiglu_quantize_fp8(H, inter)        # silu(H[:, :I]) * H[:, I:2I] -> e4m3 + scales
     D = moe_ffn_fp8(A, sfa, W13, sfw13, W2, sfw2, offsets)   # grouped up, SwiGLU, grouped down
+    moe_ffn_fp8_noalloc(A, sfa, W13, sfw13, W2, sfw2, offsets, out=D)   # no workspace, no allocation
 """
 from __future__ import annotations
 
@@ -68,6 +69,11 @@ EXPORTS = {
                     _vp, _i64, _i64, _vp, _i64, _i64,
                     _vp, _i32, _i64, _i64, _i64,
                     _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i32, _vp],
+    "moe_ffn_fp8_noalloc": [_vp, _i64, _vp, _i64,
+                            _vp, _i64, _i64, _vp, _i64, _i64,
+                            _vp, _i64, _i64, _vp, _i64, _i64,
+                            _vp, _i32, _i64, _i64, _i64,
+                            _vp, _i64, _i32, _vp],
 }
 
 
@@ -472,3 +478,30 @@ def moe_ffn_fp8(A, sfa, W13, sfw13, W2, sfw2, offsets, rule: str = "ceil", out=N
         0, 0, _ptr(Y), _mat(_bytes_u8(Y), "Y"), _ptr(sfy), _packed(sfy, "sfy"),
         _ptr(D), _mat(D, "out"), SCALE_RULES[rule], _stream(stream)))
     return D
+
+
+def moe_ffn_fp8_noalloc(A, sfa, W13, sfw13, W2, sfw2, offsets, out, rule: str = "ceil",
+                        stream=None):
+    """moe_ffn_fp8 without a workspace: the library keeps Y and its scales in a fixed
+    64 MiB device array (one per GPU), so the call allocates nothing; ``out`` (bf16
+    [M_total, hidden]) must be given.  Calls that overlap on one GPU race on that
+    array."""
+    _dev(A, sfa, W13, sfw13, W2, sfw2, offsets, out)
+    A, W13, W2 = _bytes_u8(A), _bytes_u8(W13), _bytes_u8(W2)
+    if W13.dim() != 3 or W2.dim() != 3 or sfw13.dim() != 3 or sfw2.dim() != 3:
+        raise ValueError("W13, W2 and their scales must be [G, rows, cols]")
+    _offsets_check(offsets, W13.shape[0])
+    G, two_i, hidden = W13.shape
+    M = A.shape[0]
+    if out.dtype != torch.bfloat16 or out.shape[0] < M or out.shape[1] < hidden:
+        raise ValueError("out must be a bfloat16 tensor of at least [M_total, hidden]")
+    for t, n in ((W13, "W13"), (W2, "W2"), (sfw13, "sfw13"), (sfw2, "sfw2")):
+        if t.stride(2) != 1:
+            raise ValueError(f"{n} must be contiguous along its last dimension")
+    _check("moe_ffn_fp8_noalloc", lib().moe_ffn_fp8_noalloc(
+        _ptr(A), _mat(A, "A"), _ptr(sfa), _packed(sfa, "sfa"),
+        _ptr(W13), W13.stride(1), W13.stride(0), _ptr(sfw13), sfw13.stride(1), sfw13.stride(0),
+        _ptr(W2), W2.stride(1), W2.stride(0), _ptr(sfw2), sfw2.stride(1), sfw2.stride(0),
+        _ptr(offsets), G, M, hidden, two_i // 2, _ptr(out), _mat(out, "out"),
+        SCALE_RULES[rule], _stream(stream)))
+    return out

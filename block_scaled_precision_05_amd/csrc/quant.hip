@@ -29,6 +29,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/bsg.h"
 #include "internal.h"
 #include "quant_math.h"
@@ -304,7 +306,7 @@ static int swiglu_launch(const void* H, int64_t ldh, void* Q, int64_t ldq, int16
 
 // ---------------------------------------------------------------------------
 // MoE FFN core: argument checks and the two launches, shared by moe_ffn_fp8
-// (its workspace comes from the caller).
+// (caller's workspace) and moe_ffn_fp8_noalloc (the library's scratch array).
 // ---------------------------------------------------------------------------
 static int ffn_check(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
                      const void* W13, int64_t ldw13, int64_t stride_w13, const int16_t* sfw13,
@@ -353,6 +355,30 @@ static int ffn_launch(const void* A, int64_t lda, const int16_t* sfa, int64_t ld
                             D, ldd, group_offsets, G, M_total, hidden, inter, stream);
 }
 
+// Scratch memory of moe_ffn_fp8_noalloc: the requantised intermediate Y and its
+// packed scales live here instead of in caller-provided buffers.  Every GPU the
+// library runs on holds its own copy for the life of the process.  Host code never
+// uses the array's name as an address: each device's copy is located once, with
+// that device current, and the address kept per device.
+constexpr size_t kFfnScratchBytes = size_t(64) << 20;
+__device__ __align__(256) uint8_t scratch[kFfnScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64];
+
+static int ffn_scratch(uint8_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return BSG_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BSG_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = (uint8_t*)g_scratch_ptr[dev];
+  return BSG_OK;
+}
+
 }  // namespace bsg_quant
 
 using namespace bsg_quant;
@@ -397,6 +423,39 @@ int moe_ffn_fp8(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
   return ffn_launch(A, lda, sfa, ld_sfa, W13, ldw13, stride_w13, sfw13, ld_sfw13, stride_sfw13,
                     W2, ldw2, stride_w2, sfw2, ld_sfw2, stride_sfw2, group_offsets, G, M_total,
                     hidden, inter, Y, ldy, sfy, ld_sfy, D, ldd, rule, stream);
+}
+
+int moe_ffn_fp8_noalloc(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
+                        const void* W13, int64_t ldw13, int64_t stride_w13, const int16_t* sfw13,
+                        int64_t ld_sfw13, int64_t stride_sfw13,
+                        const void* W2, int64_t ldw2, int64_t stride_w2, const int16_t* sfw2,
+                        int64_t ld_sfw2, int64_t stride_sfw2,
+                        const int32_t* group_offsets, int32_t G, int64_t M_total, int64_t hidden,
+                        int64_t inter, void* D, int64_t ldd, int32_t rule, void* stream) {
+  if (M_total < 0 || inter < 0 || hidden < 0) return BSG_ERR_INVALID_ARG;
+  // Y [M_total][inter] at the start of the scratch array, its packed scales
+  // [ceil(inter/256)][ld_sfy] at the next 256-byte boundary; ld_sfy a multiple of
+  // 4 so the down-projection takes the 8-byte scale loads.
+  const int64_t ldy = inter, ld_sfy = (M_total + 3) / 4 * 4;
+  const int64_t y_bytes = (M_total * inter + 255) / 256 * 256;
+  const int64_t s_bytes = (inter / 128 + 1) / 2 * ld_sfy * 2;
+  if (M_total > INT32_MAX || inter > INT32_MAX || y_bytes + s_bytes > (int64_t)kFfnScratchBytes)
+    return BSG_ERR_UNSUPPORTED_SHAPE;
+  // The checks see stand-in workspace addresses with the scratch array's alignment;
+  // nothing is dereferenced before the real address is known.
+  uint8_t* const y_dummy = (uint8_t*)(uintptr_t)256;
+  int st = ffn_check(A, lda, sfa, ld_sfa, W13, ldw13, stride_w13, sfw13, ld_sfw13, stride_sfw13,
+                     W2, ldw2, stride_w2, sfw2, ld_sfw2, stride_sfw2, group_offsets, G, M_total,
+                     hidden, inter, nullptr, 0, y_dummy, ldy, (int16_t*)(y_dummy + y_bytes),
+                     ld_sfy, D, ldd, rule);
+  if (st != BSG_OK || M_total == 0 || G == 0 || hidden == 0 || inter == 0) return st;
+  uint8_t* base = nullptr;
+  st = ffn_scratch(&base);
+  if (st != BSG_OK) return st;
+  return ffn_launch(A, lda, sfa, ld_sfa, W13, ldw13, stride_w13, sfw13, ld_sfw13, stride_sfw13,
+                    W2, ldw2, stride_w2, sfw2, ld_sfw2, stride_sfw2, group_offsets, G, M_total,
+                    hidden, inter, base, ldy, (int16_t*)(base + y_bytes), ld_sfy, D, ldd, rule,
+                    stream);
 }
 
 }  // extern "C"

@@ -279,6 +279,32 @@ int moe_ffn_fp8(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
                 int64_t inter, void* H, int64_t ldh, void* Y, int64_t ldy, int16_t* sfy,
                 int64_t ld_sfy, void* D, int64_t ldd, int32_t rule, void* stream);
 
+/* MoE FFN core that allocates nothing and takes no workspace: for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It computes exactly what moe_ffn_fp8 computes,
+ * with the same kernels and the same bits, but keeps the requantised intermediate
+ * Y (e4m3 [M_total][inter]) and its packed scales in a fixed device array inside
+ * the library (64 MiB on every GPU the library runs on, held until the process
+ * ends) instead of in caller buffers.
+ *   Arguments: as moe_ffn_fp8 without H, Y and sfy.
+ *   Limit: M_total * inter (rounded up to 256) + ceil(inter/256) * 2 * M_total
+ *   (M_total rounded up to 4) bytes must fit 64 MiB, else BSG_ERR_UNSUPPORTED_SHAPE
+ *   before anything runs (the one-GPU share of the 384-expert MoE step, 28 672
+ *   rows at inter 2048, takes 59 MB).
+ *   All calls on one GPU share that GPU's array, which keeps the last call's
+ *   contents: calls that overlap on one GPU (two streams, or two threads) race on
+ *   it and give wrong results; serialise them.  Nothing in the array needs to start
+ *   at any value (every byte read is written earlier in the same call).
+ *   The first call on a device looks the array up (hipGetSymbolAddress, no
+ *   allocation); a failure there returns BSG_ERR_HIP. */
+int moe_ffn_fp8_noalloc(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
+                        const void* W13, int64_t ldw13, int64_t stride_w13, const int16_t* sfw13,
+                        int64_t ld_sfw13, int64_t stride_sfw13,
+                        const void* W2, int64_t ldw2, int64_t stride_w2, const int16_t* sfw2,
+                        int64_t ld_sfw2, int64_t stride_sfw2,
+                        const int32_t* group_offsets, int32_t G, int64_t M_total, int64_t hidden,
+                        int64_t inter, void* D, int64_t ldd, int32_t rule, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -357,3 +357,20 @@ def test_moe_ffn_accepts_no_h_and_bounds_the_w13_record():
     big[14], big[15] = 128, 128 * 512
     assert f(*big) == bsg.BSG_ERR_UNSUPPORTED_SHAPE
 
+
+def test_moe_ffn_noalloc_refuses_what_exceeds_its_scratch():
+    """M_total * inter beyond the 64 MiB scratch array is refused before any HIP
+    call (fake, never dereferenced pointers); so are the usual bad arguments."""
+    f = bsg.lib().moe_ffn_fp8_noalloc
+    hidden, inter, G = 7168, 2048, 4
+    M = 40000                                   # 40000 * 2048 bytes > 64 MiB
+    args = [P, hidden, P2, M, 0x100000, hidden, 2 * inter * hidden, P2, 32, 56 * 32,
+            0x400000, inter, hidden * inter, P2, 56, 8 * 56, P2, G, M, hidden, inter,
+            0xB00000, hidden, 0, None]
+    assert f(*args) == bsg.BSG_ERR_UNSUPPORTED_SHAPE
+    small = list(args); small[3] = small[18] = 1000; small[22] = hidden - 8   # ldd < hidden
+    assert f(*small) == bsg.BSG_ERR_INVALID_ARG
+    small = list(args); small[3] = small[18] = 1000; small[23] = 7            # bad rule
+    assert f(*small) == bsg.BSG_ERR_INVALID_ARG
+    empty = list(args); empty[18] = 0                                         # M_total = 0
+    assert f(*empty) == bsg.BSG_OK
