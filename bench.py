@@ -2,7 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
                     [--dtypes bf16,fp8,fp4,grouped,grouped_bf16,grouped_fp4,quant_fp8,
-                              quant_fp4,quant_fp8_moe,moe_ffn,masked]
+                              quant_fp4,quant_fp8_moe,moe_ffn,masked,mqa_prefill_fp8,
+                              mqa_prefill_fp4,mqa_decode_fp8,mqa_decode_fp4]
 
 Workload: D = A * B^T at M=4096, N=7168, K=16384, the dense shape the pages time
 (431 TFLOPS BF16 on the other accelerator: "DeepSeek lanza kernels de DeepGEMM
@@ -38,6 +39,11 @@ The masked M-grouped FP8 GEMM runs a decode-sized case: 48 local experts of
 384, capacity 512 rows, N=4096, K=7168, counts from 4096 tokens top-6; it is
 bound by reading the experts' weights, so GB/s is reported beside TFLOPS.
 
+The MQA logits kernels (64 heads of 128, FP8 and FP4) run a prefill of one
+4096-token sequence with causal windows (TFLOPS of the scores' dot products
+against the dtype's MFMA peak) and a decode of 128 requests over 32768-token
+contexts (GB/s against HBM: each request streams its own keys).
+
 `cpu_baseline` times the CPU oracle (plain C, fp64, every host thread) on a
 bounded row sample of the BF16 case's own inputs; `per_config` adds the FP8, FP4
 and grouped FP8 cases, and `host` the core count and CPU model.
@@ -61,7 +67,12 @@ METRIC = "TFLOPS and % of MI355X dense MFMA peak, GEMM 4096×7168×16384 per dty
 
 # MI355X published dense MFMA peaks (TFLOP/s).
 PEAK = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0, "grouped": 5000.0, "moe_ffn": 5000.0,
-        "masked": 5000.0, "grouped_bf16": 2500.0, "grouped_fp4": 10100.0}
+        "masked": 5000.0, "grouped_bf16": 2500.0, "grouped_fp4": 10100.0,
+        "mqa_prefill_fp8": 5000.0, "mqa_prefill_fp4": 10100.0, "mqa_decode_fp8": 5000.0,
+        "mqa_decode_fp4": 10100.0}
+# Cases bound by HBM (their weights or keys stream once): roofline in GB/s.
+HBM_KINDS = ("masked", "mqa_decode_fp8", "mqa_decode_fp4")
+MQA_KINDS = ("mqa_prefill_fp8", "mqa_prefill_fp4", "mqa_decode_fp8", "mqa_decode_fp4")
 # MI355X published HBM3E bandwidth (GB/s): the bound of the quantisers.
 HBM_PEAK_GBS = 8000.0
 QUANT_KINDS = ("quant_fp8", "quant_fp4", "quant_fp8_moe")
@@ -82,6 +93,10 @@ KERNEL_NAME = {
     "masked": "gemm_kernel<1, 128, 256, 1, 4, 64, 6, 1, true, 1, 0, 0>",
     "grouped_bf16": "gemm_kernel<0, 256, 256, 2, 4, 64, 5, 1, true, 0, 6, 0>",
     "grouped_fp4": "gemm_kernel<2, 256, 256, 2, 4, 64, 5, 1, true, 1, 4, 0>",
+    "mqa_prefill_fp8": "mqa_logits_kernel<0, 2>",
+    "mqa_prefill_fp4": "mqa_logits_kernel<4, 2>",
+    "mqa_decode_fp8": "mqa_logits_kernel<0, 2>",
+    "mqa_decode_fp4": "mqa_logits_kernel<4, 2>",
 }
 
 
@@ -94,6 +109,7 @@ def log(msg):
 SOURCES = {
     "gemm": ("gemm_kernel.h", "configs.h", "quant_math.h"),
     "quant": ("quant.hip", "quant_math.h"),
+    "mqa": ("mqa.hip",),
 }
 
 
@@ -137,7 +153,7 @@ def make_case(kind, dev):
     name = {"bf16": "bf16_large", "fp8": "fp8_large", "fp4": "fp4_large",
             "grouped": "moe_fp8", "quant_fp8": "act_large", "quant_fp4": "act_large",
             "quant_fp8_moe": "act_moe", "moe_ffn": "moe_ffn", "masked": "masked_fp8",
-            "grouped_bf16": "moe_bf16", "grouped_fp4": "moe_fp4"}[kind]
+            "grouped_bf16": "moe_bf16", "grouped_fp4": "moe_fp4"}.get(kind, kind)
     w = workloads.make(name, device=dev)
     t = w.tensors
     M, N, K = w.M, w.N, w.K
@@ -165,6 +181,28 @@ def make_case(kind, dev):
                 "bytes_per_call": nbytes}
         meta.update({"M": M, "K": K})
         return call, 0.0, nbytes, meta, None
+    if kind in MQA_KINDS:
+        fmt = kind.rsplit("_", 1)[1]
+        m = w.meta
+        T, S, H = t["W"].shape[0], m["S"], m["H"]
+        sfq = bsg.ensure_packed(t["sfq"], t["sfq"].shape[0], t["sfq"].shape[1])
+        sfk = bsg.ensure_packed(t["sfk"], t["sfk"].shape[0], t["sfk"].shape[1])
+        L = torch.empty(T, S, dtype=torch.float32, device=dev)
+        call = lambda: bsg.mqa_logits(fmt, t["Q"], sfq, t["K"], sfk, t["W"], t["ks"], t["ke"], S,
+                                      q_per_group=m["q_per_group"], group_rows=m["group_rows"],
+                                      out=L)
+        row = t["Q"].shape[1]
+        # queries, their weights and all logits once; keys once per group for
+        # prefill (one sequence, shared by every query), once per window key for
+        # decode (each request reads its own context)
+        keys = S if m["mode"] == "prefill" else m["valid_pairs"]
+        nbytes = (T * H * row + 2 * sfq.numel() + 4 * T * H + 4 * T * S
+                  + keys * (row + 2 * sfk.shape[0]))
+        meta = {"mode": m["mode"], "queries": T, "keys": S, "heads": H, "head_dim": m["D"],
+                "windows": m["windows"], "window_pairs": m["valid_pairs"], "bytes_per_call": nbytes,
+                "flops_note": "2*H*D per (query, window key): the scores' dot products; the "
+                              "weighted max-sum adds 2*H more on the vector units"}
+        return call, w.flops, nbytes, meta, None
     if kind in ("grouped_bf16", "grouped_fp4"):
         A, B, off = t["A"], t["B"], t["offsets"]
         G = B.shape[0]
@@ -392,13 +430,13 @@ def summarize(kind, r, steps):
         out["warm"] = dict(warm, tflops=r["flops"] / (warm["us_median"] * 1e-6) / 1e12,
                            frac_of_peak=r["flops"] / (warm["us_median"] * 1e-6) / 1e12 / PEAK[kind],
                            wall_ms_per_call=r["warm_wall_s"] * 1e3 / steps)
-    if kind == "masked":
+    if kind in HBM_KINDS:
         out["gb_per_s"] = r["min_bytes"] / (med * 1e-6) / 1e9
         out["frac_of_hbm_peak"] = out["gb_per_s"] / HBM_PEAK_GBS
     # per-launch roofline of the case's GEMM kernel over the timed region (the FFN
     # core: its two kernels together, against the FP8 peak)
-    sha = kernel_sources_sha()
-    if kind == "masked":
+    sha = kernel_sources_sha("mqa" if kind in MQA_KINDS else "gemm")
+    if kind in HBM_KINDS:
         ach = r["min_bytes"] / (mean_us * 1e-6) / 1e9
         out["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     else:
@@ -466,7 +504,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--dtypes",
                     default="bf16,fp8,fp4,grouped,grouped_bf16,grouped_fp4,quant_fp8,quant_fp4,"
-                            "quant_fp8_moe,moe_ffn,masked")
+                            "quant_fp8_moe,moe_ffn,masked,mqa_prefill_fp8,mqa_prefill_fp4,"
+                            "mqa_decode_fp8,mqa_decode_fp4")
     ap.add_argument("--cpu-budget", type=float, default=24.0,
                     help="seconds of oracle time for cpu_baseline, shared by the BF16, FP8, FP4 "
                          "and grouped cases (0 disables it)")

@@ -19,6 +19,7 @@ if ``libbsg.so`` is missing or cannot be loaded, every call raises.
     Q, P = swiglu_quantize_fp8(H, inter)        # silu(H[:, :I]) * H[:, I:2I] -> e4m3 + scales
     D = moe_ffn_fp8(A, sfa, W13, sfw13, W2, sfw2, offsets)   # grouped up, SwiGLU, grouped down
     moe_ffn_fp8_noalloc(A, sfa, W13, sfw13, W2, sfw2, offsets, out=D)   # no workspace, no allocation
+    L = mqa_logits(fmt, Q, sfq, K, sfk, W, ks, ke, S)  # sum_h w * max(0, q_h . k) in key windows
 """
 from __future__ import annotations
 
@@ -69,6 +70,10 @@ EXPORTS = {
                     _vp, _i64, _i64, _vp, _i64, _i64,
                     _vp, _i32, _i64, _i64, _i64,
                     _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i32, _vp],
+    "mqa_logits_fp8": [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64,
+                       _i64, _i64, _i32, _i64, _i64, _vp],
+    "mqa_logits_fp4": [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64,
+                       _i64, _i64, _i32, _i64, _i64, _vp],
     "moe_ffn_fp8_noalloc": [_vp, _i64, _vp, _i64,
                             _vp, _i64, _i64, _vp, _i64, _i64,
                             _vp, _i64, _i64, _vp, _i64, _i64,
@@ -504,4 +509,32 @@ def moe_ffn_fp8_noalloc(A, sfa, W13, sfw13, W2, sfw2, offsets, out, rule: str = 
         _ptr(W2), W2.stride(1), W2.stride(0), _ptr(sfw2), sfw2.stride(1), sfw2.stride(0),
         _ptr(offsets), G, M, hidden, two_i // 2, _ptr(out), _mat(out, "out"),
         SCALE_RULES[rule], _stream(stream)))
+    return out
+
+
+def mqa_logits(fmt: str, Q, sfq, K, sfk, W, ks, ke, S: int, q_per_group: int | None = None,
+               group_rows: int = 0, out=None, stream=None):
+    """MQA logits (fmt "fp8" or "fp4"): L[t][s] = sum_h W[t][h] * max(0, q[t][h] . k[s])
+    for ks[t] <= s < ke[t], -inf for the other s < S.  Q: codes [T*H, 128] (fp8) or
+    [T*H, 64] (fp4, two per byte) with packed scales sfq over its rows; K: codes over
+    the key rows with packed scales sfk; W float32 [T, H]; ks, ke int32 [T] on the GPU.
+    Query t reads key group t // q_per_group (default: one group), whose key s is
+    row g * group_rows + s of K.  Returns float32 [T, S]."""
+    _dev(Q, sfq, K, sfk, W, ks, ke, out)
+    if fmt not in ("fp8", "fp4"):
+        raise ValueError("fmt must be 'fp8' or 'fp4'")
+    Q, K = _bytes_u8(Q), _bytes_u8(K)
+    if W.dtype != torch.float32 or ks.dtype != torch.int32 or ke.dtype != torch.int32:
+        raise TypeError("W must be float32 and ks, ke int32")
+    T, H = W.shape
+    if Q.shape[0] != T * H:
+        raise ValueError("Q must hold T*H rows")
+    per = T if q_per_group is None else int(q_per_group)
+    if out is None:
+        out = torch.empty((T, S), dtype=torch.float32, device=Q.device)
+    fn = lib().mqa_logits_fp8 if fmt == "fp8" else lib().mqa_logits_fp4
+    _check("mqa_logits_" + fmt, fn(
+        _ptr(Q), _mat(Q, "Q"), _ptr(sfq), _packed(sfq, "sfq"), _ptr(K), _mat(K, "K"), _ptr(sfk),
+        _packed(sfk, "sfk"), _ptr(W), _mat(W, "W"), _ptr(ks), _ptr(ke), _ptr(out), _mat(out, "out"),
+        T, S, H, max(per, 1), int(group_rows), _stream(stream)))
     return out

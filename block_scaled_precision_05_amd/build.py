@@ -8,7 +8,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libbsg.so")
-SOURCES = [os.path.join(HERE, "csrc", "api.hip"), os.path.join(HERE, "csrc", "quant.hip")]
+SOURCES = [os.path.join(HERE, "csrc", "api.hip"), os.path.join(HERE, "csrc", "quant.hip"),
+           os.path.join(HERE, "csrc", "mqa.hip")]
 HEADERS = [os.path.join(HERE, "csrc", h) for h in ("gemm_kernel.h", "configs.h", "internal.h",
                                                        "quant_math.h")] + \
     [os.path.join(ROOT, "include", "bsg.h")]

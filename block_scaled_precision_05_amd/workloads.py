@@ -24,6 +24,9 @@ para calculo e comunicacao de IA", section "Resultados de kernel e comunicacao")
   act_moe       bf16 activations 16384x7168 (the MoE tokens), to be quantised
   masked_fp8    masked M-grouped FP8 (decode): 48 local experts of 384 (EP8),
                 capacity 512 rows each, N=4096, K=7168, 4096 tokens top-6
+  mqa_*         MQA logits (64 heads of 128): prefill of one 4096-token sequence
+                (causal) and decode of 128 requests over 32768-token contexts, FP8
+                and FP4
   moe_ffn       MoE FFN core on one GPU's share of the pages' fused MoE case:
                 384 experts over EP8 -> 48 local experts plus the shared expert,
                 16384 tokens top-6, hidden 7168, intermediate 2048
@@ -219,6 +222,10 @@ class Workload:
             return 2.0 * float(self.meta["useful_rows"]) * self.N * self.K
         if self.kind == "moe_ffn":
             return float(self.meta["useful_flops"])
+        if self.kind.startswith("mqa_"):
+            # the scores' dot products over the window pairs (the weighted max-sum
+            # adds 2 flops per head and pair on top: counted separately)
+            return 2.0 * float(self.meta["valid_pairs"]) * self.meta["H"] * self.meta["D"]
         return 2.0 * self.M * self.N * self.K
 
 
@@ -235,6 +242,12 @@ SHAPES = {
     "act_moe": ("act", 16384, None, 7168, 1008),
     "moe_ffn": ("moe_ffn", None, None, None, 1009),
     "masked_fp8": ("masked_fp8", None, 4096, 7168, 1010),
+    # MQA logits (H = 64 heads of 128): prefill of one 4096-token sequence, causal;
+    # decode of 128 requests with 32768-token contexts
+    "mqa_prefill_fp8": ("mqa_fp8_prefill", 4096, 4096, 128, 1013),
+    "mqa_prefill_fp4": ("mqa_fp4_prefill", 4096, 4096, 128, 1014),
+    "mqa_decode_fp8": ("mqa_fp8_decode", 128, 32768, 128, 1015),
+    "mqa_decode_fp4": ("mqa_fp4_decode", 128, 32768, 128, 1016),
 }
 
 
@@ -355,6 +368,46 @@ def moe_ffn(seed: int, device="cpu", hidden: int = 7168, inter: int = 2048, expe
     return w
 
 
+def mqa(fmt: str, mode: str, seed: int, device="cpu", T: int = 4096, S: int = 4096, H: int = 64,
+        ctx=None, name: str = "custom"):
+    """Inputs of the MQA logits kernel (head dimension 128).  fmt "fp8" or "fp4";
+    mode "prefill": T query tokens of one sequence over its S = T keys, causal
+    windows [0, t+1); mode "decode": T requests with one query each over their own
+    S-key context (key group per request), windows [0, ctx_t) with ctx_t drawn
+    uniformly in [S/2, S] unless ``ctx`` gives them.  q and k rows follow the GEMM
+    operand recipes (FP8: one UE8M0 scale per 128-element row, e ~ U{-8..4}; FP4:
+    the OCP MX rule per 32), w ~ N(0,1) in fp32."""
+    g = _gen(device, seed)
+    D = 128
+    groups = 1 if mode == "prefill" else T
+    k_rows = groups * S
+    if fmt == "fp8":
+        Q, sfq = fp8_operand(T * H, D, 1, g, device)
+        K, sfk = fp8_operand(k_rows, D, 1, g, device)
+    else:
+        Q, sfq = fp4_operand(T * H, D, g, device)
+        K, sfk = fp4_operand(k_rows, D, g, device)
+    W = torch.randn(T, H, generator=g, device=device, dtype=torch.float32)
+    t = torch.arange(T, device=device, dtype=torch.int64)
+    if mode == "prefill":
+        ks = torch.zeros(T, dtype=torch.int32, device=device)
+        ke = (t + 1).clamp(max=S).to(torch.int32)
+        per, grows = T, 0
+    else:
+        if ctx is None:
+            ctx = torch.randint(S // 2, S + 1, (T,), generator=g, device=device)
+        ks = torch.zeros(T, dtype=torch.int32, device=device)
+        ke = torch.as_tensor(ctx, device=device).to(torch.int32)
+        per, grows = 1, S
+    w = Workload(name, "mqa_" + fmt, T, S, D)
+    w.tensors.update(Q=Q, sfq=sfq, K=K, sfk=sfk, W=W, ks=ks, ke=ke)
+    valid = int((ke.to(torch.int64) - ks.to(torch.int64)).clamp(min=0).sum().item())
+    w.meta.update(seed=seed, mode=mode, H=H, D=D, S=S, q_per_group=per, group_rows=grows,
+                  k_rows=k_rows, valid_pairs=valid,
+                  windows="causal [0, t+1)" if mode == "prefill" else "[0, ctx), ctx ~ U[S/2, S]")
+    return w
+
+
 def make(name: str, device="cpu", seed: int | None = None) -> Workload:
     """One of the named workloads in ``SHAPES``."""
     kind, M, N, K, default_seed = SHAPES[name]
@@ -365,6 +418,9 @@ def make(name: str, device="cpu", seed: int | None = None) -> Workload:
         w = moe_ffn(seed, device=device, name=name)
     elif kind == "masked_fp8":
         w = masked(seed, device=device, N=N, K=K, name=name)
+    elif kind.startswith("mqa_"):
+        _, fmt, mode = kind.split("_")
+        w = mqa(fmt, mode, seed, device=device, T=M, S=N, name=name)
     elif kind == "act":
         w = Workload(name, "act", M, 0, K)
         w.tensors["X"] = activations(M, K, seed, device=device)

@@ -279,6 +279,46 @@ int moe_ffn_fp8(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
                 int64_t inter, void* H, int64_t ldh, void* Y, int64_t ldy, int16_t* sfy,
                 int64_t ld_sfy, void* D, int64_t ldd, int32_t rule, void* stream);
 
+/* MQA logits, FP8 and FP4 (the pages list "MQA logits" among the library's
+ * kernels: attention scores of multi-query attention on the DeepSeek Lightning
+ * Indexer path, with FP8 and FP4 prefill and decode cases; first page,
+ * "DeepGEMM-Ascend cobre quantas operacoes no Ascend 950?", section "Cobertura de
+ * operacoes e a lacuna declarada no repositorio"; third page, section "Kernels
+ * especificos de modelo: logits de MQA e prenorm mHC").  The pages do not define
+ * the computation; the reading is the indexer's score, with the head dimension
+ * fixed at 128:
+ *   L[t][s] = sum_{h<H} w[t][h] * max(0, q[t][h] . k[g(t)][s])   ks[t] <= s < ke[t]
+ *   L[t][s] = -inf                                               other s < S
+ * where q and k are dequantised with their UE8M0 block scales and accumulated in
+ * fp32, g(t) = t / q_per_group is the query's key group (a sequence: prefill has
+ * one group of all T queries, decode one group per request), and key s of group g
+ * is row g*group_rows + s of K.
+ *   Q: codes [T*H][ldq] (row t*H + h): mqa_logits_fp8 e4m3, 128 bytes a row, one
+ *      scale per row (sfq packed int16 [1][ld_sfq >= T*H], the low byte);
+ *      mqa_logits_fp4 e2m1, two per byte (even index in the low nibble), 64 bytes
+ *      a row, one scale per 32 elements (sfq packed [2][ld_sfq]).
+ *   K: codes [k_rows][ldk] with k_rows = (ceil(T/q_per_group) - 1)*group_rows + S,
+ *      same formats; sfk packed over K's rows (ld_sfk >= k_rows).
+ *   W: fp32 [T][ldw >= H].  ks, ke: DEVICE int32 [T]; windows are clamped to
+ *      [0, S], and ks >= ke gives a row of -inf.
+ *   L: fp32 [T][ldl >= S]; columns S .. ldl-1 are not written.
+ *   Requires H a multiple of 32, at most 128; Q, K 16-byte aligned with ldq, ldk
+ *   multiples of 16 bytes; sfq, sfk 2-byte aligned; W, L 4-byte aligned;
+ *   q_per_group >= 1, group_rows >= 0.  T == 0 or S == 0 is a no-op.  Errors:
+ *   BSG_ERR_INVALID_ARG, BSG_ERR_UNSUPPORTED_SHAPE (H, or offsets past 2^31 bytes),
+ *   BSG_ERR_MISALIGNED, BSG_ERR_HIP (launch). */
+int mqa_logits_fp8(const void* Q, int64_t ldq, const int16_t* sfq, int64_t ld_sfq,
+                   const void* K, int64_t ldk, const int16_t* sfk, int64_t ld_sfk,
+                   const float* W, int64_t ldw, const int32_t* ks, const int32_t* ke,
+                   float* L, int64_t ldl, int64_t T, int64_t S, int32_t H,
+                   int64_t q_per_group, int64_t group_rows, void* stream);
+
+int mqa_logits_fp4(const void* Q, int64_t ldq, const int16_t* sfq, int64_t ld_sfq,
+                   const void* K, int64_t ldk, const int16_t* sfk, int64_t ld_sfk,
+                   const float* W, int64_t ldw, const int32_t* ks, const int32_t* ke,
+                   float* L, int64_t ldl, int64_t T, int64_t S, int32_t H,
+                   int64_t q_per_group, int64_t group_rows, void* stream);
+
 /* MoE FFN core that allocates nothing and takes no workspace: for callers that
  * cannot allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  It computes exactly what moe_ffn_fp8 computes,

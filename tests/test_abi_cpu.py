@@ -374,3 +374,36 @@ def test_moe_ffn_noalloc_refuses_what_exceeds_its_scratch():
     assert f(*small) == bsg.BSG_ERR_INVALID_ARG
     empty = list(args); empty[18] = 0                                         # M_total = 0
     assert f(*empty) == bsg.BSG_OK
+
+
+@pytest.mark.parametrize("name,row", [("mqa_logits_fp8", 128), ("mqa_logits_fp4", 64)])
+def test_mqa_validation(name, row):
+    """Bad arguments are refused before any HIP call (fake pointers)."""
+    f = getattr(bsg.lib(), name)
+    T, S, H = 8, 300, 64
+    args = [P, row, P2, T * H, 0x100000, row, P2 + 0x1000, S, 0x200000, H, 0x300000, 0x300100,
+            0x400000, S, T, S, H, T, 0, None]
+    bad = list(args); bad[16] = 48                                  # H not a multiple of 32
+    assert f(*bad) == bsg.BSG_ERR_UNSUPPORTED_SHAPE
+    bad = list(args); bad[16] = 160                                 # H > 128
+    assert f(*bad) == bsg.BSG_ERR_UNSUPPORTED_SHAPE
+    bad = list(args); bad[1] = row - 16                             # ldq too small
+    assert f(*bad) == bsg.BSG_ERR_INVALID_ARG
+    bad = list(args); bad[3] = T * H - 1                            # ld_sfq < T*H
+    assert f(*bad) == bsg.BSG_ERR_INVALID_ARG
+    bad = list(args); bad[13] = S - 1                               # ldl < S
+    assert f(*bad) == bsg.BSG_ERR_INVALID_ARG
+    bad = list(args); bad[17] = 1; bad[18] = S                      # 8 groups: ld_sfk too small
+    assert f(*bad) == bsg.BSG_ERR_INVALID_ARG
+    bad = list(args); bad[17] = 0                                   # q_per_group < 1
+    assert f(*bad) == bsg.BSG_ERR_INVALID_ARG
+    bad = list(args); bad[0] = P + 8                                # Q misaligned
+    assert f(*bad) == bsg.BSG_ERR_MISALIGNED
+    bad = list(args); bad[12] = 0x400002                            # L misaligned
+    assert f(*bad) == bsg.BSG_ERR_MISALIGNED
+    bad = list(args); bad[10] = 0                                   # no ks
+    assert f(*bad) == bsg.BSG_ERR_INVALID_ARG
+    empty = list(args); empty[14] = 0                               # T = 0: no-op
+    assert f(*empty) == bsg.BSG_OK
+    empty = list(args); empty[15] = 0                               # S = 0: no-op
+    assert f(*empty) == bsg.BSG_OK

@@ -1,0 +1,166 @@
+"""GPU parity of the MQA logits kernels (FP8 and FP4) against the oracle.
+
+Acceptance (derived from the arithmetic, since the pages fix none for this kernel):
+each score q[t][h] . k[s] is formed by the matrix cores in fp32 from exact products
+(two 64-wide k-steps), the max is exact, and the weighted sum over H heads is H
+fp32 fused multiply-adds plus one add across the wave's halves.  With u = 2^-24,
+the error of L[t][s] is at most about (2*64 + H + 2) u times
+den[t][s] = sum_h |w[t][h]| |q[t][h]| |k[s]|, under 2e-5 for H <= 128; the test
+allows 1e-4 * den.  Outside the window the output must be exactly -inf; inside it
+must be finite.  A structured case whose every step is exact in fp32 is compared
+bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_precision_05_amd as bsg
+from block_scaled_precision_05_amd import workloads
+import oracle
+from oracle import mqa
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+TOL = 1e-4
+SENTINEL = 12345.0
+
+
+def _say(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+
+
+def _packed(sf_u8):
+    return bsg.ensure_packed(sf_u8, sf_u8.shape[0], sf_u8.shape[1])
+
+
+def _run(w, fmt, ldl_pad=0):
+    t = w.tensors
+    T, S = t["W"].shape[0], w.meta["S"]
+    out = torch.full((T, S + ldl_pad), SENTINEL, dtype=torch.float32, device=DEV)
+    L = bsg.mqa_logits(fmt, t["Q"], _packed(t["sfq"]), t["K"], _packed(t["sfk"]), t["W"],
+                       t["ks"], t["ke"], S, q_per_group=w.meta["q_per_group"],
+                       group_rows=w.meta["group_rows"], out=out[:, :S])
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    if ldl_pad:
+        assert np.all(got[:, S:] == SENTINEL), "columns past S were written"
+    return got[:, :S]
+
+
+def _check(w, fmt, got, queries=None):
+    t = {k: v.cpu().numpy() for k, v in w.tensors.items()}
+    m = w.meta
+    ofmt = "e4m3" if fmt == "fp8" else "e2m1"
+    sfq, sfk = oracle.pack_scales(t["sfq"]), oracle.pack_scales(t["sfk"])
+    args = (ofmt, t["Q"], sfq, t["K"], sfk, t["W"])
+    ref = mqa.mqa_logits(*args, t["ks"], t["ke"], m["S"], m["H"], m["q_per_group"],
+                         m["group_rows"], queries=queries)
+    den = mqa.norm_denominator(*args, m["S"], m["H"], m["q_per_group"], m["group_rows"],
+                               queries=queries)
+    rows = got if queries is None else got[queries]
+    outside = np.isinf(ref)
+    assert np.all(rows[outside] == -np.inf), "an entry outside the window is not -inf"
+    assert np.all(np.isfinite(rows[~outside])), "an entry inside the window is not finite"
+    err = np.abs(rows[~outside] - ref[~outside]) / den[~outside]
+    worst = float(err.max()) if err.size else 0.0
+    print(f"[parity] mqa {fmt} {m['mode']}: max normalised error {worst:.3e} over {err.size} "
+          f"window entries", flush=True)
+    assert worst <= TOL
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
+@pytest.mark.parametrize("T,S", [(37, 37), (130, 700), (9, 1100)])
+def test_prefill_causal_full(fmt, T, S):
+    _say(f"mqa {fmt} prefill T={T} S={S} H=64 (causal windows)")
+    w = workloads.mqa(fmt, "prefill", 300 + T, device=DEV, T=T, S=S)
+    _check(w, fmt, _run(w, fmt, ldl_pad=3))
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
+@pytest.mark.parametrize("H", [32, 96, 128])
+def test_head_counts(fmt, H):
+    _say(f"mqa {fmt} decode T=6 S=600 H={H}")
+    w = workloads.mqa(fmt, "decode", 400 + H, device=DEV, T=6, S=600, H=H,
+                      ctx=[600, 0, 1, 31, 33, 513])
+    _check(w, fmt, _run(w, fmt))
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
+def test_decode_groups_and_arbitrary_windows(fmt):
+    """One key group per request, windows anywhere (empty, one key, crossing the
+    512-key workgroup ranges, reversed), key rows of later groups offset."""
+    _say(f"mqa {fmt} decode T=11 S=1300 with arbitrary windows")
+    w = workloads.mqa(fmt, "decode", 77, device=DEV, T=11, S=1300)
+    ks = torch.tensor([0, 5, 511, 512, 700, 1299, 1300, 20, 0, 100, 600], dtype=torch.int32)
+    ke = torch.tensor([1300, 5, 513, 1024, 1299, 1300, 1300, 10, 1, 1100, 601], dtype=torch.int32)
+    w.tensors["ks"], w.tensors["ke"] = ks.to(DEV), ke.to(DEV)
+    _check(w, fmt, _run(w, fmt))
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
+def test_prefill_several_sequences(fmt):
+    """Packed prefill of several sequences: queries t read group t // 4, whose keys
+    start group_rows = 80 rows further on; causal windows inside each sequence."""
+    _say(f"mqa {fmt} three sequences of 4 queries over 70 keys each")
+    T, S, per, grows = 12, 70, 4, 80
+    w = workloads.mqa(fmt, "decode", 91, device=DEV, T=T, S=grows)
+    k = w.tensors["K"][:3 * grows]
+    sfk = w.tensors["sfk"][:3 * grows]
+    w.tensors.update(K=k.contiguous(), sfk=sfk.contiguous(),
+                     ks=torch.zeros(T, dtype=torch.int32, device=DEV),
+                     ke=torch.tensor([66 + (i % per) + 1 for i in range(T)], dtype=torch.int32,
+                                     device=DEV))
+    w.meta.update(S=S, q_per_group=per, group_rows=grows)
+    _check(w, fmt, _run(w, fmt))
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
+def test_structured_exact(fmt):
+    """Unit codes of random sign per head with power-of-two scales and weights: every
+    score, max and weighted sum is exact in fp32, so L equals the oracle bit for bit."""
+    _say(f"mqa {fmt} structured exact case")
+    T, S, H = 8, 300, 64
+    r = np.random.default_rng(5)
+    rows_q = T * H
+    if fmt == "fp8":
+        q = np.where(r.random((rows_q, 1)) < 0.5, 0x38, 0xB8).astype(np.uint8).repeat(128, 1)
+        k = np.full((S, 128), 0x38, dtype=np.uint8)
+        k[r.random(S) < 0.3] = 0xB8
+        sq = r.integers(126, 129, (rows_q, 1), dtype=np.uint8)
+        sk = r.integers(126, 129, (S, 1), dtype=np.uint8)
+    else:
+        q = np.where(r.random((rows_q, 1)) < 0.5, 0x22, 0xAA).astype(np.uint8).repeat(64, 1)
+        k = np.full((S, 64), 0x22, dtype=np.uint8)
+        k[r.random(S) < 0.3] = 0xAA
+        sq = r.integers(126, 129, (rows_q, 4), dtype=np.uint8)
+        sk = r.integers(126, 129, (S, 4), dtype=np.uint8)
+    # terms 2^1 .. 2^13, at most 64 of them: every partial sum fits fp32's 24 bits
+    W = (2.0 ** r.integers(-2, 3, (T, H)) * np.where(r.random((T, H)) < 0.5, 1, -1)).astype(np.float32)
+    ke = r.integers(0, S + 1, T).astype(np.int32)
+
+    class Wl:
+        tensors = {"Q": torch.from_numpy(q).to(DEV), "sfq": torch.from_numpy(sq).to(DEV),
+                   "K": torch.from_numpy(k).to(DEV), "sfk": torch.from_numpy(sk).to(DEV),
+                   "W": torch.from_numpy(W).to(DEV),
+                   "ks": torch.zeros(T, dtype=torch.int32, device=DEV),
+                   "ke": torch.from_numpy(ke).to(DEV)}
+        meta = {"S": S, "H": H, "q_per_group": T, "group_rows": 0, "mode": "structured"}
+    got = _run(Wl, fmt)
+    ofmt = "e4m3" if fmt == "fp8" else "e2m1"
+    ref = mqa.mqa_logits(ofmt, q, oracle.pack_scales(sq), k, oracle.pack_scales(sk), W,
+                         np.zeros(T), ke, S, H, T, 0)
+    assert np.array_equal(got, ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("name", ["mqa_prefill_fp8", "mqa_prefill_fp4", "mqa_decode_fp8",
+                                  "mqa_decode_fp4"])
+def test_workload_sampled_queries(name):
+    """The benchmark's shapes in the launch it times; the oracle computes sampled
+    queries in full."""
+    fmt = name.rsplit("_", 1)[1]
+    _say(f"{name}: full workload, sampled queries")
+    w = workloads.make(name, device=DEV)
+    got = _run(w, fmt)
+    T = got.shape[0]
+    q = np.unique(np.array([0, 1, 31, 32, T // 2, T - 2, T - 1]))
+    _check(w, fmt, got, queries=q)
