@@ -70,6 +70,13 @@ PEAK = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0, "grouped": 5000.0, "moe_f
         "masked": 5000.0, "grouped_bf16": 2500.0, "grouped_fp4": 10100.0,
         "mqa_prefill_fp8": 5000.0, "mqa_prefill_fp4": 10100.0, "mqa_decode_fp8": 5000.0,
         "mqa_decode_fp4": 10100.0}
+# Vector-ALU lane operations per second of the chip: 256 CUs x 4 SIMDs x 16 lanes x
+# 2.4 GHz (one fp32 max or fused multiply-add per lane per clock; the packed
+# two-wide fp32 forms, which the 157.3 TFLOP/s vector figure counts, are not used
+# by this library).  Bound of the MQA prefill: per (query, window key) pair it
+# takes one max and one fused multiply-add per head on the vector units.
+ALU_PEAK_GOPS = 256 * 4 * 16 * 2.4
+ALU_KINDS = ("mqa_prefill_fp8", "mqa_prefill_fp4")
 # Cases bound by HBM (their weights or keys stream once): roofline in GB/s.
 HBM_KINDS = ("masked", "mqa_decode_fp8", "mqa_decode_fp4")
 MQA_KINDS = ("mqa_prefill_fp8", "mqa_prefill_fp4", "mqa_decode_fp8", "mqa_decode_fp4")
@@ -188,9 +195,21 @@ def make_case(kind, dev):
         sfq = bsg.ensure_packed(t["sfq"], t["sfq"].shape[0], t["sfq"].shape[1])
         sfk = bsg.ensure_packed(t["sfk"], t["sfk"].shape[0], t["sfk"].shape[1])
         L = torch.empty(T, S, dtype=torch.float32, device=dev)
-        call = lambda: bsg.mqa_logits(fmt, t["Q"], sfq, t["K"], sfk, t["W"], t["ks"], t["ke"], S,
-                                      q_per_group=m["q_per_group"], group_rows=m["group_rows"],
-                                      out=L)
+        # checked once through the binding, then timed at the C entry point (the
+        # decode kernel runs for tens of microseconds)
+        bsg.mqa_logits(fmt, t["Q"], sfq, t["K"], sfk, t["W"], t["ks"], t["ke"], S,
+                       q_per_group=m["q_per_group"], group_rows=m["group_rows"], out=L)
+        entry = getattr(bsg.lib(), "mqa_logits_" + fmt)
+        Qb, Kb = t["Q"].view(torch.uint8), t["K"].view(torch.uint8)
+        cargs = (Qb.data_ptr(), Qb.stride(0), sfq.data_ptr(), sfq.stride(0), Kb.data_ptr(),
+                 Kb.stride(0), sfk.data_ptr(), sfk.stride(0), t["W"].data_ptr(), t["W"].stride(0),
+                 t["ks"].data_ptr(), t["ke"].data_ptr(), L.data_ptr(), L.stride(0), T, S, H,
+                 m["q_per_group"], m["group_rows"], torch.cuda.current_stream().cuda_stream)
+
+        def call():
+            st = entry(*cargs)
+            if st:
+                raise RuntimeError(f"mqa_logits_{fmt} failed: {bsg.status_string(st)}")
         row = t["Q"].shape[1]
         # queries, their weights and all logits once; keys once per group for
         # prefill (one sequence, shared by every query), once per window key for
@@ -439,6 +458,12 @@ def summarize(kind, r, steps):
     if kind in HBM_KINDS:
         ach = r["min_bytes"] / (mean_us * 1e-6) / 1e9
         out["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    elif kind in ALU_KINDS:
+        ops = 2.0 * r["meta"]["window_pairs"] * r["meta"]["heads"]
+        ach = ops / (mean_us * 1e-6) / 1e9
+        out["roofline"] = {"bound": "alu", "achieved": ach, "peak": ALU_PEAK_GOPS,
+                           "unit": "Gop/s (vector lane operations)",
+                           "mfma_frac": r["flops"] / (mean_us * 1e-6) / 1e12 / PEAK[kind]}
     else:
         ach = r["flops"] / (mean_us * 1e-6) / 1e12
         out["roofline"] = {"bound": "mfma", "achieved": ach, "peak": PEAK[kind], "unit": "TFLOP/s"}

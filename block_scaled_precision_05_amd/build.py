@@ -17,24 +17,51 @@ HEADERS = [os.path.join(HERE, "csrc", h) for h in ("gemm_kernel.h", "configs.h",
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops keeps the compiler from emitting v_pk_{add,mul,fma}_f32.
-FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-shared",
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I" + os.path.join(ROOT, "include")]
+# Per-source code generation options.  The MQA logits kernel feeds its MFMA
+# accumulators straight to vector arithmetic: kept in VGPRs (the MFMA's VGPR form)
+# they need no accumulator-register reads, 32 instructions per key fragment.
+SOURCE_FLAGS = {"mqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def build(force: bool = True, verbose: bool = False) -> str:
-    """Compile every HIP source into libbsg.so next to this file."""
+    """Compile every HIP source (in parallel, one object each) and link libbsg.so
+    next to this file."""
     if not force and os.path.exists(LIB):
         return LIB
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + SOURCES + ["-o", tmp]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libbsg.so")
-    if verbose:
-        sys.stderr.write(res.stderr)
-    os.replace(tmp, LIB)
+    tag = ".tmp%d" % os.getpid()
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(HERE, os.path.basename(src) + tag + ".o")
+        cmd = [HIPCC] + FLAGS + SOURCE_FLAGS.get(os.path.basename(src), []) + \
+            ["-c", src, "-o", obj]
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                            text=True)))
+        objs.append(obj)
+    failed = []
+    for src, p in procs:
+        out, err = p.communicate()
+        if p.returncode != 0:
+            failed.append(src)
+            sys.stderr.write(out + err)
+        elif verbose:
+            sys.stderr.write(err)
+    try:
+        if failed:
+            raise RuntimeError("hipcc failed on " + ", ".join(os.path.basename(f) for f in failed))
+        tmp = LIB + tag
+        res = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs +
+                             ["-o", tmp], capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError("hipcc failed linking libbsg.so")
+        os.replace(tmp, LIB)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     return LIB
 
 
