@@ -22,7 +22,11 @@ on; `ms_per_step` is that median.  The same calls back to back give the warm
 rate beside it (`warm`).  Every other case is timed the same way in the same run
 and reported under `per_dtype` with its fraction of the dtype's dense MFMA peak;
 the mean event-timed launch of the cold calls is the duration behind each
-`roofline`.  `vs_baseline` is null: the pages' 431 TFLOPS at this shape was
+`roofline`.  Before the timed calls, the warm-up calls are followed by 0.2 s of
+untimed calls: under sustained load the clocks take tens of milliseconds to
+settle.  A third loop, with the scratch write followed by a 512 MiB read, gives
+`cold_clean`: caches just as cold, without the scratch's dirty lines being
+written back during the call.  `vs_baseline` is null: the pages' 431 TFLOPS at this shape was
 measured on another accelerator and is reported under `context`.
 
 The per-token quantisers (bf16 activations -> FP8 1x128 or FP4 1x32 codes with
@@ -370,39 +374,57 @@ def _stats(us):
             "us_p90": us[min(len(us) - 1, int(0.9 * len(us)))]}
 
 
-def time_case(kind, steps, warmup, dev, cpu_budget=0.0):
-    """Warm-up, then the timed region: exactly `steps` calls, each preceded on the
-    same stream by a 512 MiB scratch write (more than the 256 MB MALL plus the
-    eight 4 MB L2s), each bracketed by HIP events on that stream, with device
-    synchronisation before and after the region.  A second loop of `steps`
-    back-to-back calls (no scratch write) gives the warm rate beside it.  With
+def time_case(kind, steps, warmup, dev, cpu_budget=0.0, settle_s=0.2):
+    """Warm-up: `warmup` calls, then untimed calls for `settle_s` seconds (under
+    sustained load the chip's clocks take tens of milliseconds to settle; timed
+    right after a short warm-up, the first loop reads 5-12% slow).  Then the timed
+    region: exactly `steps` calls, each preceded on the same stream by a 512 MiB
+    scratch write (more than the 256 MB MALL plus the eight 4 MB L2s), each
+    bracketed by HIP events on that stream, with device synchronisation before and
+    after the region.  Two more loops of `steps` calls give the warm rate (back to
+    back) and a clean cold rate (the scratch write followed by a 512 MiB read, so
+    no dirty line of the scratch is left to write back during the call).  With
     `cpu_budget` > 0 the oracle is then timed on a sample of the same inputs."""
     import torch
     call, flops, nbytes, meta, cpu_sample = make_case(kind, dev)
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    settle = 0
+    while time.perf_counter() - t0 < settle_s:
+        for _ in range(4):
+            call()
+        settle += 4
+        torch.cuda.synchronize()
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    rscratch = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
 
-    def timed(cold):
+    def timed(mode):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for s, e in ev:
-            if cold:
+            if mode != "warm":
                 scratch.fill_(1)
+            if mode == "clean":
+                torch.sum(rscratch, dim=(0,), out=sink)
             s.record(stream)
             call()
             e.record(stream)
         torch.cuda.synchronize()
         return time.perf_counter() - t0, [s.elapsed_time(e) * 1e3 for s, e in ev]
 
-    wall_cold, cold = timed(True)
-    wall_warm, warm = timed(False)
-    del scratch
+    wall_cold, cold = timed("cold")
+    wall_warm, warm = timed("warm")
+    _, clean = timed("clean")
+    del scratch, rscratch
     res = {"per_launch_us": cold, "wall_s": wall_cold, "warm_us": warm, "warm_wall_s": wall_warm,
-           "flops": flops, "min_bytes": nbytes, "meta": meta}
+           "clean_us": clean, "settle_calls": settle, "flops": flops, "min_bytes": nbytes,
+           "meta": meta}
     if cpu_budget > 0 and cpu_sample is not None:
         log(f"{kind}: oracle on a sample of the same inputs for ~{cpu_budget:.0f} s")
         res["cpu"] = cpu_sample(cpu_budget)
@@ -415,6 +437,8 @@ def summarize(kind, r, steps):
     cold = _stats(r["per_launch_us"])
     med, mean_us = cold["us_median"], cold["us_mean"]
     warm = _stats(r["warm_us"]) if r.get("warm_us") else None
+    clean = statistics.median(r["clean_us"]) if r.get("clean_us") else None
+    cold["settle_calls"] = r.get("settle_calls", 0)
     if kind in QUANT_KINDS:
         gbs = r["min_bytes"] / (med * 1e-6) / 1e9
         out = {
@@ -428,6 +452,10 @@ def summarize(kind, r, steps):
         if warm:
             out["warm"] = dict(warm, gb_per_s=r["min_bytes"] / (warm["us_median"] * 1e-6) / 1e9,
                                wall_us_per_call=r["warm_wall_s"] * 1e6 / steps)
+        if clean:
+            out["cold_clean"] = {"us_median": clean,
+                                 "gb_per_s": r["min_bytes"] / (clean * 1e-6) / 1e9,
+                                 "flush": "512 MiB write then 512 MiB read"}
         achieved = r["min_bytes"] / (mean_us * 1e-6) / 1e9
         out["roofline"] = {"kernel": KERNEL_NAME[kind], "bound": "hbm", "achieved": achieved,
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
@@ -449,6 +477,9 @@ def summarize(kind, r, steps):
         out["warm"] = dict(warm, tflops=r["flops"] / (warm["us_median"] * 1e-6) / 1e12,
                            frac_of_peak=r["flops"] / (warm["us_median"] * 1e-6) / 1e12 / PEAK[kind],
                            wall_ms_per_call=r["warm_wall_s"] * 1e3 / steps)
+    if clean:
+        out["cold_clean"] = {"us_median": clean, "tflops": r["flops"] / (clean * 1e-6) / 1e12,
+                             "flush": "512 MiB write then 512 MiB read"}
     if kind in HBM_KINDS:
         out["gb_per_s"] = r["min_bytes"] / (med * 1e-6) / 1e9
         out["frac_of_hbm_peak"] = out["gb_per_s"] / HBM_PEAK_GBS
@@ -609,10 +640,12 @@ def main():
                                "fp32 accumulate, bf16 out",
                    "M": 4096, "N": 7168, "K": 16384, "parallelism": "single GPU"},
         "timing": "value and ms_per_step: median of the timed calls, each after a 512 MiB "
-                  "scratch write (cold L2 and MALL), HIP events on the launch stream; "
-                  "warm: the same calls back to back",
+                  "scratch write (cold L2 and MALL), HIP events on the launch stream, after "
+                  "the warm-up calls and a 0.2 s settle phase of untimed calls; warm: the same "
+                  "calls back to back; cold_clean: after the scratch write and a 512 MiB read",
         "frac_of_peak": b["frac_of_peak"],
         "warm": b["warm"],
+        "cold_clean": b.get("cold_clean"),
         "roofline": roof,
         "cpu_baseline": cpu,
         "context": {"pages_bf16_tflops": PAGES_BF16_TFLOPS,
