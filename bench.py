@@ -104,10 +104,10 @@ KERNEL_NAME = {
     "masked": "gemm_kernel<1, 128, 256, 1, 4, 64, 6, 1, true, 1, 0, 0>",
     "grouped_bf16": "gemm_kernel<0, 256, 256, 2, 4, 64, 5, 1, true, 0, 6, 0>",
     "grouped_fp4": "gemm_kernel<2, 256, 256, 2, 4, 64, 5, 1, true, 1, 4, 0>",
-    "mqa_prefill_fp8": "mqa_logits_kernel<0, 2>",
-    "mqa_prefill_fp4": "mqa_logits_kernel<4, 2>",
-    "mqa_decode_fp8": "mqa_logits_kernel<0, 2>",
-    "mqa_decode_fp4": "mqa_logits_kernel<4, 2>",
+    "mqa_prefill_fp8": "mqa_logits_kernel<0, 2, true>",
+    "mqa_prefill_fp4": "mqa_logits_kernel<4, 2, true>",
+    "mqa_decode_fp8": "mqa_logits_kernel<0, 2, false>",
+    "mqa_decode_fp4": "mqa_logits_kernel<4, 2, false>",
 }
 
 
