@@ -87,6 +87,9 @@ MQA_KINDS = ("mqa_prefill_fp8", "mqa_prefill_fp4", "mqa_decode_fp8", "mqa_decode
 # MI355X published HBM3E bandwidth (GB/s): the bound of the quantisers.
 HBM_PEAK_GBS = 8000.0
 QUANT_KINDS = ("quant_fp8", "quant_fp4", "quant_fp8_moe")
+# Operand values of the dense cases: "random" (the workloads' own draws, the
+# benchmark) or "zeros" (an experiment on power: see --operands).
+OPERANDS = "random"
 # Cases whose inputs the CPU oracle is also timed on (cpu_baseline).
 CPU_KINDS = ("bf16", "fp8", "fp4", "grouped")
 # The pages' own figure at this shape (other accelerator; context only).
@@ -168,6 +171,11 @@ def make_case(kind, dev):
     w = workloads.make(name, device=dev)
     t = w.tensors
     M, N, K = w.M, w.N, w.K
+    if OPERANDS == "zeros" and kind in ("bf16", "fp8", "fp4"):
+        # the same instruction stream on all-zero codes (scales unchanged): what the
+        # operand values cost in power, hence in clock
+        t["A"].zero_()
+        t["B"].zero_()
     if kind in QUANT_KINDS:
         X = t["X"]
         fp4 = kind == "quant_fp4"
@@ -182,8 +190,9 @@ def make_case(kind, dev):
         entry = getattr(bsg.lib(), "quantize_fp4_per_token" if fp4 else "quantize_fp8_per_token")
         args = (X.data_ptr(), X.stride(0), Q.data_ptr(), Q.stride(0), S.data_ptr(), S.stride(0),
                 M, K, bsg.SCALE_RULES["ceil"], torch.cuda.current_stream().cuda_stream)
+        held = (X, Q, S)   # the raw pointers above stay valid while the call lives
 
-        def call():
+        def call(held=held):
             st = entry(*args)
             if st:
                 raise RuntimeError(f"quantiser failed: {bsg.status_string(st)}")
@@ -209,8 +218,9 @@ def make_case(kind, dev):
                  Kb.stride(0), sfk.data_ptr(), sfk.stride(0), t["W"].data_ptr(), t["W"].stride(0),
                  t["ks"].data_ptr(), t["ke"].data_ptr(), L.data_ptr(), L.stride(0), T, S, H,
                  m["q_per_group"], m["group_rows"], torch.cuda.current_stream().cuda_stream)
+        held = (Qb, Kb, sfq, sfk, t["W"], t["ks"], t["ke"], L)   # owners of the raw pointers
 
-        def call():
+        def call(held=held):
             st = entry(*cargs)
             if st:
                 raise RuntimeError(f"mqa_logits_{fmt} failed: {bsg.status_string(st)}")
@@ -533,24 +543,39 @@ def host_info():
 
 
 def oracle_rows(fn, n_rows, flops_per_row, budget_s, what):
-    """Runs the oracle call fn(rows) on a probe chunk of rows, then on one more
-    chunk sized to fill the budget.  Returns the oracle's rate in TFLOPS."""
+    """Runs the oracle call fn(rows) on successive chunks of rows until about
+    `budget_s` seconds are spent: a probe chunk, a second chunk four times as large
+    (the two separate a call's fixed cost, the decode of B, from its cost per row),
+    then one chunk sized to the rest of the budget.  Returns the oracle's rate over
+    all rows and time, in TFLOPS."""
     import numpy as np
     import oracle
     t0 = time.perf_counter()
-    probe = min(16, n_rows)
-    fn(np.arange(0, probe))
-    dt = time.perf_counter() - t0
-    done = probe
-    more = int(min(n_rows - probe, max(0.0, budget_s - dt) / max(dt / probe, 1e-9)))
-    if more > 0:
-        fn(np.arange(probe, probe + more))
-        done += more
+    done, calls, times = 0, 0, []
+    for size in (16, 64):
+        size = min(size, n_rows - done)
+        if size <= 0:
+            break
+        t = time.perf_counter()
+        fn(np.arange(done, done + size))
+        times.append((size, time.perf_counter() - t))
+        done += size
+        calls += 1
+    if len(times) == 2 and n_rows > done:
+        (n1, d1), (n2, d2) = times
+        per_row = max((d2 - d1) / (n2 - n1), 1e-9) if d2 > d1 else d2 / n2
+        fixed = max(d1 - n1 * per_row, 0.0)
+        left = budget_s - (time.perf_counter() - t0) - fixed
+        more = int(min(n_rows - done, max(0.0, left) / per_row))
+        if more > 0:
+            fn(np.arange(done, done + more))
+            done += more
+            calls += 1
     dt = time.perf_counter() - t0
     return {"value": done * flops_per_row / dt / 1e12, "unit": "TFLOPS",
             "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{what}: rows 0..{done - 1} x all columns ({done} of {n_rows} rows, "
-                      f"{dt:.1f} s, two calls)"}
+                      f"{dt:.1f} s, {calls} calls)"}
 
 
 def main():
@@ -565,6 +590,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=24.0,
                     help="seconds of oracle time for cpu_baseline, shared by the BF16, FP8, FP4 "
                          "and grouped cases (0 disables it)")
+    ap.add_argument("--operands", choices=("random", "zeros"), default="random",
+                    help="operand codes of the dense BF16/FP8/FP4 cases: the workloads' random "
+                         "draws (the benchmark), or all zeros, an experiment that runs the same "
+                         "instruction stream at a lower power draw")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 512 MiB device copy three times (the reference "
                          "dispatch that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -581,6 +610,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     bsg.lib()   # fails loudly if the HIP library is missing
+    global OPERANDS
+    OPERANDS = args.operands
     dev = torch.device("cuda:0")
     if args.copy_calibration:
         src = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
@@ -635,7 +666,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic",
+        "data": "synthetic" if args.operands == "random" else
+                "synthetic, dense cases on all-zero operand codes (power experiment)",
         "config": {"workload": "gemm_bf16 D=A*B^T M=4096 N=7168 K=16384, bf16 N(0,1) inputs, "
                                "fp32 accumulate, bf16 out",
                    "M": 4096, "N": 7168, "K": 16384, "parallelism": "single GPU"},
