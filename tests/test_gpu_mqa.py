@@ -152,6 +152,26 @@ def test_structured_exact(fmt):
     assert np.array_equal(got, ref.astype(np.float32))
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
+@pytest.mark.parametrize("T,S", [(800, 8192), (2048, 5000)])
+def test_long_key_ranges(fmt, T, S):
+    """Enough query blocks that the launcher gives each workgroup 2048 (800 queries
+    over 8192 keys) or 4096 keys (2048 over 5000, the last range ragged) on a
+    256-CU device; windows anywhere in the keys, so both halves of a range and the
+    ragged one are computed.  Sampled queries, each checked in full."""
+    _say(f"mqa {fmt} T={T} S={S}: long key ranges per workgroup")
+    w = workloads.mqa(fmt, "prefill", 500 + T, device=DEV, T=T, S=S)
+    r = np.random.default_rng(T)
+    ks = r.integers(0, S, T)
+    ke = np.minimum(S, ks + r.integers(0, S, T))
+    ks[:4], ke[:4] = 0, S
+    w.tensors["ks"] = torch.from_numpy(ks.astype(np.int32)).to(DEV)
+    w.tensors["ke"] = torch.from_numpy(ke.astype(np.int32)).to(DEV)
+    got = _run(w, fmt)
+    q = np.unique(np.array([0, 1, 2, 3, 5, T // 3, T // 2 + 1, T - 4, T - 1]))
+    _check(w, fmt, got, queries=q)
+
+
 @pytest.mark.parametrize("name", ["mqa_prefill_fp8", "mqa_prefill_fp4", "mqa_decode_fp8",
                                   "mqa_decode_fp4"])
 def test_workload_sampled_queries(name):
