@@ -109,3 +109,19 @@ def test_grouped_moe_workload_sampled(kind):
         s0, c = int(off[g]), int(counts[g])
         rows += sorted(set([s0, s0 + (c - 1) // 2, s0 + c - 1]))
     _check(kind, w, got, np.array(rows), f"grouped {kind} MoE")
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp4"])
+def test_grouped_moe_workload_every_expert(kind):
+    """Every routed expert of the MoE workload: its first and last routed rows, all
+    2048 columns."""
+    _say(f"grouped {kind} MoE workload, every expert")
+    w = workloads.make("moe_" + kind, device=DEV)
+    got = _run(kind, w)
+    off = w.tensors["offsets"].cpu().numpy()
+    counts = w.tensors["counts"].cpu().numpy()
+    rows = []
+    for g in range(len(counts)):
+        if counts[g] > 0:
+            rows += sorted({int(off[g]), int(off[g] + counts[g] - 1)})
+    _check(kind, w, got, np.array(rows), f"grouped {kind} MoE, every expert")

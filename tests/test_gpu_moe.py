@@ -265,3 +265,17 @@ def test_moe_ffn_workload_sampled_rows():
         s0, c = int(off[g]), int(counts[g])
         rows += sorted(set([s0, s0 + c - 1, s0 + (c - 1) // 2]))
     _check_ffn(w, np.array(rows), "moe_ffn workload")
+
+
+def test_moe_ffn_workload_every_expert():
+    """The benchmark's FFN share: the first and last routed rows of every expert
+    (the shared one included), checked in full."""
+    _say("moe_ffn workload, every expert")
+    w = workloads.make("moe_ffn", device=DEV)
+    off = w.tensors["offsets"].cpu().numpy()
+    counts = w.tensors["counts"].cpu().numpy()
+    rows = []
+    for g in range(len(counts)):
+        if counts[g] > 0:
+            rows += sorted({int(off[g]), int(off[g] + counts[g] - 1)})
+    _check_ffn(w, np.array(rows), "moe_ffn workload, every expert")

@@ -530,6 +530,37 @@ def test_grouped_moe_workload_sampled():
     check_grouped(w, D, sorted(set(int(r) for r in rows)), "moe_fp8")
 
 
+def test_grouped_moe_workload_every_expert():
+    """Every routed expert of the MoE workload: its first row, its last routed row and
+    its last padded row, all 2048 columns, against one oracle call over the whole
+    expert tensor (copied to the host)."""
+    _say("moe_fp8: every expert, GPU")
+    w = workloads.make("moe_fp8", device=DEV)
+    D = run_grouped(w)
+    torch.cuda.synchronize()
+    t = w.tensors
+    off = t["offsets"].cpu().numpy()
+    counts = t["counts"].cpu().numpy()
+    rows = []
+    for g in range(len(counts)):
+        if off[g + 1] > off[g]:
+            rows += sorted({int(off[g]), int(off[g] + max(counts[g], 1) - 1), int(off[g + 1] - 1)})
+    rows = np.array(rows)
+    _say(f"moe_fp8: oracle on {rows.size} rows of {int((off[1:] > off[:-1]).sum())} experts")
+    A = _u8(t["A"])
+    sfa = oracle.pack_scales(t["sfa"].cpu().numpy())
+    B = _u8(t["B"])
+    sfb = np.stack([oracle.pack_scales(x) for x in t["sfb"].cpu().numpy()])
+    ref = oracle.grouped_fp8(A, sfa, B, sfb, off, rows=rows)
+    na = oracle.row_norms("e4m3", A, sfa, rows=rows)
+    Dh = gpu_bits(D)
+    g_of = np.searchsorted(off, rows, side="right") - 1
+    for g in np.unique(g_of):
+        sel = np.nonzero(g_of == g)[0]
+        nb = oracle.row_norms("e4m3", B[g], sfb[g], gran_mn=128)
+        assert_parity(Dh[rows[sel]], ref[sel], na[sel], nb, what=f"moe_fp8 expert {g}")
+
+
 def test_fp4_scale_load_variants_agree():
     """FP4 fetches a lane's four scale words with one 8-byte load when the packed
     arrays allow it (8-byte aligned, leading dimension a multiple of 4) and with
