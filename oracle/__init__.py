@@ -82,11 +82,12 @@ def _load():
         lib.orc_gemm_bf16.restype = ctypes.c_int
         lib.orc_gemm_bf16.argtypes = [_vp, ctypes.c_int64, _vp, ctypes.c_int64,
                                       ctypes.c_int64] + sel
-        for name in ("orc_gemm_fp8", "orc_gemm_fp4"):
-            f = getattr(lib, name)
-            f.restype = ctypes.c_int
-            f.argtypes = [_vp, ctypes.c_int64, _vp, ctypes.c_int64,
-                          _vp, ctypes.c_int64, _vp, ctypes.c_int64, ctypes.c_int64] + sel
+        lib.orc_gemm_fp8.restype = ctypes.c_int
+        lib.orc_gemm_fp8.argtypes = [_vp, ctypes.c_int64, _vp, ctypes.c_int64, _vp, ctypes.c_int64,
+                                     _vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64] + sel
+        lib.orc_gemm_fp4.restype = ctypes.c_int
+        lib.orc_gemm_fp4.argtypes = [_vp, ctypes.c_int64, _vp, ctypes.c_int64,
+                                     _vp, ctypes.c_int64, _vp, ctypes.c_int64, ctypes.c_int64] + sel
         lib.orc_grouped_fp8.restype = ctypes.c_int
         lib.orc_grouped_fp8.argtypes = [_vp, ctypes.c_int64, _vp, ctypes.c_int64,
                                         _vp, ctypes.c_int64, ctypes.c_int64,
@@ -228,9 +229,10 @@ def gemm_bf16(A, B, rows=None, cols=None) -> np.ndarray:
     return _run(_load().orc_gemm_bf16, (_ptr(A), _ld(A), _ptr(B), _ld(B), K), rows, cols)
 
 
-def gemm_fp8(A, sfa, B, sfb, rows=None, cols=None) -> np.ndarray:
+def gemm_fp8(A, sfa, B, sfb, rows=None, cols=None, sfb_gran_mn: int = 128) -> np.ndarray:
     """A e4m3 codes uint8 [M][K], sfa packed int16 [ceil(K/256)][>=M];
-    B uint8 [N][K], sfb packed int16 [ceil(K/256)][>=ceil(N/128)]."""
+    B uint8 [N][K], sfb packed int16 [ceil(K/256)][>=ceil(N/sfb_gran_mn)]: one scale
+    per 128x128 block of B (sfb_gran_mn = 128) or per row and 128-wide K-block (1)."""
     A = _c2d(A, np.uint8)
     B = _c2d(B, np.uint8)
     sfa = _c2d(sfa, np.int16)
@@ -238,14 +240,16 @@ def gemm_fp8(A, sfa, B, sfb, rows=None, cols=None) -> np.ndarray:
     K = A.shape[1]
     if B.shape[1] != K or K % 128:
         raise ValueError("bad K")
+    if sfb_gran_mn not in (1, 128):
+        raise ValueError("sfb_gran_mn must be 1 or 128")
     kp = (K // 128 + 1) // 2
     if sfa.shape[0] < kp or sfa.shape[1] < A.shape[0] or sfb.shape[0] < kp or \
-            sfb.shape[1] < (B.shape[0] + 127) // 128:
+            sfb.shape[1] < (B.shape[0] + sfb_gran_mn - 1) // sfb_gran_mn:
         raise ValueError("scale array too small")
     rows = _sel(rows, A.shape[0])
     cols = _sel(cols, B.shape[0])
     return _run(_load().orc_gemm_fp8, (_ptr(A), _ld(A), _ptr(sfa), _ld(sfa), _ptr(B), _ld(B),
-                                       _ptr(sfb), _ld(sfb), K), rows, cols)
+                                       _ptr(sfb), _ld(sfb), sfb_gran_mn, K), rows, cols)
 
 
 def gemm_fp4(A, sfa, B, sfb, K: int, rows=None, cols=None) -> np.ndarray:

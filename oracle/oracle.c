@@ -267,14 +267,16 @@ int orc_gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb
 }
 
 /* FP8 e4m3: A [M][lda] with packed per-row, per-128-K scales (sfa, scale rows =
- * M); B [N][ldb] with packed per-128-row, per-128-K scales (sfb, scale rows =
- * ceil(N/128)). */
+ * M); B [N][ldb] with packed per-128-K scales shared by sfb_gran_mn consecutive
+ * rows: 128 (128x128 blocks, scale rows = ceil(N/128)) or 1 (one per row, scale
+ * rows = N). */
 int orc_gemm_fp8(const uint8_t* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
-                 const uint8_t* B, int64_t ldb, const int16_t* sfb, int64_t ld_sfb, int64_t K,
+                 const uint8_t* B, int64_t ldb, const int16_t* sfb, int64_t ld_sfb,
+                 int64_t sfb_gran_mn, int64_t K,
                  const int64_t* rows, int64_t nrows, const int64_t* cols, int64_t ncols,
                  double* out) {
   orc_operand a = {ORC_E4M3, A, lda, sfa, ld_sfa, 1, 128};
-  orc_operand b = {ORC_E4M3, B, ldb, sfb, ld_sfb, 128, 128};
+  orc_operand b = {ORC_E4M3, B, ldb, sfb, ld_sfb, sfb_gran_mn, 128};
   return orc_gemm(&a, &b, K, rows, nrows, cols, ncols, out);
 }
 

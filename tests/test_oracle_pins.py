@@ -286,6 +286,51 @@ def test_scale_only_closed_form_fp8(orc):
             assert D[i, j] == want
 
 
+def test_scale_only_closed_form_fp8_per_row_b(orc):
+    """FP8 with one B scale per row (sfb_gran_mn = 1): q_a = q_b = 1.0 gives
+    D[i][j] = 128 * sum_kb 2^(ea(i,kb) + eb(j,kb)); every column its own exponents,
+    which the 128-row reading would get wrong."""
+    M, N, K = 5, 200, 128 * 3
+    r = _rng(81)
+    ea = r.integers(-8, 5, (M, 3))
+    eb = r.integers(-8, 5, (N, 3))
+    A = np.full((M, K), 0x38, np.uint8)
+    B = np.full((N, K), 0x38, np.uint8)
+    sfa = orc.pack_scales((ea + 127).astype(np.uint8))
+    sfb = orc.pack_scales((eb + 127).astype(np.uint8), ld_packed=N + 5)
+    D = orc.gemm_fp8(A, sfa, B, sfb, sfb_gran_mn=1)
+    for i in range(M):
+        for j in range(N):
+            assert D[i, j] == sum(128 * 2.0 ** (ea[i, kb] + eb[j, kb]) for kb in range(3))
+
+
+def test_fp8_per_row_b_equals_blocks_when_rows_repeat_the_block(orc):
+    """Per-row B scales that repeat each 128-row block's byte give the 128x128 result
+    exactly, ragged last block included."""
+    r = _rng(82)
+    M, N, K = 9, 300, 512
+    A = _rand_e4m3(r, M, K)
+    B = _rand_e4m3(r, N, K)
+    sfa = orc.pack_scales(r.integers(119, 134, (M, 4), dtype=np.uint8))
+    blk = r.integers(119, 134, (3, 4), dtype=np.uint8)
+    rows = np.repeat(blk, 128, axis=0)[:N]
+    D128 = orc.gemm_fp8(A, sfa, B, orc.pack_scales(blk))
+    D1 = orc.gemm_fp8(A, sfa, B, orc.pack_scales(rows), sfb_gran_mn=1)
+    assert np.array_equal(D1, D128)
+
+
+def test_brute_force_fp8_per_row_b(orc):
+    r = _rng(83)
+    M, N, K = 5, 40, 256
+    A = _rand_e4m3(r, M, K)
+    B = _rand_e4m3(r, N, K)
+    sfa = r.integers(110, 140, (M, 2), dtype=np.uint8)
+    sfb = r.integers(110, 140, (N, 2), dtype=np.uint8)
+    D = orc.gemm_fp8(A, orc.pack_scales(sfa), B, orc.pack_scales(sfb), sfb_gran_mn=1)
+    _compare_exact(orc, D, exact.exact_nt(exact.dequant_e4m3(A, sfa, 1, 128),
+                                          exact.dequant_e4m3(B, sfb, 1, 128)))
+
+
 def test_scale_only_closed_form_fp4(orc):
     M, N, K = 5, 6, 32 * 7
     r = _rng(9)
