@@ -49,7 +49,7 @@ _i32 = ctypes.c_int32
 
 EXPORTS = {
     "gemm_bf16": [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp],
-    "gemm_fp8_blockscaled": [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+    "gemm_fp8_blockscaled": [_vp, _i64, _vp, _i64, _i32, _vp, _i64, _vp, _i64, _i32, _vp, _i64,
                              _i64, _i64, _i64, _vp],
     "gemm_fp4_blockscaled": [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
                              _i64, _i64, _i64, _vp],
@@ -177,10 +177,11 @@ def _packed(sf: torch.Tensor, name: str) -> int:
     return _mat(sf, name)
 
 
-def gemm_fp8_blockscaled(A, sfa, B, sfb, out=None, stream=None):
+def gemm_fp8_blockscaled(A, sfa, B, sfb, out=None, stream=None, sfb_gran_mn: int = 128):
     """FP8 e4m3 GEMM with UE8M0 scales: sfa packed int16 [ceil(K/256), >=M] (1x128
-    per row of A), sfb packed int16 [ceil(K/256), >=ceil(N/128)] (128x128 blocks
-    of B).  A and B are float8_e4m3fn or uint8 codes."""
+    per row of A); sfb packed int16 [ceil(K/256), >=ceil(N/128)] (128x128 blocks of
+    B, sfb_gran_mn = 128) or [ceil(K/256), >=N] (one per row of B per 128-wide
+    K-block, sfb_gran_mn = 1).  A and B are float8_e4m3fn or uint8 codes."""
     _dev(A, sfa, B, sfb, out)
     A, B = _bytes_u8(A), _bytes_u8(B)
     M, K = A.shape
@@ -189,8 +190,9 @@ def gemm_fp8_blockscaled(A, sfa, B, sfb, out=None, stream=None):
         raise ValueError("K mismatch")
     D = _out(out, M, N, A.device)
     _check("gemm_fp8_blockscaled", lib().gemm_fp8_blockscaled(
-        _ptr(A), _mat(A, "A"), _ptr(sfa), _packed(sfa, "sfa"), _ptr(B), _mat(B, "B"), _ptr(sfb),
-        _packed(sfb, "sfb"), _ptr(D), _mat(D, "out"), M, N, K, _stream(stream)))
+        _ptr(A), _mat(A, "A"), _ptr(sfa), _packed(sfa, "sfa"), 1, _ptr(B), _mat(B, "B"),
+        _ptr(sfb), _packed(sfb, "sfb"), sfb_gran_mn, _ptr(D), _mat(D, "out"), M, N, K,
+        _stream(stream)))
     return D
 
 

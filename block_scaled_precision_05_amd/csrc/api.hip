@@ -233,11 +233,14 @@ int gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, void* D, i
 }
 
 int gemm_fp8_blockscaled(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
-                         const void* B, int64_t ldb, const int16_t* sfb, int64_t ld_sfb,
-                         void* D, int64_t ldd, int64_t M, int64_t N, int64_t K, void* stream) {
+                         int32_t sfa_gran_mn, const void* B, int64_t ldb, const int16_t* sfb,
+                         int64_t ld_sfb, int32_t sfb_gran_mn, void* D, int64_t ldd, int64_t M,
+                         int64_t N, int64_t K, void* stream) {
+  if (sfa_gran_mn != 1 || (sfb_gran_mn != 128 && sfb_gran_mn != 1)) return BSG_ERR_UNSUPPORTED_SHAPE;
   int st = check_dense(A, lda, B, ldb, D, ldd, M, N, K, 128, K, 1);
   if (st != BSG_OK || M == 0 || N == 0) return st;
-  st = check_scales(sfa, ld_sfa, M, sfb, ld_sfb, (N + 127) / 128, K);
+  const int64_t sfb_rows = (N + sfb_gran_mn - 1) / sfb_gran_mn;
+  st = check_scales(sfa, ld_sfa, M, sfb, ld_sfb, sfb_rows, K);
   if (st != BSG_OK) return st;
   GemmArgs a = {};
   a.A = (const uint8_t*)A;
@@ -255,10 +258,15 @@ int gemm_fp8_blockscaled(const void* A, int64_t lda, const int16_t* sfa, int64_t
   a.K = (int32_t)K;
   a.k_bytes = (int32_t)K;
   a.kp_count = (int32_t)((K / 128 + 1) / 2);
-  a.sfb_rows = (int32_t)((N + 127) / 128);
-  // one 8-byte load for a lane's four A scale words when sfa allows it
-  if (sv_ok(sfa, ld_sfa)) return launch<KIND_FP8, BSG_FP8_CFG, false, 1>(a, (hipStream_t)stream);
-  return launch<KIND_FP8, BSG_FP8_CFG, false, 0>(a, (hipStream_t)stream);
+  a.sfb_rows = (int32_t)sfb_rows;
+  // one 8-byte load for a lane's four A scale words when sfa allows it; per-row B
+  // scales (one word per B fragment, the lane's own row) are the kernel's flag 2
+  const bool wide = sv_ok(sfa, ld_sfa);
+  if (sfb_gran_mn == 1)
+    return wide ? launch<KIND_FP8, BSG_FP8_CFG, false, 3>(a, (hipStream_t)stream)
+                : launch<KIND_FP8, BSG_FP8_CFG, false, 2>(a, (hipStream_t)stream);
+  return wide ? launch<KIND_FP8, BSG_FP8_CFG, false, 1>(a, (hipStream_t)stream)
+              : launch<KIND_FP8, BSG_FP8_CFG, false, 0>(a, (hipStream_t)stream);
 }
 
 int gemm_fp4_blockscaled(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,

@@ -187,9 +187,16 @@ struct GemmTile {
                 "staged rows must split evenly over the lanes");
   static_assert(NW * EPI_WAVE_BYTES <= NS * STAGE_BYTES, "the epilogue staging must fit the ring");
   static_assert((EPI_CHUNKS & (EPI_CHUNKS - 1)) == 0, "the chunk swizzle is a mask");
-  // FP8 B scales: one 128-row block per wave when the wave's TN rows stay inside
-  // one block, else one word per 32-row fragment.
-  static constexpr bool ONE_B_SCALE = TN <= 128 && 128 % TN == 0 && BN % 128 == 0;
+  // SV is a set of flags.  Bit 0 (WIDE): a lane's packed scale words of its
+  // fragment rows come in one wide load (below).  Bit 1 (B_ROW, FP8 only): B has
+  // one scale per row and 128-wide K-block instead of one per 128x128 block.
+  static constexpr bool WIDE = (SV & 1) != 0;
+  static constexpr bool B_ROW = KIND == KIND_FP8 && (SV & 2) != 0;
+  static_assert((SV & ~3) == 0 && (KIND == KIND_FP8 || (SV & 2) == 0), "unknown scale-form flags");
+  // FP8 B scales in 128x128 blocks: one block per wave when the wave's TN rows
+  // stay inside one, else one word per 32-row fragment.  Per-row B scales: one
+  // word per fragment, the lane's own row.
+  static constexpr bool ONE_B_SCALE = !B_ROW && TN <= 128 && 128 % TN == 0 && BN % 128 == 0;
   // A fragments double-buffered in registers (the next k-step's read beside the
   // current MFMAs) unless two waves share a SIMD on the halved register budget:
   // then the MFMAs come first and the other wave covers the read's latency.
@@ -202,9 +209,9 @@ struct GemmTile {
   // rows of every wave block of n fragments (n = 4 for A; n = FN, 4 or 2, for
   // B): LDS slot 32f + i (fragment f, lane row i) holds block row n*i + f.  A
   // lane's n fragment rows are then adjacent in memory, and so are their packed
-  // scale words: SV = 1 fetches them with one 8-byte (n = 4) or 4-byte (n = 2)
+  // scale words: WIDE fetches them with one 8-byte (n = 4) or 4-byte (n = 2)
   // load per operand (the packed arrays must be 8-byte aligned, with leading
-  // dimensions that are multiples of 4), SV = 0 with n 2-byte loads.
+  // dimensions that are multiples of 4), otherwise n 2-byte loads.
   static constexpr bool PERM_A = KIND != KIND_BF16;
   static constexpr bool PERM_B = KIND == KIND_FP4;
   static constexpr bool PERM = PERM_B;   // FP4: both operands
@@ -220,7 +227,7 @@ struct GemmTile {
     return (PERM_A ? (row >> 2) : row) & (EPI_CHUNKS - 1);
   }
   static constexpr int perm_b(int x) { return perm_rows(PERM_B ? FN : 1, x); }
-  static constexpr int NSC = SV ? (1 + (PERM_B ? 1 : NSB)) * SW : (FM + NSB) * SW;
+  static constexpr int NSC = WIDE ? (1 + (PERM_B ? 1 : NSB)) * SW : (FM + NSB) * SW;
   static constexpr int VMEM_PER_STAGE = N_DMA + NSC;
   static_assert(SB == 64 || SB == 128, "a stage is 64 or 128 bytes of K per row");
   static_assert(NS >= 2 && NS <= 8, "ring of 2..8 stages");
@@ -644,8 +651,8 @@ void gemm_kernel(const GemmArgs args) {
       // leading dimension is a multiple of 4, so those words lie inside the array):
       // a record ending at row M would drop the valid words of a dword that
       // straddles it.
-      constexpr bool SV_B = SV && T::PERM_B;
-      const int a_rows = SV ? (args.M + 3) & ~3 : args.M;
+      constexpr bool SV_B = T::WIDE && T::PERM_B;
+      const int a_rows = T::WIDE ? (args.M + 3) & ~3 : args.M;
       const int b_rows = SV_B ? (args.sfb_rows + 3) & ~3 : args.sfb_rows;
       const __amdgpu_buffer_rsrc_t rsa = make_rsrc(
           args.sfa, (uint32_t)(2 * ((int64_t)(args.kp_count - 1) * args.ld_sfa + a_rows)));
@@ -655,8 +662,9 @@ void gemm_kernel(const GemmArgs args) {
       uint32_t sa_voff = 2u * (uint32_t)(m0 + wm * T::TM + (T::PERM_A ? 4 * l32 : l32));
       asm volatile("" : "+v"(sa_voff));
       const int brow0 = EPI && wn * T::TN >= BN / 2 ? args.inter + n0 + wn * T::TN - BN / 2 : n0 + wn * T::TN;
-      uint32_t sb_voff = KIND == KIND_FP8 ? 2u * (uint32_t)(brow0 / 128)
-                                          : 2u * (uint32_t)(n0 + wn * T::TN + (T::PERM_B ? FN * l32 : l32));
+      uint32_t sb_voff = KIND == KIND_FP8 && !T::B_ROW
+                             ? 2u * (uint32_t)(brow0 / 128)
+                             : 2u * (uint32_t)(n0 + wn * T::TN + (T::PERM_B ? FN * l32 : l32));
       asm volatile("" : "+v"(sb_voff));
       // Raw scale words of stage kt (packed int16, not decoded yet).
       //   FP8: K-block kt*SB/128, held in packed row kb/2, byte kb%2.
@@ -666,7 +674,7 @@ void gemm_kernel(const GemmArgs args) {
       // value at every call).  FP4 with SV: the two dwords of each operand's 8-byte
       // load, fragments 2i and 2i+1 in the low and high halves of dword i.
       uint16_t rs_a[NS][FM][SW > 0 ? SW : 1] = {}, rs_b[NS][NSB][SW > 0 ? SW : 1] = {};
-      uint32_t rv_a[SV ? NS : 1][2] = {}, rv_b[SV ? NS : 1][2] = {};
+      uint32_t rv_a[T::WIDE ? NS : 1][2] = {}, rv_b[T::WIDE ? NS : 1][2] = {};
       auto load_scales = [&](int kt, auto slot) {
         constexpr int sl = decltype(slot)::value;
         if constexpr (KIND != KIND_BF16) {
@@ -679,7 +687,7 @@ void gemm_kernel(const GemmArgs args) {
             // fragment f's word: 2 bytes further on (permuted rows: adjacent) or
             // 64 bytes (32 rows) further on
             constexpr uint32_t fstep_a = T::PERM_A ? 2 : 64, fstep_b = T::PERM_B ? 2 : 64;
-            if constexpr (SV) {
+            if constexpr (T::WIDE) {
               const u32x2_t da = __builtin_amdgcn_raw_buffer_load_b64(rsa, va, 0, 0);
               rv_a[sl][0] = da[0];
               rv_a[sl][1] = da[1];
@@ -688,16 +696,16 @@ void gemm_kernel(const GemmArgs args) {
               for (int f = 0; f < FM; ++f)
                 rs_a[sl][f][w] = __builtin_amdgcn_raw_buffer_load_b16(rsa, va + fstep_a * f, 0, 0);
             }
-            if constexpr (SV && T::PERM_B && FN == 4) {
+            if constexpr (T::WIDE && T::PERM_B && FN == 4) {
               const u32x2_t db = __builtin_amdgcn_raw_buffer_load_b64(rsb, vb, 0, 0);
               rv_b[sl][0] = db[0];
               rv_b[sl][1] = db[1];
-            } else if constexpr (SV && T::PERM_B) {
+            } else if constexpr (T::WIDE && T::PERM_B) {
               rv_b[sl][0] = __builtin_amdgcn_raw_buffer_load_b32(rsb, vb, 0, 0);
             } else {
 #pragma unroll
               for (int f = 0; f < NSB; ++f) {
-                if constexpr (KIND == KIND_FP8 && !T::ONE_B_SCALE)
+                if constexpr (KIND == KIND_FP8 && !T::ONE_B_SCALE && !T::B_ROW)
                   rs_b[sl][f][w] = __builtin_amdgcn_raw_buffer_load_b16(
                       rsb, 2u * (uint32_t)(((nrow0 + 32 * f) >> 7) + kp * args.ld_sfb), 0, 0);
                 else
@@ -718,7 +726,7 @@ void gemm_kernel(const GemmArgs args) {
         constexpr int sl = decltype(slot)::value;
         if constexpr (KIND == KIND_FP8) {
           const int sh = ((kt * SB / 128) & 1) * 8;
-          if constexpr (SV) {
+          if constexpr (T::WIDE) {
             // the K-block's byte of fragments 2i and 2i+1 moves to bytes 0 and 2
             sa[0] = rv_a[sl][0] >> sh;
             sa[1] = rv_a[sl][1] >> sh;
@@ -729,7 +737,7 @@ void gemm_kernel(const GemmArgs args) {
 #pragma unroll
           for (int f = 0; f < FN; ++f) sb[f] = ((uint32_t)rs_b[sl][T::ONE_B_SCALE ? 0 : f][0] >> sh) & 0xFF;
         } else if constexpr (KIND == KIND_FP4) {
-          if constexpr (SV) {
+          if constexpr (T::WIDE) {
             sa[0] = rv_a[sl][0];
             sa[1] = rv_a[sl][1];
             sb[0] = rv_b[sl][0];
@@ -795,7 +803,7 @@ void gemm_kernel(const GemmArgs args) {
                        const uint32_t (&sb)[FN]) {
         constexpr int j = decltype(jc)::value;
         if constexpr (!MM) return;
-        if constexpr (KIND == KIND_FP8 && SV) {
+        if constexpr (KIND == KIND_FP8 && T::WIDE) {
           // A fragment f's scale: byte 2*(f%2) of dword f/2 (decoded per K-block)
           [&]<int... ab>(std::integer_sequence<int, ab...>) {
             ((acc[ab / FN][ab % FN] = mfma_scaled2<0, 0, 2 * ((ab / FN) % 2)>(

@@ -16,6 +16,7 @@ para calculo e comunicacao de IA", section "Resultados de kernel e comunicacao")
   fp8_mid       FP8 1024x2048x4096, 1x128 (A) and 128x128 (B) UE8M0 scales
   bf16_large    BF16 4096x7168x16384
   fp8_large     FP8 4096x7168x16384, scales as fp8_mid
+  fp8_rowb_large  FP8 4096x7168x16384 with one B scale per row (1x128 on B too)
   moe_fp8       M-grouped FP8: 256 experts, N=2048, K=7168, Zipf(1.1) routing
   moe_bf16      the same routing and shape in BF16
   moe_fp4       the same routing and shape in FP4 (1x32 scales)
@@ -238,6 +239,7 @@ SHAPES = {
     "moe_fp4": ("grouped_fp4", None, 2048, 7168, 1012),
     "fp4_large": ("fp4", 4096, 7168, 16384, 1005),
     "fp8_large": ("fp8", 4096, 7168, 16384, 1006),
+    "fp8_rowb_large": ("fp8_rowb", 4096, 7168, 16384, 1017),
     "act_large": ("act", 4096, None, 16384, 1007),
     "act_moe": ("act", 16384, None, 7168, 1008),
     "moe_ffn": ("moe_ffn", None, None, None, 1009),
@@ -260,6 +262,10 @@ def dense(kind: str, M: int, N: int, K: int, seed: int, device="cpu", name: str 
     elif kind == "fp8":
         w.tensors["A"], w.tensors["sfa"] = fp8_operand(M, K, 1, g, device)
         w.tensors["B"], w.tensors["sfb"] = fp8_operand(N, K, 128, g, device)
+    elif kind == "fp8_rowb":
+        # FP8 with one B scale per row and 128-wide K-block (sfb_gran_mn = 1)
+        w.tensors["A"], w.tensors["sfa"] = fp8_operand(M, K, 1, g, device)
+        w.tensors["B"], w.tensors["sfb"] = fp8_operand(N, K, 1, g, device)
     elif kind == "fp4":
         w.tensors["A"], w.tensors["sfa"] = fp4_operand(M, K, g, device)
         w.tensors["B"], w.tensors["sfb"] = fp4_operand(N, K, g, device)

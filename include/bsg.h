@@ -81,18 +81,20 @@ int gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, void* D, i
               int64_t M, int64_t N, int64_t K, void* stream);
 
 /* FP8 block-scaled GEMM:
- *   D[m][n] = bf16( sum_k a[m][k] * 2^(sa[m][k/128]-127) * b[n][k] * 2^(sb[n/128][k/128]-127) )
+ *   D[m][n] = bf16( sum_k a[m][k] * 2^(sa[m][k/128]-127) * b[n][k] * 2^(sb[n/gb][k/128]-127) )
  *   A: e4m3 [M][lda] bytes; sfa: packed int16 [K/256 rounded up][ld_sfa], scale rows = M
- *   (one scale per row of A per 128-wide K-block).
- *   B: e4m3 [N][ldb] bytes; sfb: packed int16 [..][ld_sfb], scale rows = ceil(N/128)
- *   (one scale per 128x128 block of B).
+ *   (one scale per row of A per 128-wide K-block: sfa_gran_mn must be 1).
+ *   B: e4m3 [N][ldb] bytes; sfb: packed int16 [..][ld_sfb] with gb = sfb_gran_mn:
+ *   128, one scale per 128x128 block of B (scale rows = ceil(N/128)), or 1, one
+ *   per row of B per 128-wide K-block (scale rows = N).
  *   D: bf16 [M][ldd].
- *   Requires K % 128 == 0, ld_sfa >= M, ld_sfb >= ceil(N/128), lda, ldb >= K,
+ *   Requires K % 128 == 0, ld_sfa >= M, ld_sfb >= the scale rows of B, lda, ldb >= K,
  *   ldd >= N; A and B 16-byte aligned, lda and ldb multiples of 16; D, sfa and
- *   sfb 2-byte aligned. */
+ *   sfb 2-byte aligned.  Other granularities: BSG_ERR_UNSUPPORTED_SHAPE. */
 int gemm_fp8_blockscaled(const void* A, int64_t lda, const int16_t* sfa, int64_t ld_sfa,
-                         const void* B, int64_t ldb, const int16_t* sfb, int64_t ld_sfb,
-                         void* D, int64_t ldd, int64_t M, int64_t N, int64_t K, void* stream);
+                         int32_t sfa_gran_mn, const void* B, int64_t ldb, const int16_t* sfb,
+                         int64_t ld_sfb, int32_t sfb_gran_mn, void* D, int64_t ldd, int64_t M,
+                         int64_t N, int64_t K, void* stream);
 
 /* FP4 block-scaled GEMM:
  *   D[m][n] = bf16( sum_k a[m][k] * 2^(sa[m][k/32]-127) * b[n][k] * 2^(sb[n][k/32]-127) )

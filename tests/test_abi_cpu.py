@@ -67,9 +67,10 @@ def test_bf16_validation():
 def test_fp8_validation():
     L = bsg.lib()
     f = L.gemm_fp8_blockscaled
-    ok_args = [P, 256, P2, 8, P, 256, P2, 2, P, 256, 8, 256, 256, None]
+    #          A  lda  sfa ld  gA B  ldb  sfb ld gB   D  ldd M  N    K
+    ok_args = [P, 256, P2, 8, 1, P, 256, P2, 2, 128, P, 256, 8, 256, 256, None]
     a = list(ok_args)
-    a[12] = 200            # K % 128
+    a[14] = 200            # K % 128
     assert f(*a) == bsg.BSG_ERR_UNSUPPORTED_SHAPE
     a = list(ok_args)
     a[2] = 0               # null sfa
@@ -78,8 +79,15 @@ def test_fp8_validation():
     a[3] = 4               # ld_sfa < M
     assert f(*a) == bsg.BSG_ERR_INVALID_ARG
     a = list(ok_args)
-    a[7] = 1               # ld_sfb < ceil(N/128) = 2
+    a[8] = 1               # ld_sfb < ceil(N/128) = 2
     assert f(*a) == bsg.BSG_ERR_INVALID_ARG
+    a = list(ok_args)
+    a[9] = 1               # per-row B scales: ld_sfb must cover N = 256 rows
+    assert f(*a) == bsg.BSG_ERR_INVALID_ARG
+    for gA, gB in ((128, 128), (0, 128), (1, 64), (1, 0), (1, 256)):
+        a = list(ok_args)
+        a[4], a[9] = gA, gB  # only sfa_gran_mn = 1 and sfb_gran_mn in {128, 1}
+        assert f(*a) == bsg.BSG_ERR_UNSUPPORTED_SHAPE, (gA, gB)
     a = list(ok_args)
     a[2] = P2 + 1          # odd scale pointer
     assert f(*a) == bsg.BSG_ERR_MISALIGNED

@@ -45,6 +45,11 @@ def run_gpu(kind, t, K=None, out=None):
         sfa = bsg.ensure_packed(t["sfa"], M, K // 128)
         sfb = bsg.ensure_packed(t["sfb"], (N + 127) // 128, K // 128)
         return bsg.gemm_fp8_blockscaled(t["A"], sfa, t["B"], sfb, out=out)
+    if kind == "fp8_rowb":
+        K = t["A"].shape[1]
+        sfa = bsg.ensure_packed(t["sfa"], M, K // 128)
+        sfb = bsg.ensure_packed(t["sfb"], N, K // 128)
+        return bsg.gemm_fp8_blockscaled(t["A"], sfa, t["B"], sfb, out=out, sfb_gran_mn=1)
     K = K if K is not None else 2 * t["A"].shape[1]
     sfa = bsg.ensure_packed(t["sfa"], M, K // 32)
     sfb = bsg.ensure_packed(t["sfb"], N, K // 32)
@@ -61,10 +66,11 @@ def run_oracle(kind, h, K, rows=None, cols=None):
         return ref, na, nb
     sfa = oracle.pack_scales(h["sfa"])
     sfb = oracle.pack_scales(h["sfb"])
-    if kind == "fp8":
-        ref = oracle.gemm_fp8(h["A"], sfa, h["B"], sfb, rows=rows, cols=cols)
+    if kind in ("fp8", "fp8_rowb"):
+        gb = 128 if kind == "fp8" else 1
+        ref = oracle.gemm_fp8(h["A"], sfa, h["B"], sfb, rows=rows, cols=cols, sfb_gran_mn=gb)
         na = oracle.row_norms("e4m3", h["A"], sfa, rows=rows)
-        nb = oracle.row_norms("e4m3", h["B"], sfb, rows=cols, gran_mn=128)
+        nb = oracle.row_norms("e4m3", h["B"], sfb, rows=cols, gran_mn=gb)
     else:
         ref = oracle.gemm_fp4(h["A"], sfa, h["B"], sfb, K, rows=rows, cols=cols)
         na = oracle.row_norms("e2m1", h["A"], sfa, K=K, rows=rows)
@@ -126,7 +132,7 @@ def test_ensure_packed_reuses_or_converts():
 # dense parity
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("kind", ["bf16", "fp8", "fp4"])
+@pytest.mark.parametrize("kind", ["bf16", "fp8", "fp4", "fp8_rowb"])
 def test_dense_small(kind):
     _say(f"dense small {kind}")
     dense_full(kind, 256, 256, 512, 1001)
@@ -136,6 +142,7 @@ def test_dense_small(kind):
     ("bf16", 300, 520, 200), ("bf16", 1, 1, 8), ("bf16", 513, 257, 1032),
     ("fp8", 300, 520, 384), ("fp8", 1, 129, 128), ("fp8", 777, 300, 1152),
     ("fp4", 300, 520, 224), ("fp4", 3, 5, 32), ("fp4", 600, 270, 1056),
+    ("fp8_rowb", 300, 520, 384), ("fp8_rowb", 1, 129, 128), ("fp8_rowb", 777, 300, 1152),
 ])
 def test_dense_ragged(kind, M, N, K):
     _say(f"dense ragged {kind} {M}x{N}x{K}")
@@ -148,6 +155,7 @@ def test_dense_ragged(kind, M, N, K):
 # remainder for every kind: nk = ceil(bytes of K per row / 64).
 @pytest.mark.parametrize("kind,K", [
     ("fp8", 128), ("fp8", 256), ("fp8", 384), ("fp8", 512), ("fp8", 640), ("fp8", 6528),
+    ("fp8_rowb", 256), ("fp8_rowb", 640), ("fp8_rowb", 6528),
     ("fp4", 32), ("fp4", 160), ("fp4", 288), ("fp4", 544), ("fp4", 800), ("fp4", 1184),
     ("fp4", 3264),
     ("bf16", 8), ("bf16", 40), ("bf16", 104), ("bf16", 168), ("bf16", 232), ("bf16", 296),
@@ -189,10 +197,10 @@ def test_bf16_small_workload():
     assert_parity(gpu_bits(D), ref, na, nb, what="bf16_small full")
 
 
-LARGE = {"bf16": "bf16_large", "fp8": "fp8_large", "fp4": "fp4_large"}
+LARGE = {"bf16": "bf16_large", "fp8": "fp8_large", "fp4": "fp4_large", "fp8_rowb": "fp8_rowb_large"}
 
 
-@pytest.mark.parametrize("kind", ["bf16", "fp8", "fp4"])
+@pytest.mark.parametrize("kind", ["bf16", "fp8", "fp4", "fp8_rowb"])
 def test_large_workload_sampled(kind):
     """4096x7168x16384: sampled rows x all columns and sampled columns x all rows."""
     name = LARGE[kind]
@@ -254,27 +262,53 @@ def test_fp4_identity_gives_dequant_b_bit_exact():
     assert np.array_equal(got[nz], want[nz]) and np.all((got[~nz] & 0x7FFF) == 0)
 
 
-@pytest.mark.parametrize("kind", ["fp8", "fp4"])
+@pytest.mark.parametrize("kind", ["fp8", "fp4", "fp8_rowb"])
 def test_scale_only_closed_form_bit_exact(kind):
-    """Unit codes everywhere: D depends on the scales alone and is exact in fp32."""
+    """Unit codes everywhere: D depends on the scales alone.  Scale exponents lie in
+    [-4, 3], so every partial sum of the accumulation fits fp32's 24-bit significand
+    in any order and the result is exact.  (With exponents in [-7, 5] and one B scale
+    per row, a few sums need 25 bits: the GPU's fp32 result then differs from the
+    exact one by a rounding, which is right but not bit-exact.)"""
     M, N = 200, 300
-    K = 128 * 6 if kind == "fp8" else 32 * 14
+    K = 32 * 14 if kind == "fp4" else 128 * 6
     g = torch.Generator().manual_seed(13)
-    if kind == "fp8":
+    if kind != "fp4":
         A = torch.full((M, K), 0x38, dtype=torch.uint8)
         B = torch.full((N, K), 0x38, dtype=torch.uint8)
-        sfa = torch.randint(120, 133, (M, K // 128), generator=g, dtype=torch.int32).to(torch.uint8)
-        sfb = torch.randint(120, 133, ((N + 127) // 128, K // 128), generator=g,
+        sfa = torch.randint(123, 131, (M, K // 128), generator=g, dtype=torch.int32).to(torch.uint8)
+        sb_rows = N if kind == "fp8_rowb" else (N + 127) // 128
+        sfb = torch.randint(123, 131, (sb_rows, K // 128), generator=g,
                             dtype=torch.int32).to(torch.uint8)
     else:
         A = torch.full((M, K // 2), 0x22, dtype=torch.uint8)
         B = torch.full((N, K // 2), 0x22, dtype=torch.uint8)
-        sfa = torch.randint(120, 133, (M, K // 32), generator=g, dtype=torch.int32).to(torch.uint8)
-        sfb = torch.randint(120, 133, (N, K // 32), generator=g, dtype=torch.int32).to(torch.uint8)
+        sfa = torch.randint(123, 131, (M, K // 32), generator=g, dtype=torch.int32).to(torch.uint8)
+        sfb = torch.randint(123, 131, (N, K // 32), generator=g, dtype=torch.int32).to(torch.uint8)
     t = {"A": A.to(DEV), "sfa": sfa.to(DEV), "B": B.to(DEV), "sfb": sfb.to(DEV)}
     D = run_gpu(kind, t, K=K)
     ref, _, _ = run_oracle(kind, host({"A": A, "sfa": sfa, "B": B, "sfb": sfb}), K)
     assert np.array_equal(gpu_bits(D), oracle.bf16_rne(ref))
+
+
+@pytest.mark.parametrize("wide", [True, False])
+def test_fp8_per_row_b_scales_repeating_blocks_equal_block_scales(wide):
+    """Per-row B scales that repeat every 128-row block's byte must give the bits of
+    the 128x128 call (ragged last block), with the A scale words loaded wide (8-byte
+    aligned, leading dimension a multiple of 4) or two bytes at a time."""
+    M, N, K = 336, 300, 1152                    # ld_sfa = M, a multiple of 4
+    w = workloads.dense("fp8", M, N, K, 4242, device=DEV)
+    t = w.tensors
+    sfa = bsg.ensure_packed(t["sfa"], M, K // 128)
+    if not wide:
+        wider = torch.zeros(sfa.shape[0], M + 1, dtype=torch.int16, device=DEV)
+        wider[:, :M] = sfa
+        sfa = wider[:, :M]                       # leading dimension M + 1: not a multiple of 4
+    blk = bsg.ensure_packed(t["sfb"], (N + 127) // 128, K // 128)
+    rows = bsg.ensure_packed(t["sfb"].repeat_interleave(128, 0)[:N].contiguous(), N, K // 128)
+    D128 = bsg.gemm_fp8_blockscaled(t["A"], sfa, t["B"], blk)
+    D1 = bsg.gemm_fp8_blockscaled(t["A"], sfa, t["B"], rows, sfb_gran_mn=1)
+    torch.cuda.synchronize()
+    assert np.array_equal(gpu_bits(D1), gpu_bits(D128))
 
 
 def test_all_ones_gives_K():
