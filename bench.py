@@ -96,9 +96,9 @@ CPU_KINDS = ("bf16", "fp8", "fp4", "grouped")
 PAGES_BF16_TFLOPS = 431.0
 
 KERNEL_NAME = {
-    "bf16": "gemm_kernel<0, 256, 256, 2, 4, 64, 5, 1, false, 0, 0, 0>",
+    "bf16": "gemm_kernel<0, 256, 256, 2, 4, 64, 5, 1, false, 0, 8, 0>",
     "fp8": "gemm_kernel<1, 256, 256, 2, 4, 64, 5, 1, false, 1, 0, 0>",
-    "fp4": "gemm_kernel<2, 256, 256, 2, 4, 64, 5, 1, false, 1, 0, 0>",
+    "fp4": "gemm_kernel<2, 256, 256, 2, 4, 64, 5, 1, false, 1, 2, 0>",
     "grouped": "gemm_kernel<1, 256, 256, 2, 4, 64, 5, 1, true, 1, 8, 0>",
     "quant_fp8": "quant_kernel<0, 0, 32, 2, 0>",
     "quant_fp4": "quant_kernel<1, 0, 32, 2, 0>",
