@@ -337,31 +337,37 @@ struct GroupCursor {
 // Rows of expert g: [off[g], off[g+1]) in the contiguous layout, or, in the masked
 // layout (cap > 0, off = per-expert valid counts), the first min(off[g], cap) of
 // its cap rows.
-__device__ __forceinline__ void group_range(const int32_t* off, int g, int cap, int& lo, int& hi) {
+// Rows of expert g.  The offsets live on the device and are not checked by the
+// host; clamped here into [0, M] (contiguous layout: lo <= hi <= M; masked: the
+// count into [0, cap]), offsets that break the precondition give wrong rows but
+// never an access outside A, D or their scales.
+__device__ __forceinline__ void group_range(const int32_t* off, int g, int cap, int M, int& lo,
+                                            int& hi) {
   if (cap > 0) {
     const int m = off[g];
     lo = g * cap;
     hi = lo + (m < 0 ? 0 : (m > cap ? cap : m));
   } else {
-    lo = off[g];
-    hi = off[g + 1];
+    const int a = off[g], b = off[g + 1];
+    lo = a < 0 ? 0 : (a > M ? M : a);
+    hi = b < lo ? lo : (b > M ? M : b);
   }
 }
 
 template <int BM>
-__device__ __forceinline__ int group_tiles(const int32_t* off, int g, int G, int cap) {
+__device__ __forceinline__ int group_tiles(const int32_t* off, int g, int G, int cap, int M) {
   if (g >= G) return 0;
   int lo, hi;
-  group_range(off, g, cap, lo, hi);
+  group_range(off, g, cap, M, lo, hi);
   return hi > lo ? (hi - lo + BM - 1) / BM : 0;
 }
 
 // Total row tiles over all experts.
 template <int BM>
-__device__ int grouped_total_row_tiles(const int32_t* off, int G, int cap) {
+__device__ int grouped_total_row_tiles(const int32_t* off, int G, int cap, int M) {
   int total = 0;
   for (int g0 = 0; g0 < G; g0 += 64) {
-    int t = group_tiles<BM>(off, g0 + (threadIdx.x & 63), G, cap);
+    int t = group_tiles<BM>(off, g0 + (threadIdx.x & 63), G, cap, M);
     int s = wave_incl_scan(t);
     total += __shfl(s, 63, 64);
   }
@@ -372,11 +378,11 @@ __device__ int grouped_total_row_tiles(const int32_t* off, int G, int cap) {
 // order); returns false when rt is past the end.  Outputs the expert g, the index
 // of its first row tile, its number of row tiles and its row range.
 template <int BM>
-__device__ bool grouped_find(const int32_t* off, int G, int cap, int rt, GroupCursor& cur, int& g,
-                             int& tile0, int& ntiles, int& row_lo, int& row_hi) {
+__device__ bool grouped_find(const int32_t* off, int G, int cap, int M, int rt, GroupCursor& cur,
+                             int& g, int& tile0, int& ntiles, int& row_lo, int& row_hi) {
   const int lane = threadIdx.x & 63;
   while (cur.g0 < G) {
-    int t = group_tiles<BM>(off, cur.g0 + lane, G, cap);
+    int t = group_tiles<BM>(off, cur.g0 + lane, G, cap, M);
     int incl = wave_incl_scan(t) + cur.before;
     uint64_t hit = __ballot(incl > rt);
     if (hit) {
@@ -385,7 +391,7 @@ __device__ bool grouped_find(const int32_t* off, int G, int cap, int rt, GroupCu
       ntiles = __shfl(t, j, 64);
       g = cur.g0 + j;
       tile0 = incl_j - ntiles;
-      group_range(off, g, cap, row_lo, row_hi);
+      group_range(off, g, cap, M, row_lo, row_hi);
       return true;
     }
     cur.before = __shfl(incl, 63, 64);
@@ -500,7 +506,7 @@ void gemm_kernel(const GemmArgs args) {
   int total_tiles;
   GroupCursor cur{0, 0};
   if constexpr (GROUPED) {
-    total_tiles = grouped_total_row_tiles<BM>(args.offsets, args.G, args.cap) * args.tiles_n;
+    total_tiles = grouped_total_row_tiles<BM>(args.offsets, args.G, args.cap, args.M) * args.tiles_n;
   } else {
     total_tiles = args.tiles_m * args.tiles_n;
   }
@@ -544,7 +550,7 @@ void gemm_kernel(const GemmArgs args) {
       // so the tiles an XCD runs together share expert weights as well as rows.
       // (Two-row super-rows measured 1% faster than four on the MoE shapes.)
       int g, tile0, ntl, row_lo, row_hi;
-      if (!grouped_find<BM>(args.offsets, args.G, args.cap, p / args.tiles_n, cur, g, tile0, ntl,
+      if (!grouped_find<BM>(args.offsets, args.G, args.cap, args.M, p / args.tiles_n, cur, g, tile0, ntl,
                             row_lo, row_hi))
         break;
       int tm, tn;

@@ -117,9 +117,13 @@ int gemm_fp4_blockscaled(const void* A, int64_t lda, const int16_t* sfa, int64_t
  *   sfb_g = sfb + g*stride_sfb (packed int16, scale rows = ceil(N/128)):
  *     D[m][n] = bf16( sum_k a[m][k] * 2^(sa[m][k/128]-127) * b_g[n][k] * 2^(sb_g[n/128][k/128]-127) )
  *   A: e4m3 [M_total][lda]; sfa packed, scale rows = M_total; D: bf16 [M_total][ldd].
- *   group_offsets: DEVICE int32 [G+1].  Precondition (not checked, the offsets
- *   live on the device): 0 <= off[0] <= off[1] <= ... <= off[G] <= M_total.
- *   Rows outside [off[0], off[G]) are not written.  Empty groups are allowed.
+ *   group_offsets: DEVICE int32 [G+1].  Precondition (not checked by the host, the
+ *   offsets live on the device): 0 <= off[0] <= off[1] <= ... <= off[G] <= M_total.
+ *   The kernel clamps each expert's range into [0, M_total] (lo = clamp(off[g]),
+ *   hi = clamp(off[g+1]) >= lo), so offsets that break it give wrong rows (experts
+ *   whose ranges overlap race on the shared rows) but never an access outside A,
+ *   D or their scales.  Rows outside [off[0], off[G]) are not written.  Empty
+ *   groups are allowed.
  *   Offsets need no alignment; 128-row aligned groups waste no tile rows.
  *   G == 0 is a no-op.  Requires G <= 1024, K % 128 == 0, stride_b >= (N-1)*ldb + K,
  *   stride_sfb >= ceil(K/256)*ld_sfb, plus the dense FP8 requirements. */

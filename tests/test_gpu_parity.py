@@ -545,6 +545,45 @@ def test_grouped_single_expert_equals_dense():
     assert torch.equal(D.view(torch.int16), Dd.view(torch.int16))
 
 
+def test_grouped_offsets_outside_the_precondition_stay_in_bounds():
+    """Device offsets that break the documented precondition (a negative first
+    offset, a decreasing pair, a last offset past M_total) are clamped into
+    [0, M_total] by the kernel: every row it writes lies inside D, the rows past
+    M_total of the output buffer keep their sentinel, and the rows only one expert
+    covers hold that expert's result."""
+    _say("grouped FP8 with out-of-range offsets")
+    M, N, K, G = 256, 256, 512, 3
+    w = workloads.grouped(G, N, K, 4343, device=DEV, counts=[128, 0, 128])
+    t = w.tensors
+    A = t["A"][:M].contiguous()
+    sfa_u8 = t["sfa"][:M].contiguous()
+    sfa = bsg.ensure_packed(sfa_u8, M, K // 128)
+    sfb = torch.stack([bsg.ensure_packed(x, (N + 127) // 128, K // 128) for x in t["sfb"]])
+    off = torch.tensor([-5, 100, 50, 10 ** 6], dtype=torch.int32, device=DEV)
+    buf = torch.full((M + 64, N), 0, dtype=torch.int16, device=DEV)
+    buf.fill_(SENTINEL_BITS)
+    D = buf.view(torch.bfloat16)
+    bsg.m_grouped_gemm_fp8(A, sfa, t["B"], sfb, off, out=D[:M])
+    torch.cuda.synchronize()
+    got = gpu_bits(D)
+    assert np.all(got[M:] == SENTINEL_BITS), "rows past M_total were written"
+    Ah, sfah = _u8(A), oracle.pack_scales(sfa_u8.cpu().numpy())
+    na = oracle.row_norms("e4m3", Ah, sfah)
+    ref, nb = {}, {}
+    for g in (0, 2):
+        Bg = _u8(t["B"][g])
+        sfbg = oracle.pack_scales(t["sfb"][g].cpu().numpy())
+        ref[g] = oracle.gemm_fp8(Ah, sfah, Bg, sfbg)
+        nb[g] = oracle.row_norms("e4m3", Bg, sfbg, gran_mn=128)
+    # expert 0: rows [0, 100); expert 1: empty; expert 2: rows [50, 256)
+    assert_parity(got[:50], ref[0][:50], na[:50], nb[0], what="rows of expert 0 only")
+    assert_parity(got[100:M], ref[2][100:M], na[100:M], nb[2], what="rows of expert 2 only")
+    # rows both ranges cover: every element is one of the two experts' results
+    mid = bf16_bits_to_f64(got[50:100])
+    err = [np.abs(mid - ref[g][50:100]) / (na[50:100, None] * nb[g][None, :]) for g in (0, 2)]
+    assert np.all(np.minimum(err[0], err[1]) <= 4e-3)
+
+
 def test_grouped_moe_workload_sampled():
     """256 experts, N=2048, K=7168, Zipf(1.1) routing padded to 128 rows."""
     _say("moe_fp8: generating on the GPU")
