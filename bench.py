@@ -333,13 +333,16 @@ def make_case(kind, dev):
                 "executed_tflop": 2.0 * M * N * K / 1e12}
     flops = w.flops
     meta.update({"M": M, "N": N, "K": K})
-    return call, flops, nbytes, meta, lambda budget: cpu_sample(kind, w, budget)
+    return call, flops, nbytes, meta, lambda budget: cpu_sample(kind, w, budget, D)
 
 
-def cpu_sample(kind, w, budget_s):
+def cpu_sample(kind, w, budget_s, D=None):
     """The CPU oracle (plain C, fp64, all host threads) on leading rows of the case's
     own inputs, copied to host memory: the dense shapes' first rows x all N columns;
-    for the grouped GEMM the first rows of its largest expert x all N columns."""
+    for the grouped GEMM the first rows of its largest expert x all N columns.  With
+    the GPU's output D of the same inputs (after the timed calls), the rows the oracle
+    computed, and the last 128x128 tile of the dense shapes, are also compared with
+    it: the normalised error |D - bf16(oracle)| / (|a_i| |b_j|) against 1e-3."""
     import numpy as np
     import torch
     import oracle
@@ -349,20 +352,27 @@ def cpu_sample(kind, w, budget_s):
     def u8(x):
         return x.contiguous().view(torch.uint8).cpu().numpy()
 
+    r0 = 0
     if kind == "bf16":
         B = t["B"].view(torch.int16).cpu().numpy().view(np.uint16)
         A = t["A"].view(torch.int16).cpu().numpy().view(np.uint16)
-        fn = lambda rows: oracle.gemm_bf16(A, B, rows=rows)
+        fn = lambda rows, cols=None: oracle.gemm_bf16(A, B, rows=rows, cols=cols)
+        norms = lambda rows, cols: (oracle.row_norms("bf16", A, rows=rows),
+                                    oracle.row_norms("bf16", B, rows=cols))
         n_rows, what = M, f"BF16 {M}x{N}x{K}"
     elif kind == "fp8":
         A, B = u8(t["A"]), u8(t["B"])
         sfa, sfb = oracle.pack_scales(u8(t["sfa"])), oracle.pack_scales(u8(t["sfb"]))
-        fn = lambda rows: oracle.gemm_fp8(A, sfa, B, sfb, rows=rows)
+        fn = lambda rows, cols=None: oracle.gemm_fp8(A, sfa, B, sfb, rows=rows, cols=cols)
+        norms = lambda rows, cols: (oracle.row_norms("e4m3", A, sfa, rows=rows),
+                                    oracle.row_norms("e4m3", B, sfb, rows=cols, gran_mn=128))
         n_rows, what = M, f"FP8 {M}x{N}x{K}"
     elif kind == "fp4":
         A, B = u8(t["A"]), u8(t["B"])
         sfa, sfb = oracle.pack_scales(u8(t["sfa"])), oracle.pack_scales(u8(t["sfb"]))
-        fn = lambda rows: oracle.gemm_fp4(A, sfa, B, sfb, K, rows=rows)
+        fn = lambda rows, cols=None: oracle.gemm_fp4(A, sfa, B, sfb, K, rows=rows, cols=cols)
+        norms = lambda rows, cols: (oracle.row_norms("e2m1", A, sfa, K=K, rows=rows),
+                                    oracle.row_norms("e2m1", B, sfb, K=K, rows=cols))
         n_rows, what = M, f"FP4 {M}x{N}x{K}"
     else:
         counts = t["counts"].cpu().numpy()
@@ -373,9 +383,48 @@ def cpu_sample(kind, w, budget_s):
         sfa = oracle.pack_scales(u8(t["sfa"][r0:r0 + n_rows]))
         Bg, sfbg = u8(t["B"][g:g + 1]), np.stack([oracle.pack_scales(u8(t["sfb"][g]))])
         one = np.array([0, n_rows], dtype=np.int32)
-        fn = lambda rows: oracle.grouped_fp8(A, sfa, Bg, sfbg, one, rows=rows)
+        fn = lambda rows, cols=None: oracle.grouped_fp8(A, sfa, Bg, sfbg, one, rows=rows, cols=cols)
+        norms = lambda rows, cols: (oracle.row_norms("e4m3", A, sfa, rows=rows),
+                                    oracle.row_norms("e4m3", Bg[0], sfbg[0], rows=cols, gran_mn=128))
         what = f"M-grouped FP8, expert {g} ({n_rows} rows) of {w.meta['G']}, N={N}, K={K}"
-    return oracle_rows(fn, n_rows, 2.0 * N * K, budget_s, what)
+    kept = []
+
+    def timed_fn(rows):
+        kept.append((rows, fn(rows)))
+    out = oracle_rows(timed_fn, n_rows, 2.0 * N * K, budget_s, what)
+    if D is not None:
+        out["parity"] = _sample_parity(D, kept, fn, norms, r0, n_rows, N, kind != "grouped")
+    return out
+
+
+def _sample_parity(D, kept, fn, norms, r0, n_rows, N, corner):
+    """Normalised error of the GPU output against the oracle rows already computed
+    (and, for the dense shapes, the last 128x128 tile)."""
+    import numpy as np
+    import oracle
+    import torch
+    Dh = D.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    blocks = [(rows, None, vals) for rows, vals in kept]
+    if corner:
+        rows = np.arange(max(0, n_rows - 128), n_rows)
+        cols = np.arange(max(0, N - 128), N)
+        blocks.append((rows, cols, fn(rows, cols)))
+    worst, n_over, n_out = 0.0, 0, 0
+    for rows, cols, vals in blocks:
+        cols_i = np.arange(N) if cols is None else cols
+        na, nb = norms(rows, cols_i)
+        got = Dh[np.ix_(r0 + np.asarray(rows), cols_i)]
+        got = (got.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        want = (oracle.bf16_rne(vals).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        den = na[:, None] * nb[None, :]
+        err = np.abs(got - want) / np.where(den > 0, den, 1.0)
+        err = np.where(den > 0, err, np.where(got == want, 0.0, np.inf))
+        worst = max(worst, float(err.max()) if err.size else 0.0)
+        n_over += int((err > 1e-3).sum())
+        n_out += err.size
+    return {"outputs": n_out, "max_normalised_error": worst, "over_1e-3": n_over,
+            "tolerance": 1e-3, "what": "the oracle's sampled rows x all columns" +
+            (", and the last 128x128 tile" if corner else "")}
 
 
 def _stats(us):
@@ -649,7 +698,8 @@ def main():
     cpu = None
     if cpu_kinds and args.cpu_budget > 0:
         base = per["bf16"]["cpu_oracle"]
-        cpu = {k: base[k] for k in ("value", "unit", "cores", "kind", "sample")}
+        cpu = {k: base[k] for k in ("value", "unit", "cores", "kind", "sample", "parity")
+               if k in base}
         cpu["host"] = host_info()
         cpu["per_config"] = {k: per[k]["cpu_oracle"] for k in cpu_kinds}
 

@@ -114,3 +114,31 @@ def test_cpu_sample_times_the_oracle_on_the_case_inputs(kind):
 def test_host_info_names_cores_and_model():
     h = bench.host_info()
     assert h["nproc"] >= 1 and h["usable_cpus"] >= 1
+
+
+def test_sample_parity_counts_what_the_oracle_disagrees_with():
+    """bench.py compares the GPU output with the oracle rows its CPU sample computed:
+    an output equal to bf16(oracle) reads 0, a planted wrong element is counted."""
+    import numpy as np
+    import torch
+    import oracle
+    r = np.random.default_rng(3)
+    M, N, K = 200, 160, 64
+    A = (r.standard_normal((M, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    B = (r.standard_normal((N, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    fn = lambda rows, cols=None: oracle.gemm_bf16(A, B, rows=rows, cols=cols)
+    norms = lambda rows, cols: (oracle.row_norms("bf16", A, rows=rows),
+                                oracle.row_norms("bf16", B, rows=cols))
+    full = oracle.bf16_rne(fn(np.arange(M)))
+    D = torch.from_numpy(full.view(np.int16).copy()).view(torch.bfloat16)
+    kept = [(np.arange(0, 16), fn(np.arange(0, 16))), (np.arange(16, 80), fn(np.arange(16, 80)))]
+    rep = bench._sample_parity(D, kept, fn, norms, 0, M, N, True)
+    assert rep["outputs"] == 80 * N + 128 * 128 and rep["over_1e-3"] == 0
+    assert rep["max_normalised_error"] == 0.0
+    bad = full.copy()
+    bad[5, 7] ^= 0x4000                      # a large change in one output
+    bad[M - 1, N - 1] ^= 0x4000              # and one in the last tile
+    D = torch.from_numpy(bad.view(np.int16).copy()).view(torch.bfloat16)
+    rep = bench._sample_parity(D, kept, fn, norms, 0, M, N, True)
+    assert rep["over_1e-3"] == 2
+
