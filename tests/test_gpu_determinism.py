@@ -1,9 +1,9 @@
-"""Run-to-run bitwise determinism of the grouped launches (the dense GEMMs are
-covered in test_gpu_parity.py): the persistent grid, the expert search and the
-SwiGLU epilogue must not make an output depend on scheduling.  Each case runs
-twice into freshly filled outputs at the shapes the benchmark times; every
-written row must agree bit for bit, and rows outside every expert must keep the
-fill."""
+"""Run-to-run bitwise determinism of the grouped, masked, FFN, quantiser and MQA
+launches (the dense GEMMs are covered in test_gpu_parity.py): the persistent
+grid, the expert search, the SwiGLU epilogue and the MQA key ranges must not make
+an output depend on scheduling.  Each case runs twice into freshly filled outputs
+at the shapes the benchmark times; every written output must agree bit for bit,
+and rows outside every expert must keep the fill."""
 import numpy as np
 import pytest
 import torch
@@ -101,3 +101,40 @@ def test_moe_ffn_workload_deterministic():
     assert torch.equal(ys[0][0], ys[1][0]) and torch.equal(ys[0][1], ys[1][1])
     off = t["offsets"].cpu().numpy()
     assert not np.any(d1[off[0]:off[-1]] == FILL)
+
+
+@pytest.mark.parametrize("name", ["mqa_prefill_fp8", "mqa_prefill_fp4", "mqa_decode_fp8",
+                                  "mqa_decode_fp4"])
+def test_mqa_workload_deterministic(name):
+    """The MQA logits at the benchmark's shapes (workgroups over 4096-key ranges in
+    prefill, per-request key rings in decode): two runs, the same bits."""
+    _say(f"determinism: {name}")
+    fmt = name.rsplit("_", 1)[1]
+    w = workloads.make(name, device=DEV)
+    t, m = w.tensors, w.meta
+    T, S = t["W"].shape[0], m["S"]
+    sfq = bsg.ensure_packed(t["sfq"], t["sfq"].shape[0], t["sfq"].shape[1])
+    sfk = bsg.ensure_packed(t["sfk"], t["sfk"].shape[0], t["sfk"].shape[1])
+    outs = []
+    for _ in range(2):
+        L = torch.full((T, S), 12345.0, dtype=torch.float32, device=DEV)
+        bsg.mqa_logits(fmt, t["Q"], sfq, t["K"], sfk, t["W"], t["ks"], t["ke"], S,
+                       q_per_group=m["q_per_group"], group_rows=m["group_rows"], out=L)
+        torch.cuda.synchronize()
+        outs.append(L.view(torch.int32).cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+    assert not np.any(outs[0] == np.float32(12345.0).view(np.int32)), "an output was not written"
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
+def test_quantiser_workload_deterministic(fmt):
+    _say(f"determinism: quantiser {fmt} on 16384x7168 activations")
+    w = workloads.make("act_moe", device=DEV)
+    X = w.tensors["X"]
+    fn = bsg.quantize_fp4_per_token if fmt == "fp4" else bsg.quantize_fp8_per_token
+    outs = []
+    for _ in range(2):
+        q, s = fn(X)
+        torch.cuda.synchronize()
+        outs.append((q.view(torch.uint8).cpu().numpy(), s.cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
