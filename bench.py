@@ -44,13 +44,19 @@ The masked M-grouped FP8 GEMM runs a decode-sized case: 48 local experts of
 bound by reading the experts' weights, so GB/s is reported beside TFLOPS.
 
 The MQA logits kernels (64 heads of 128, FP8 and FP4) run a prefill of one
-4096-token sequence with causal windows (TFLOPS of the scores' dot products
-against the dtype's MFMA peak) and a decode of 128 requests over 32768-token
-contexts (GB/s against HBM: each request streams its own keys).
+4096-token sequence with causal windows (its roofline: the vector ALU's max and
+multiply-add per window pair and head; TFLOPS of the scores' dot products beside
+it) and a decode of 128 requests over 32768-token contexts (GB/s against HBM:
+each request streams its own keys).
 
 `cpu_baseline` times the CPU oracle (plain C, fp64, every host thread) on a
 bounded row sample of the BF16 case's own inputs; `per_config` adds the FP8, FP4
-and grouped FP8 cases, and `host` the core count and CPU model.
+and grouped FP8 cases, and `host` the core count and CPU model.  The oracle's
+rows are also compared with the GPU output of the timed calls (`parity`).
+
+`--operands zeros` runs the dense cases on all-zero codes instead of the random
+draws: the same instruction stream at a lower power draw, an experiment on the
+clock, never the benchmark.
 """
 from __future__ import annotations
 
