@@ -5,10 +5,14 @@
  *   - BF16 x BF16,
  *   - FP8 e4m3 x e4m3 with UE8M0 block scales,
  *   - FP4 e2m1 x e2m1 with UE8M0 block scales,
- *   - an M-grouped FP8 variant for mixture-of-experts layers,
+ *   - M-grouped variants (FP8, BF16, FP4, and a masked FP8 layout) for
+ *     mixture-of-experts layers,
  * always accumulating in fp32 and writing bf16 (round to nearest even).  It also
  * packs and unpacks UE8M0 scales into the int16, MN-major layout the scaled GEMMs
- * read.
+ * read, quantises bf16 rows into that format (the producer side), runs the MoE
+ * FFN core on one GPU's share (grouped up-projection with SwiGLU and FP8
+ * requantisation fused into its epilogue, grouped down-projection), and computes
+ * the MQA logits of a lightning-indexer step in FP8 and FP4.
  *
  * The pages this follows list BF16, FP8 and FP4 dense GEMM plus grouped (MoE)
  * GEMM as the library's coverage ("DeepGEMM-Ascend cobre quantas operacoes no
@@ -31,9 +35,11 @@
  *  - Packed scales: int16 P[ceil(Kb/2)][ld_sf] where Kb is the number of K-blocks;
  *    element (kp, mn) sits at kp*ld_sf + mn, its low byte is K-block 2kp and its
  *    high byte K-block 2kp+1 (0x7F when Kb is odd).  "Scale rows" (mn) are the
- *    rows of A, the 128-row blocks of B (FP8) or the rows of B (FP4).
+ *    rows of A, the 128-row blocks of B (FP8; its rows with sfb_gran_mn = 1) or
+ *    the rows of B (FP4).
  *  - Every pointer is a device pointer owned by the caller; the library allocates
- *    nothing, keeps no state between calls and never synchronises.  Work is
+ *    nothing, keeps no state between calls (apart from the fixed device array of
+ *    moe_ffn_fp8_noalloc) and never synchronises.  Work is
  *    enqueued on `stream` (a hipStream_t; NULL is the default stream) and is
  *    complete when the stream says so.  The one exception is the scale
  *    pack/unpack pair: there NULL means host pointers and a synchronous call.
