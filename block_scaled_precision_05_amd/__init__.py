@@ -62,6 +62,7 @@ EXPORTS = {
                                   _i64, _vp, _i32, _i64, _i64, _i64, _vp],
     "pack_ue8m0_scales": [_vp, _i64, _i64, _i64, _vp, _i64, _vp],
     "unpack_ue8m0_scales": [_vp, _i64, _i64, _i64, _vp, _i64, _vp],
+    "pack_ue8m0_scales_f32": [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp],
     "quantize_fp8_per_token": [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i32, _vp],
     "quantize_fp4_per_token": [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i32, _vp],
     "swiglu_quantize_fp8": [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i32, _vp],
@@ -359,6 +360,28 @@ def pack_ue8m0_scales(sf: torch.Tensor, ld_packed: int | None = None, out=None, 
     return out
 
 
+def pack_ue8m0_scales_f32(sf: torch.Tensor, ld_packed: int | None = None, out=None, stream=None):
+    """fp32 [mn, kb] holding powers of two 2^e (-127 <= e <= 127) -> packed int16
+    [ceil(kb/2), ld_packed], exactly; raises ValueError if any value has no UE8M0
+    code (the library counts them; for GPU tensors reading the count back
+    synchronises the stream)."""
+    if sf.dtype != torch.float32 or sf.dim() != 2:
+        raise TypeError("sf must be a 2-D float32 tensor")
+    mn, kb = sf.shape
+    ldp = mn if ld_packed is None else int(ld_packed)
+    if out is None:
+        out = torch.empty(((kb + 1) // 2, ldp), dtype=torch.int16, device=sf.device)
+    count = torch.zeros(1, dtype=torch.int32, device=sf.device)
+    st = _pack_stream((sf, out, count), stream)
+    _check("pack_ue8m0_scales_f32", lib().pack_ue8m0_scales_f32(
+        _ptr(sf), mn, kb, _mat(sf, "sf"), _ptr(out), _mat(out, "out"), _ptr(count), st))
+    bad = int(count.item())
+    if bad:
+        raise ValueError(f"{bad} scale factors are not powers of two in [2^-127, 2^127]: "
+                         "UE8M0 cannot represent them (rounding scales is the quantiser's job)")
+    return out
+
+
 def unpack_ue8m0_scales(packed: torch.Tensor, mn: int, kb: int, out=None, stream=None):
     """packed int16 [ceil(kb/2), >=mn] -> uint8 [mn, kb] (on the GPU or, for host
     tensors, on the calling thread)."""
@@ -380,8 +403,9 @@ def is_packed(sf: torch.Tensor, mn: int, kb: int) -> bool:
 
 def ensure_packed(sf: torch.Tensor, mn: int, kb: int, stream=None) -> torch.Tensor:
     """Reuse-or-convert, decided on every call: an already packed tensor is
-    returned as it is; UE8M0 bytes ([mn, kb] uint8 or float8_e8m0fnu) are packed
-    on the GPU.  The pages describe this helper and note the conversion costs
+    returned as it is; UE8M0 bytes ([mn, kb] uint8 or float8_e8m0fnu) are packed,
+    and fp32 powers of two ([mn, kb]) converted exactly and packed (anything else
+    in fp32 raises: UE8M0 cannot hold it), on the GPU for GPU tensors.  The pages describe this helper and note the conversion costs
     time when it is needed ("DeepGEMM-Ascend cobre quantas operacoes no Ascend
     950?", section "Fatores de escala FP8 e o formato UE8M0 no Ascend")."""
     if is_packed(sf, mn, kb):
@@ -389,9 +413,11 @@ def ensure_packed(sf: torch.Tensor, mn: int, kb: int, stream=None) -> torch.Tens
     if sf.dtype in (torch.uint8, torch.float8_e8m0fnu) and sf.dim() == 2 and \
             tuple(sf.shape) == (mn, kb):
         return pack_ue8m0_scales(sf, stream=stream if sf.is_cuda else None)
+    if sf.dtype == torch.float32 and sf.dim() == 2 and tuple(sf.shape) == (mn, kb):
+        return pack_ue8m0_scales_f32(sf, stream=stream if sf.is_cuda else None)
     raise TypeError(
-        f"scales must be packed int16 [{(kb + 1) // 2}, >={mn}] or UE8M0 bytes [{mn}, {kb}]; "
-        f"got {sf.dtype} {tuple(sf.shape)}")
+        f"scales must be packed int16 [{(kb + 1) // 2}, >={mn}], UE8M0 bytes [{mn}, {kb}] or "
+        f"fp32 powers of two [{mn}, {kb}]; got {sf.dtype} {tuple(sf.shape)}")
 
 
 def _quantize(fn: str, X, rule, q_cols, gk, out, sf_out, ld_sf, stream):

@@ -35,6 +35,40 @@ __global__ void pack_kernel(const uint8_t* __restrict__ sf, int64_t mn, int64_t 
   }
 }
 
+// fp32 scale factors (exact powers of two, as fp32 scale tensors of block-scaled
+// operands hold them) -> UE8M0 byte: the exponent field of a positive normal with
+// zero mantissa is the byte itself; 2^-127 is the fp32 subnormal 0x00400000 and
+// gives byte 0.  Anything else (not a power of two, <= 0, inf, NaN, below 2^-127)
+// has no UE8M0 code: it is counted as inexact and gets its exponent field.
+__host__ __device__ inline uint32_t ue8m0_of_f32(uint32_t bits, bool& exact) {
+  const uint32_t e = (bits >> 23) & 0xFF;
+  if (bits == 0x00400000u) {
+    exact = true;
+    return 0;
+  }
+  exact = (bits & 0x807FFFFFu) == 0 && e >= 1 && e <= 254;
+  return e;
+}
+
+__global__ void pack_f32_kernel(const float* __restrict__ sf, int64_t mn, int64_t kb, int64_t ld_sf,
+                                int16_t* __restrict__ packed, int64_t ld_packed,
+                                int32_t* __restrict__ inexact) {
+  const int64_t kp_n = (kb + 1) / 2;
+  const int64_t total = kp_n * mn;
+  int bad = 0;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t kp = idx / mn, r = idx - kp * mn;
+    bool ex_lo = true, ex_hi = true;
+    const uint32_t lo = ue8m0_of_f32(__float_as_uint(sf[r * ld_sf + 2 * kp]), ex_lo);
+    const uint32_t hi =
+        (2 * kp + 1 < kb) ? ue8m0_of_f32(__float_as_uint(sf[r * ld_sf + 2 * kp + 1]), ex_hi) : 0x7Fu;
+    bad += !ex_lo + !ex_hi;
+    packed[kp * ld_packed + r] = (int16_t)(uint16_t)(lo | (hi << 8));
+  }
+  if (inexact && bad) atomicAdd(inexact, bad);
+}
+
 __global__ void unpack_kernel(const int16_t* __restrict__ packed, int64_t mn, int64_t kb,
                               int64_t ld_packed, uint8_t* __restrict__ sf, int64_t ld_sf) {
   const int64_t kp_n = (kb + 1) / 2;
@@ -529,6 +563,43 @@ int pack_ue8m0_scales(const uint8_t* sf, int64_t mn, int64_t kb, int64_t ld_sf, 
     return BSG_OK;
   }
   return launch_pack(false, sf, mn, kb, ld_sf, packed, ld_packed, stream);
+}
+
+int pack_ue8m0_scales_f32(const float* sf, int64_t mn, int64_t kb, int64_t ld_sf, int16_t* packed,
+                          int64_t ld_packed, int32_t* inexact, void* stream) {
+  if (mn < 0 || kb < 0) return BSG_ERR_INVALID_ARG;
+  if (mn == 0 || kb == 0) return BSG_OK;
+  if (!sf || !packed || ld_sf < kb || ld_packed < mn) return BSG_ERR_INVALID_ARG;
+  if (((uintptr_t)packed & 1) || ((uintptr_t)sf & 3) || ((uintptr_t)inexact & 3))
+    return BSG_ERR_MISALIGNED;
+  if (!stream) {
+    int32_t bad = 0;
+    for (int64_t kp = 0; kp < (kb + 1) / 2; ++kp)
+      for (int64_t r = 0; r < mn; ++r) {
+        bool ex_lo = true, ex_hi = true;
+        uint32_t b;
+        const float* p = sf + r * ld_sf + 2 * kp;
+        __builtin_memcpy(&b, p, 4);
+        const uint32_t lo = bsg::ue8m0_of_f32(b, ex_lo);
+        uint32_t hi = 0x7Fu;
+        if (2 * kp + 1 < kb) {
+          __builtin_memcpy(&b, p + 1, 4);
+          hi = bsg::ue8m0_of_f32(b, ex_hi);
+        }
+        bad += !ex_lo + !ex_hi;
+        packed[kp * ld_packed + r] = (int16_t)(uint16_t)(lo | (hi << 8));
+      }
+    if (inexact) *inexact += bad;
+    return BSG_OK;
+  }
+  const int64_t total = (kb + 1) / 2 * mn;
+  const int threads = 256;
+  int64_t blocks = (total + threads - 1) / threads;
+  if (blocks > 65536) blocks = 65536;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(bsg::pack_f32_kernel, dim3((unsigned)blocks), dim3(threads), 0,
+                     (hipStream_t)stream, sf, mn, kb, ld_sf, packed, ld_packed, inexact);
+  return hipGetLastError() == hipSuccess ? BSG_OK : BSG_ERR_HIP;
 }
 
 int unpack_ue8m0_scales(const int16_t* packed, int64_t mn, int64_t kb, int64_t ld_packed,

@@ -200,6 +200,22 @@ int m_grouped_gemm_fp8_masked(const void* A, int64_t lda, const int16_t* sfa, in
 int pack_ue8m0_scales(const uint8_t* sf, int64_t mn, int64_t kb, int64_t ld_sf,
                       int16_t* packed, int64_t ld_packed, void* stream);
 
+/* Pack fp32 scale factors: the conversion half of the same reuse-or-convert helper
+ * for scales that arrive as fp32 tensors holding powers of two (the form in which
+ * block-scaled operands often carry their factors; the pages' helper converts
+ * whatever layout it is given into the packed one: first page, section "Fatores de
+ * escala FP8 e o formato UE8M0 no Ascend").
+ *   sf: fp32 [mn][ld_sf], K-blocks contiguous -> packed as in pack_ue8m0_scales.
+ *   A value 2^e with -127 <= e <= 127 becomes the byte e + 127 exactly (2^-127 is
+ *   the fp32 subnormal 0x00400000).  Any other value (not a power of two, zero or
+ *   negative, inf, NaN, below 2^-127) has no UE8M0 code: its byte is unspecified
+ *   and it is counted into *inexact (a DEVICE int32 with stream != NULL, added to
+ *   atomically, so the caller zeroes it first; a HOST int32 with stream == NULL;
+ *   NULL: not counted).
+ *   Stream rule, requirements and errors as pack_ue8m0_scales; sf 4-byte aligned. */
+int pack_ue8m0_scales_f32(const float* sf, int64_t mn, int64_t kb, int64_t ld_sf,
+                          int16_t* packed, int64_t ld_packed, int32_t* inexact, void* stream);
+
 /* Inverse of pack_ue8m0_scales, with the same stream rule (NULL: host pointers,
  * synchronous; otherwise device pointers and a kernel on `stream`): packed int16
  * [ceil(kb/2)][ld_packed] -> sf uint8 [mn][ld_sf]; the 0x7F filler byte of an odd

@@ -415,3 +415,53 @@ def test_mqa_validation(name, row):
     assert f(*empty) == bsg.BSG_OK
     empty = list(args); empty[15] = 0                               # S = 0: no-op
     assert f(*empty) == bsg.BSG_OK
+
+
+def _f32_scales(r, mn, kb, ld):
+    """fp32 powers of two 2^e over the whole UE8M0 range (e = -127 .. 127), and the
+    bytes e + 127 they must become."""
+    import numpy as np
+    e = r.integers(-127, 128, (mn, ld))
+    e[0, :min(kb, 3)] = [-127, 127, 0][:min(kb, 3)]
+    sf = np.ldexp(np.ones((mn, ld)), e).astype(np.float32)   # 2^-127 is an fp32 subnormal
+    return sf, (e + 127).astype(np.uint8)
+
+
+@pytest.mark.parametrize("mn,kb,ld_sf,ldp", [(1, 1, 1, 1), (5, 3, 6, 9), (37, 8, 8, 40)])
+def test_host_pack_f32_is_exact(mn, kb, ld_sf, ldp):
+    """pack_ue8m0_scales_f32(..., NULL) turns fp32 powers of two into their UE8M0
+    bytes exactly (2^-127 and 2^127 included) and packs them as the oracle does."""
+    import numpy as np
+    import oracle
+    L = bsg.lib()
+    r = np.random.default_rng(mn + 10 * kb)
+    sf, want_bytes = _f32_scales(r, mn, kb, ld_sf)
+    packed = np.full(((kb + 1) // 2, ldp), 0x5A5A, dtype=np.int16)
+    bad = np.zeros(1, dtype=np.int32)
+    assert L.pack_ue8m0_scales_f32(_np_ptr(sf), mn, kb, ld_sf, _np_ptr(packed), ldp,
+                                   _np_ptr(bad), None) == bsg.BSG_OK
+    assert bad[0] == 0
+    want = oracle.pack_scales(np.ascontiguousarray(want_bytes[:, :kb]), ld_packed=ldp)
+    assert np.array_equal(packed[:, :mn], want[:, :mn])
+    assert np.all(packed[:, mn:] == 0x5A5A)
+
+
+def test_host_pack_f32_counts_values_without_a_code():
+    import numpy as np
+    import torch
+    L = bsg.lib()
+    vals = np.array([[3.0, 0.0, -2.0, np.inf], [np.nan, 2.0 ** -128, 1.5, 0.25]], dtype=np.float32)
+    packed = np.zeros((2, 2), dtype=np.int16)
+    bad = np.zeros(1, dtype=np.int32)
+    assert L.pack_ue8m0_scales_f32(_np_ptr(vals), 2, 4, 4, _np_ptr(packed), 2, _np_ptr(bad),
+                                   None) == bsg.BSG_OK
+    assert bad[0] == 7                      # only 0.25 has a code
+    assert (int(packed[1, 1]) >> 8) & 0xFF == 125
+    # the binding and the reuse-or-convert helper refuse them
+    with pytest.raises(ValueError):
+        bsg.pack_ue8m0_scales_f32(torch.from_numpy(vals))
+    with pytest.raises(ValueError):
+        bsg.ensure_packed(torch.from_numpy(vals), 2, 4)
+    ok = torch.from_numpy(np.array([[0.5, 4.0, 1.0]], dtype=np.float32))
+    p = bsg.ensure_packed(ok, 1, 3)
+    assert p.view(torch.int16).numpy().view(np.uint16).tolist() == [[0x817E], [0x7F7F]]

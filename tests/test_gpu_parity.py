@@ -124,8 +124,33 @@ def test_ensure_packed_reuses_or_converts():
     assert bsg.ensure_packed(p, 64, 6) is p
     e8 = sf.view(torch.float8_e8m0fnu)
     assert torch.equal(bsg.ensure_packed(e8, 64, 6), p)
+    # fp32 scale factors: the powers of two those bytes stand for convert exactly
+    # (byte 255, NaN in UE8M0, stays out: it has no fp32 power of two)
+    ok = sf.clamp(max=254)
+    f32 = torch.ldexp(torch.ones(64, 6, dtype=torch.float64, device=DEV),
+                      ok.to(torch.int64) - 127).to(torch.float32)
+    assert torch.equal(bsg.ensure_packed(f32, 64, 6), bsg.ensure_packed(ok, 64, 6))
+    with pytest.raises(ValueError):         # byte values read as fp32: not powers of two
+        bsg.ensure_packed(sf.float() + 3.0, 64, 6)
     with pytest.raises(TypeError):
-        bsg.ensure_packed(sf.float(), 64, 6)
+        bsg.ensure_packed(sf.to(torch.int64), 64, 6)
+
+
+def test_fp32_scales_feed_the_gemm_like_their_bytes():
+    """FP8 GEMM with scales given as fp32 powers of two (converted on the GPU by the
+    library) gives the bits of the same scales given as UE8M0 bytes."""
+    w = workloads.dense("fp8", 300, 260, 640, 7777, device=DEV)
+    t = w.tensors
+    M, N, K = 300, 260, 640
+    fa = torch.ldexp(torch.ones(t["sfa"].shape, dtype=torch.float64, device=DEV),
+                     t["sfa"].to(torch.int64) - 127).to(torch.float32)
+    fb = torch.ldexp(torch.ones(t["sfb"].shape, dtype=torch.float64, device=DEV),
+                     t["sfb"].to(torch.int64) - 127).to(torch.float32)
+    D1 = bsg.gemm_fp8_blockscaled(t["A"], bsg.ensure_packed(fa, M, K // 128), t["B"],
+                                  bsg.ensure_packed(fb, (N + 127) // 128, K // 128))
+    D2 = run_gpu("fp8", t)
+    torch.cuda.synchronize()
+    assert np.array_equal(gpu_bits(D1), gpu_bits(D2))
 
 
 # ---------------------------------------------------------------------------
