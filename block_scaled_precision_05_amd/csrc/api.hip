@@ -187,12 +187,19 @@ static int check_dense(const void* A, int64_t lda, const void* B, int64_t ldb, c
   return BSG_OK;
 }
 
+// Packed scale arrays of kp = ceil(K / kgran / 2) rows.  The kernels address them
+// with 32-bit byte offsets, up to one packed row past the last (FP4 lane groups on a
+// K tail), so 2 (kp + 1) ld bytes must stay inside 31 bits.
 static int check_scales(const int16_t* sfa, int64_t ld_sfa, int64_t rows_a, const int16_t* sfb,
-                        int64_t ld_sfb, int64_t rows_b, int64_t K) {
+                        int64_t ld_sfb, int64_t rows_b, int64_t K, int64_t kgran) {
   if (K == 0) return BSG_OK;
   if (!sfa || !sfb) return BSG_ERR_INVALID_ARG;
   if (ld_sfa < rows_a || ld_sfb < rows_b) return BSG_ERR_INVALID_ARG;
   if (((uintptr_t)sfa & 1) || ((uintptr_t)sfb & 1)) return BSG_ERR_MISALIGNED;
+  const int64_t kp = (K / kgran + 1) / 2;
+  if (ld_sfa > kMaxDim || ld_sfb > kMaxDim || 2 * (kp + 1) * ld_sfa > kMaxDim ||
+      2 * (kp + 1) * ld_sfb > kMaxDim)
+    return BSG_ERR_UNSUPPORTED_SHAPE;
   return BSG_OK;
 }
 
@@ -211,7 +218,7 @@ int grouped_check(int kind, const void* A, int64_t lda, const int16_t* sfa, int6
   int64_t kp = 0;
   if (kind != KIND_BF16) {
     const int64_t b_rows = kind == KIND_FP8 ? (N + 127) / 128 : N;
-    st = check_scales(sfa, ld_sfa, M_total, sfb, ld_sfb, b_rows, K);
+    st = check_scales(sfa, ld_sfa, M_total, sfb, ld_sfb, b_rows, K, gran);
     if (st != BSG_OK) return st;
     kp = (K / gran + 1) / 2;
   }
@@ -274,7 +281,7 @@ int gemm_fp8_blockscaled(const void* A, int64_t lda, const int16_t* sfa, int64_t
   int st = check_dense(A, lda, B, ldb, D, ldd, M, N, K, 128, K, 1);
   if (st != BSG_OK || M == 0 || N == 0) return st;
   const int64_t sfb_rows = (N + sfb_gran_mn - 1) / sfb_gran_mn;
-  st = check_scales(sfa, ld_sfa, M, sfb, ld_sfb, sfb_rows, K);
+  st = check_scales(sfa, ld_sfa, M, sfb, ld_sfb, sfb_rows, K, 128);
   if (st != BSG_OK) return st;
   GemmArgs a = {};
   a.A = (const uint8_t*)A;
@@ -308,7 +315,7 @@ int gemm_fp4_blockscaled(const void* A, int64_t lda, const int16_t* sfa, int64_t
                          void* D, int64_t ldd, int64_t M, int64_t N, int64_t K, void* stream) {
   int st = check_dense(A, lda, B, ldb, D, ldd, M, N, K, 32, K / 2, 1);
   if (st != BSG_OK || M == 0 || N == 0) return st;
-  st = check_scales(sfa, ld_sfa, M, sfb, ld_sfb, N, K);
+  st = check_scales(sfa, ld_sfa, M, sfb, ld_sfb, N, K, 32);
   if (st != BSG_OK) return st;
   GemmArgs a = {};
   a.A = (const uint8_t*)A;

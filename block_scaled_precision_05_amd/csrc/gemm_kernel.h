@@ -198,9 +198,10 @@ struct GemmTile {
   // word per fragment, the lane's own row.
   static constexpr bool ONE_B_SCALE = !B_ROW && TN <= 128 && 128 % TN == 0 && BN % 128 == 0;
   // A fragments double-buffered in registers (the next k-step's read beside the
-  // current MFMAs) unless two waves share a SIMD on the halved register budget:
-  // then the MFMAs come first and the other wave covers the read's latency.
-  static constexpr bool DBA = NW <= 4 || KIND == KIND_BF16;
+  // current MFMAs) unless two waves share a SIMD on the halved register budget and
+  // the fragments do not fit it (FP8: 8 registers each): then the MFMAs come first
+  // and the other wave covers the read's latency.
+  static constexpr bool DBA = NW <= 4 || KIND == KIND_BF16 || KIND == KIND_FP4;
   static constexpr int NSB = KIND == KIND_FP8 ? (ONE_B_SCALE ? 1 : FN) : FN;
   // packed scale words per lane per fragment per stage: FP8 one (the K-block's
   // pair), FP4 NC/4 (lane group lg takes NC/2 K-blocks of 32)
@@ -258,18 +259,31 @@ struct GemmTile {
   static constexpr int chunk_vmem(int g) {
     return 2 * QPC + (chunk_at(g) == 0 || (chunk_at(g) == 1 && !SHARED_SCALES) ? NSC : 0);
   }
-  // Copies of one wave issued after the last copy of stage st, counted at the
-  // moment the barrier of stage s waits (s = -1: the prologue's wait for stage
-  // 0).  Replays the kernel's issue order: every chunk due at a k-step g < 0 is
-  // issued by the prologue, the rest at their k-steps, the barrier k-step's chunk
-  // after its wait.  Non-paired: stage s+NS is issued whole at the barrier of s.
-  static constexpr int copies_after(int s, int st) {
+  // Vector memory loads of one wave issued after the last copy of stage st,
+  // counted at the moment the barrier of stage s waits (s = -1: the prologue's
+  // wait for stage 0).  Replays the kernel's issue order: every chunk due at a
+  // k-step g < 0 is issued by the prologue, the rest at their k-steps, the barrier
+  // k-step's chunk after its wait; a chunk that loads scale words issues them
+  // before its copies.  Non-paired: stage s+NS (its scale words, then its copies)
+  // is issued whole at the barrier of s.  The scale loads count like the copies:
+  // vmcnt counts every load, so leaving them out would make each barrier wait for
+  // as many copies of later stages as there are scale loads after stage st (FP4
+  // four, FP8 two: most of a stage, the ring one stage shallower; counting them
+  // took 3 to 6% off the FP4 and grouped FP8 GEMMs).  A chunk's loads stay in
+  // its k-step (a scheduling barrier closes each), and inside the chunk holding
+  // stage st's last copy the compiler may only move scale loads after it, which
+  // makes the wait stricter, never looser.
+  static constexpr int copies_after(int s, int st, bool sc = true) {
+    const int nsc = sc ? NSC : 0;
     int issued = 0, last = -1;
     if (!PR) {
-      for (int t = 0; t < NS; ++t)
+      for (int t = 0; t < NS; ++t) {
+        issued += nsc;
         for (int q = 0; q < N_DMA; ++q) { if (t == st) last = issued; ++issued; }
+      }
       for (int b = 0; b <= s; ++b) {
         if (b == s) return issued - 1 - last;
+        issued += nsc;
         for (int q = 0; q < N_DMA; ++q) { if (b + NS == st) last = issued; ++issued; }
       }
       return issued - 1 - last;
@@ -277,6 +291,7 @@ struct GemmTile {
     auto chunk = [&](int g) {
       const int c = chunk_at(g), t = pair_start(g) + NS - 1;
       if (t < 0) return;
+      if (c == 0 || (c == 1 && !SHARED_SCALES)) issued += nsc;
       for (int q = c * QPC; q < (c + 1) * QPC; ++q) {
         if (t == st) last = issued;
         ++issued;
@@ -292,19 +307,22 @@ struct GemmTile {
     }
   }
   // vmcnt for the barrier of stage s (position si in the round): safe for every
-  // round (the first round may differ from the steady state)
-  static constexpr int wait_at(int si) {
-    const int a = copies_after(si, si + 1), b = copies_after(si + U, si + U + 1),
-              c = copies_after(si + 2 * U, si + 2 * U + 1);
+  // round (the first round may differ from the steady state).  sc: the wave
+  // loads scale words (a wave with no MFMAs on its tile loads none).
+  static constexpr int wait_at(int si, bool sc) {
+    const int a = copies_after(si, si + 1, sc), b = copies_after(si + U, si + U + 1, sc),
+              c = copies_after(si + 2 * U, si + 2 * U + 1, sc);
     const int m = a < b ? a : b;
     return m < c ? m : c;
   }
   static constexpr bool steady(int si) {
-    return copies_after(si + U, si + U + 1) == copies_after(si + 2 * U, si + 2 * U + 1);
+    return copies_after(si + U, si + U + 1, true) == copies_after(si + 2 * U, si + 2 * U + 1, true) &&
+           copies_after(si + U, si + U + 1, false) == copies_after(si + 2 * U, si + 2 * U + 1, false);
   }
-  static constexpr int wait_prologue() { return copies_after(-1, 0); }
-  static_assert(wait_at(0) >= 0 && wait_at(0) <= 63 && wait_at(1) >= 0 && wait_at(1) <= 63 &&
-                    wait_prologue() >= 0 && wait_prologue() <= 63,
+  static constexpr int wait_prologue(bool sc) { return copies_after(-1, 0, sc); }
+  static_assert(wait_at(0, true) >= 0 && wait_at(0, true) <= 63 && wait_at(1, true) >= 0 &&
+                    wait_at(1, true) <= 63 && wait_prologue(true) >= 0 && wait_prologue(true) <= 63 &&
+                    wait_at(0, false) >= 0 && wait_at(1, false) >= 0 && wait_prologue(false) >= 0,
                 "vmcnt is 6 bits");
   // LDS position of 16-byte chunk c of tile row r: the chunk is XOR-swizzled with
   // (r / RPS) % NC so that the 16 lanes of one ds_read_b128 phase, reading one
@@ -612,7 +630,12 @@ void gemm_kernel(const GemmArgs args) {
           const int ci = q * T::NW + wave;
           const bool dummy = T::DUMMY && ci >= T::A_COPIES;
           const uint32_t qrow = (uint32_t)T::perm_a(q * T::NW * T::ROWS_PER_COPY);
-          const uint32_t off = (a_vbase + qrow * (uint32_t)args.lda + kb) | oob | (dummy ? kOOB : 0u);
+          // The row and K parts stay below 2^31 (256 rows of at most 2^31/256
+          // bytes), so OR-ing or adding the out-of-range bit give the same offset;
+          // the dense kernels run 1.7% faster (FP8) with the sum, the grouped ones
+          // 1% slower (the compiler allocates the registers differently).
+          const uint32_t off = GROUPED ? (a_vbase + qrow * (uint32_t)args.lda + kb) | oob | (dummy ? kOOB : 0u)
+                                       : a_vbase + qrow * (uint32_t)args.lda + (uint32_t)kb + (oob | (dummy ? kOOB : 0u));
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
               ra, (__attribute__((address_space(3))) void*)(dummy ? spare : sA + T::ROWS_PER_COPY * ci * SB),
               16, off, 0, 0, 0);
@@ -623,7 +646,8 @@ void gemm_kernel(const GemmArgs args) {
           const uint32_t qrow0 = (uint32_t)T::perm_b(qb * T::NW * T::ROWS_PER_COPY);
           // (SwiGLU epilogue: tile rows past BN/2 are up rows, inter rows further on)
           const uint32_t qrow = EPI && qrow0 >= (uint32_t)(BN / 2) ? qrow0 - BN / 2 + (uint32_t)args.inter : qrow0;
-          const uint32_t off = (b_vbase + qrow * (uint32_t)args.ldb + kb) | oob | (dummy ? kOOB : 0u);
+          const uint32_t off = GROUPED ? (b_vbase + qrow * (uint32_t)args.ldb + kb) | oob | (dummy ? kOOB : 0u)
+                                       : b_vbase + qrow * (uint32_t)args.ldb + (uint32_t)kb + (oob | (dummy ? kOOB : 0u));
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
               rb, (__attribute__((address_space(3))) void*)(dummy ? spare : sB + T::ROWS_PER_COPY * ci * SB),
               16, off, 0, 0, 0);
@@ -665,12 +689,17 @@ void gemm_kernel(const GemmArgs args) {
       const __amdgpu_buffer_rsrc_t rsb = make_rsrc(
           sfb, (uint32_t)(2 * ((int64_t)(args.kp_count - 1) * args.ld_sfb + b_rows)));
       // (FP4: the lane's fragment rows are 4*l32 .. 4*l32 + 3 of the wave block)
-      uint32_t sa_voff = 2u * (uint32_t)(m0 + wm * T::TM + (T::PERM_A ? 4 * l32 : l32));
+      // (FP4: lane group lg reads packed rows (NC/4)*lg further on)
+      const uint32_t ld_a = (uint32_t)args.ld_sfa, ld_b = (uint32_t)args.ld_sfb;
+      constexpr uint32_t lg_rows = KIND == KIND_FP4 ? NC / 4 : 0;
+      uint32_t sa_voff = 2u * (uint32_t)(m0 + wm * T::TM + (T::PERM_A ? 4 * l32 : l32)) +
+                         2u * lg_rows * (uint32_t)lg * ld_a;
       asm volatile("" : "+v"(sa_voff));
       const int brow0 = EPI && wn * T::TN >= BN / 2 ? args.inter + n0 + wn * T::TN - BN / 2 : n0 + wn * T::TN;
       uint32_t sb_voff = KIND == KIND_FP8 && !T::B_ROW
                              ? 2u * (uint32_t)(brow0 / 128)
-                             : 2u * (uint32_t)(n0 + wn * T::TN + (T::PERM_B ? FN * l32 : l32));
+                             : 2u * (uint32_t)(n0 + wn * T::TN + (T::PERM_B ? FN * l32 : l32)) +
+                                   2u * lg_rows * (uint32_t)lg * ld_b;
       asm volatile("" : "+v"(sb_voff));
       // Raw scale words of stage kt (packed int16, not decoded yet).
       //   FP8: K-block kt*SB/128, held in packed row kb/2, byte kb%2.
@@ -681,15 +710,26 @@ void gemm_kernel(const GemmArgs args) {
       // load, fragments 2i and 2i+1 in the low and high halves of dword i.
       uint16_t rs_a[NS][FM][SW > 0 ? SW : 1] = {}, rs_b[NS][NSB][SW > 0 ? SW : 1] = {};
       uint32_t rv_a[T::WIDE ? NS : 1][2] = {}, rv_b[T::WIDE ? NS : 1][2] = {};
+      // The barrier waits count these loads (a wave that runs the tile without MFMAs
+      // issues none), so every call must issue exactly its loads: each address is
+      // made opaque, so that no two calls merge (the clamped stages of the first
+      // round read the same words), and decode_scales keeps every result alive.
       auto load_scales = [&](int kt, auto slot) {
         constexpr int sl = decltype(slot)::value;
-        if constexpr (KIND != KIND_BF16) {
+        if constexpr (MM && KIND != KIND_BF16) {
 #pragma unroll
           for (int w = 0; w < SW; ++w) {
-            int kp = KIND == KIND_FP8 ? (kt * SB / 128) >> 1 : kt * (NC / 2) + (NC / 4) * lg + w;
-            kp = kp < args.kp_count ? kp : args.kp_count - 1;
-            const uint32_t va = sa_voff + 2u * (uint32_t)(kp * args.ld_sfa);
-            const uint32_t vb = sb_voff + 2u * (uint32_t)(kp * args.ld_sfb);
+            // Wave-uniform packed row (the lane group's part is in sa_voff / sb_voff).
+            // FP8 clamps it to the last packed row; FP4 lane group 1 may read one row
+            // past the end on a K tail, which the record count turns into zero
+            // words: those scales only meet zero operands.
+            int kp = KIND == KIND_FP8 ? (kt * SB / 128) >> 1 : kt * (NC / 2) + w;
+            if constexpr (KIND == KIND_FP8) kp = kp < args.kp_count ? kp : args.kp_count - 1;
+            kp = __builtin_amdgcn_readfirstlane(kp);
+            uint32_t va = sa_voff + 2u * (uint32_t)kp * ld_a;
+            uint32_t vb = sb_voff + 2u * (uint32_t)kp * ld_b;
+            uint32_t kq = 2u * (uint32_t)kp * ld_b;
+            asm volatile("" : "+v"(va), "+v"(vb), "+s"(kq));
             // fragment f's word: 2 bytes further on (permuted rows: adjacent) or
             // 64 bytes (32 rows) further on
             constexpr uint32_t fstep_a = T::PERM_A ? 2 : 64, fstep_b = T::PERM_B ? 2 : 64;
@@ -711,10 +751,13 @@ void gemm_kernel(const GemmArgs args) {
             } else {
 #pragma unroll
               for (int f = 0; f < NSB; ++f) {
-                if constexpr (KIND == KIND_FP8 && !T::ONE_B_SCALE && !T::B_ROW)
-                  rs_b[sl][f][w] = __builtin_amdgcn_raw_buffer_load_b16(
-                      rsb, 2u * (uint32_t)(((nrow0 + 32 * f) >> 7) + kp * args.ld_sfb), 0, 0);
-                else
+                if constexpr (KIND == KIND_FP8 && !T::ONE_B_SCALE && !T::B_ROW) {
+                  // (fragments in one 128-row block read the same word: opaque, so
+                  // that the loads stay apart)
+                  uint32_t o = 2u * (uint32_t)((nrow0 + 32 * f) >> 7) + kq;
+                  asm volatile("" : "+v"(o));
+                  rs_b[sl][f][w] = __builtin_amdgcn_raw_buffer_load_b16(rsb, o, 0, 0);
+                } else
                   rs_b[sl][f][w] = __builtin_amdgcn_raw_buffer_load_b16(rsb, vb + fstep_b * f, 0, 0);
               }
             }
@@ -742,6 +785,11 @@ void gemm_kernel(const GemmArgs args) {
           }
 #pragma unroll
           for (int f = 0; f < FN; ++f) sb[f] = ((uint32_t)rs_b[sl][T::ONE_B_SCALE ? 0 : f][0] >> sh) & 0xFF;
+          // (kept alive: a stage without MFMAs would otherwise drop its loads)
+#pragma unroll
+          for (int f = 0; f < (T::WIDE ? 2 : FM); ++f) asm volatile("" ::"v"(sa[f]));
+#pragma unroll
+          for (int f = 0; f < FN; ++f) asm volatile("" ::"v"(sb[f]));
         } else if constexpr (KIND == KIND_FP4) {
           if constexpr (T::WIDE) {
             sa[0] = rv_a[sl][0];
@@ -757,6 +805,10 @@ void gemm_kernel(const GemmArgs args) {
               sb[i] = (uint32_t)rs_b[sl][2 * i][0] | ((uint32_t)rs_b[sl][2 * i + 1][0] << 16);
             }
           }
+#pragma unroll
+          for (int i = 0; i < 2; ++i) asm volatile("" ::"v"(sa[i]));
+#pragma unroll
+          for (int i = 0; i < FN / 2; ++i) asm volatile("" ::"v"(sb[i]));
         }
       };
 
@@ -878,7 +930,7 @@ void gemm_kernel(const GemmArgs args) {
            ...);
         }(std::make_integer_sequence<int, NS>{});
       }
-      wait_vm_lds<T::wait_prologue()>();
+      wait_vm_lds<T::wait_prologue(MM)>();
       ring_barrier();
       decode_scales(-koff, std::integral_constant<int, 0>{}, sa_cur, sb_cur);
       read_frags(0, 0, fa[0], fb[0]);
@@ -925,9 +977,9 @@ void gemm_kernel(const GemmArgs args) {
             // across the barrier, and the compiler waits for each one just before
             // the first MFMA that uses its registers.
             if constexpr (PR && T::chunk_at(g) != 0)
-              wait_vm<T::wait_at(si)>();
+              wait_vm<T::wait_at(si, MM)>();
             else
-              wait_vm_lds<T::wait_at(si)>();
+              wait_vm_lds<T::wait_at(si, MM)>();
             ring_barrier();
             if constexpr (PR) {
               pair_chunk(std::integral_constant<int, g>{}, round);

@@ -112,6 +112,13 @@ def test_fp4_validation():
     a = list(ok_args)
     a[7] = 255             # ld_sfb < N
     assert f(*a) == bsg.BSG_ERR_INVALID_ARG
+    # packed scale arrays whose byte offsets (one packed row past the last
+    # included) leave 31 bits: 2 * (kp + 1) * ld with kp = 4 at K = 256
+    for i in (3, 7):
+        for ld in (1 << 40, 1 << 28, 214748365):   # the last: 10 * ld = 2^31 + 2
+            a = list(ok_args)
+            a[i] = ld
+            assert f(*a) == bsg.BSG_ERR_UNSUPPORTED_SHAPE, (i, ld)
 
 
 def test_grouped_validation():
@@ -135,6 +142,9 @@ def test_grouped_validation():
     assert f(*a) == bsg.BSG_ERR_INVALID_ARG
     a = list(ok)
     a[16] = 100            # K % 128
+    assert f(*a) == bsg.BSG_ERR_UNSUPPORTED_SHAPE
+    a = list(ok)
+    a[3] = 1 << 30         # packed A scales past 31-bit offsets (kp = 1: 4 * ld bytes)
     assert f(*a) == bsg.BSG_ERR_UNSUPPORTED_SHAPE
     a = list(ok)
     a[13] = 0              # no experts: no-op
