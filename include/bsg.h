@@ -50,7 +50,10 @@
  *    A, B nor the scales (their pointers may then be NULL).
  *  - A wrongly laid out scale array cannot be detected: it gives wrong numbers,
  *    not an error (the pages warn of exactly this failure mode).
- *  - Sizes: every leading dimension times 256 must stay below 2^31 bytes.
+ *  - Sizes: every leading dimension times 256 must stay below 2^31 bytes.  A
+ *    packed scale array of the GEMMs, kp packed rows of ld_sf int16, must keep
+ *    2 (kp + 1) ld_sf below 2^31 bytes (the kernels address one packed row past
+ *    the last on a K tail).  Larger shapes return BSG_ERR_UNSUPPORTED_SHAPE.
  */
 #ifndef BSG_H
 #define BSG_H
