@@ -561,8 +561,22 @@ def summarize(kind, r, steps):
                            "unit": "Gop/s (vector lane operations)",
                            "mfma_frac": r["flops"] / (mean_us * 1e-6) / 1e12 / PEAK[kind]}
     else:
+        # The bound is whichever takes longer at peak: the flops on the matrix cores or
+        # the algorithmic bytes through HBM.  The dense GEMMs are far on the flop side;
+        # the MoE-shaped grouped GEMMs sit just past the ridge on the byte side (most
+        # experts own one or two row tiles, so each weight byte meets few rows), and
+        # report the other fraction beside it.
         ach = r["flops"] / (mean_us * 1e-6) / 1e12
-        out["roofline"] = {"bound": "mfma", "achieved": ach, "peak": PEAK[kind], "unit": "TFLOP/s"}
+        ach_b = r["min_bytes"] / (mean_us * 1e-6) / 1e9
+        t_flops = r["flops"] / (PEAK[kind] * 1e12)
+        t_bytes = r["min_bytes"] / (HBM_PEAK_GBS * 1e9)
+        if t_bytes > t_flops:
+            out["roofline"] = {"bound": "hbm", "achieved": ach_b, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "mfma_frac": ach / PEAK[kind]}
+            ach = ach_b
+        else:
+            out["roofline"] = {"bound": "mfma", "achieved": ach, "peak": PEAK[kind], "unit": "TFLOP/s",
+                               "hbm_frac": ach_b / HBM_PEAK_GBS}
     if kind == "moe_ffn":
         # the call's two kernels: the up-projection (with its SwiGLU epilogue) and the
         # down-projection

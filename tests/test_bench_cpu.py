@@ -95,6 +95,24 @@ def test_headline_is_the_cold_median_and_warm_is_reported_beside():
     # the roofline takes the mean cold launch
     assert out["roofline"]["achieved"] == pytest.approx(1e12 / 1000e-6 / 1e12)
     assert out["roofline"]["frac"] == pytest.approx(out["roofline"]["achieved"] / 2500.0)
+    assert out["roofline"]["bound"] == "mfma"
+    assert out["roofline"]["hbm_frac"] == pytest.approx(4e8 / 1000e-6 / 8e12)
+
+
+def test_roofline_bound_is_the_longer_of_flops_and_bytes_at_peak():
+    # 1 TFLOP at 5 PF takes 200 us; 2 GB at 8 TB/s takes 250 us: bound by HBM
+    r = {"per_launch_us": [1000.0, 1000.0], "wall_s": 2e-3, "flops": 1e12, "min_bytes": 2e9,
+         "meta": {}}
+    out = bench.summarize("grouped", r, 2)
+    assert out["roofline"]["bound"] == "hbm"
+    assert out["roofline"]["unit"] == "GB/s"
+    assert out["roofline"]["achieved"] == pytest.approx(2e9 / 1000e-6 / 1e9)
+    assert out["roofline"]["frac"] == pytest.approx(2e9 / 1000e-6 / 8e12)
+    assert out["roofline"]["mfma_frac"] == pytest.approx(1e12 / 1000e-6 / 5e15)
+    # the rate stays in flops
+    assert out["tflops"] == pytest.approx(1e12 / 1000e-6 / 1e12)
+    r["min_bytes"] = 1e9   # 125 us: bound by the matrix cores
+    assert bench.summarize("grouped", r, 2)["roofline"]["bound"] == "mfma"
 
 
 @pytest.mark.parametrize("kind", ["bf16", "fp8", "fp4", "grouped"])
