@@ -1,5 +1,5 @@
-"""Run-to-run bitwise determinism of the grouped, masked, FFN, quantiser and MQA
-launches (the dense GEMMs are covered in test_gpu_parity.py): the persistent
+"""Run-to-run bitwise determinism of the dense GEMMs at the benchmark shape, and of
+the grouped, masked, FFN, quantiser and MQA launches: the persistent
 grid, the expert search, the SwiGLU epilogue and the MQA key ranges must not make
 an output depend on scheduling.  Each case runs twice into freshly filled outputs
 at the shapes the benchmark times; every written output must agree bit for bit,
@@ -35,20 +35,24 @@ def _twice(run, shape):
     return outs
 
 
-@pytest.mark.parametrize("name", ["moe_fp8", "moe_bf16", "moe_fp4"])
-def test_grouped_workload_deterministic(name):
-    _say(f"determinism: grouped {name} (256 experts, N=2048, K=7168)")
+@pytest.mark.parametrize("name,narrow", [("moe_fp8", False), ("moe_fp8", True), ("moe_bf16", False),
+                                         ("moe_fp4", False), ("moe_fp4", True)])
+def test_grouped_workload_deterministic(name, narrow):
+    """narrow: the A scales with a leading dimension that is not a multiple of 4, so the
+    kernel takes its 2-byte scale loads (more loads per stage in every barrier count)."""
+    _say(f"determinism: grouped {name} (256 experts, N=2048, K=7168)"
+         f"{', 2-byte scale loads' if narrow else ''}")
     w = workloads.make(name, device=DEV)
     t = w.tensors
     M, N, K = w.M, w.N, w.K
     if name == "moe_bf16":
         run = lambda D: bsg.m_grouped_gemm_bf16(t["A"], t["B"], t["offsets"], out=D)
     elif name == "moe_fp8":
-        sfa = bsg.ensure_packed(t["sfa"], M, K // 128)
+        sfa = _packed(t["sfa"], M, K // 128, narrow)
         sfb = torch.stack([bsg.ensure_packed(s, (N + 127) // 128, K // 128) for s in t["sfb"]])
         run = lambda D: bsg.m_grouped_gemm_fp8(t["A"], sfa, t["B"], sfb, t["offsets"], out=D)
     else:
-        sfa = bsg.ensure_packed(t["sfa"], M, K // 32)
+        sfa = _packed(t["sfa"], M, K // 32, narrow)
         sfb = torch.stack([bsg.ensure_packed(s, N, K // 32) for s in t["sfb"]])
         run = lambda D: bsg.m_grouped_gemm_fp4(t["A"], sfa, t["B"], sfb, t["offsets"], K=K, out=D)
     d1, d2 = _twice(run, (M, N))
@@ -138,3 +142,52 @@ def test_quantiser_workload_deterministic(fmt):
         torch.cuda.synchronize()
         outs.append((q.view(torch.uint8).cpu().numpy(), s.cpu().numpy()))
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+def _packed(sf, rows, kb, narrow):
+    """Packed scales of `rows` rows; `narrow` gives them a leading dimension that is
+    not a multiple of 4, which selects the kernels' 2-byte scale loads."""
+    p = bsg.ensure_packed(sf, rows, kb)
+    if not narrow:
+        return p
+    wider = torch.zeros(p.shape[0], rows + 1, dtype=torch.int16, device=DEV)
+    wider[:, :rows] = p[:, :rows]
+    return wider[:, :rows]
+
+
+@pytest.mark.parametrize("kind,narrow", [("bf16", False), ("fp8", False), ("fp8", True),
+                                         ("fp8_rowb", False), ("fp8_rowb", True),
+                                         ("fp4", False), ("fp4", True)])
+def test_dense_benchmark_shape_deterministic(kind, narrow):
+    """The dense GEMMs at 4096x7168x16384, with every scale-load form: the ring
+    barriers wait for exact counts of each wave's loads, so a miscounted load would
+    let a wave read a stage before it lands; on a full grid that shows up as outputs
+    that change from run to run.  The 2-byte and 8-byte scale-load forms must also
+    agree bit for bit."""
+    M, N, K = 4096, 7168, 16384
+    _say(f"determinism: dense {kind} {M}x{N}x{K} ({'2-byte' if narrow else 'wide'} scale loads)")
+    w = workloads.dense(kind, M, N, K, 1017, device=DEV)
+    t = w.tensors
+    if kind == "bf16":
+        run = lambda D: bsg.gemm_bf16(t["A"], t["B"], out=D)
+    elif kind in ("fp8", "fp8_rowb"):
+        sfa = _packed(t["sfa"], M, K // 128, narrow)
+        gb = 128 if kind == "fp8" else 1
+        sfb = bsg.ensure_packed(t["sfb"], (N + gb - 1) // gb, K // 128)
+        run = lambda D: bsg.gemm_fp8_blockscaled(t["A"], sfa, t["B"], sfb, out=D, sfb_gran_mn=gb)
+    else:
+        sfa = _packed(t["sfa"], M, K // 32, narrow)
+        sfb = _packed(t["sfb"], N, K // 32, narrow)
+        run = lambda D: bsg.gemm_fp4_blockscaled(t["A"], sfa, t["B"], sfb, K=K, out=D)
+    d1, d2 = _twice(run, (M, N))
+    assert np.array_equal(d1, d2)
+    assert not np.any(d1 == FILL)
+    if narrow:
+        if kind == "fp4":
+            sfa_w = bsg.ensure_packed(t["sfa"], M, K // 32)
+            sfb_w = bsg.ensure_packed(t["sfb"], N, K // 32)
+            wide = lambda D: bsg.gemm_fp4_blockscaled(t["A"], sfa_w, t["B"], sfb_w, K=K, out=D)
+        else:
+            sfa_w = bsg.ensure_packed(t["sfa"], M, K // 128)
+            wide = lambda D: bsg.gemm_fp8_blockscaled(t["A"], sfa_w, t["B"], sfb, out=D, sfb_gran_mn=gb)
+        assert np.array_equal(d1, _twice(wide, (M, N))[0])
