@@ -122,14 +122,11 @@ static int launch(GemmArgs a, hipStream_t stream) {
     grid = (int)(g < cus ? g : cus);
   }
   // Leading dead stages of the first round: nk padded up to whole rounds of U
-  // stages, the padding rounded down to an even count (paired stages).  FP8 keeps
-  // padding under 2% of the stage loop at the end, where it multiplies zeros: its
-  // peeled first round makes the dense kernel spill (47 registers at K = 16384).
-  // BF16 and FP4 peel it at any size (no spills; at K = 16384, 8 of 520 and 2 of
-  // 130 stages: 0.7% and 0.4% faster in an alternating A/B).
+  // stages, the padding rounded down to an even count (paired stages), at any size
+  // (at K = 16384 BF16 8 of 520 and FP4 2 of 130 stages: 0.7% and 0.4% faster than
+  // the same padding at the end, in an alternating A/B; FP8's 4 of 260 within noise).
   constexpr int U = T::U;
-  int koff = a.nk % U ? (U - a.nk % U) & ~1 : 0;
-  if (KIND == KIND_FP8 && koff * 50 <= a.nk + koff) koff = 0;
+  const int koff = a.nk % U ? (U - a.nk % U) & ~1 : 0;
   (void)hipGetLastError();
   int st = BSG_OK;
   auto go = [&](auto kc) {

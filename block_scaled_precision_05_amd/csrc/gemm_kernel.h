@@ -515,8 +515,8 @@ void gemm_kernel(const GemmArgs args) {
   // first round: KOFF stages that hold no data, an even count so that paired stages
   // stay the two halves of one 128-byte line; their copies read nothing and the first
   // round, peeled off the loop, leaves out their MFMAs.  The launcher picks KOFF =
-  // U - nk % U rounded down to even (one stage stays at the end when nk is odd), or 0
-  // when the padding is under 2% of the loop.  Ring position p holds K stage p - KOFF.
+  // U - nk % U rounded down to even (one stage stays at the end when nk is odd).  Ring
+  // position p holds K stage p - KOFF.
   static_assert(KOFF >= 0 && KOFF < T::U && KOFF % 2 == 0, "leading dead stages: even, under a round");
   constexpr int koff = KOFF;
   const int nk_pad = (nk + koff + T::U - 1) / T::U * T::U;

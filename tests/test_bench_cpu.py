@@ -64,11 +64,9 @@ def _stages(kind, K):
 
 def _leading_dead(nk, ns, kind):
     """The launcher's rule: pad nk to whole rounds of U stages (U = 2*NS for an odd
-    ring, else NS); the padding goes first, rounded down to even, except for FP8
-    when it is under 2% of the loop."""
+    ring, else NS); the padding goes first, rounded down to even."""
     u = 2 * ns if ns % 2 else ns
-    koff = (u - nk % u) & ~1 if nk % u else 0
-    return 0 if kind == "fp8" and koff * 50 <= nk + koff else koff
+    return (u - nk % u) & ~1 if nk % u else 0
 
 
 @pytest.mark.parametrize("case,kind,K", [
