@@ -103,14 +103,14 @@ PAGES_BF16_TFLOPS = 431.0
 
 KERNEL_NAME = {
     "bf16": "gemm_kernel<0, 256, 256, 2, 4, 64, 5, 1, false, 0, 8, 0>",
-    "fp8": "gemm_kernel<1, 256, 256, 2, 4, 64, 5, 1, false, 1, 4, 0>",
+    "fp8": "gemm_kernel<1, 256, 256, 2, 4, 64, 5, 1, false, 1, 0, 0>",
     "fp4": "gemm_kernel<2, 256, 256, 2, 4, 64, 5, 1, false, 1, 2, 0>",
     "grouped": "gemm_kernel<1, 256, 256, 2, 4, 64, 5, 1, true, 1, 8, 0>",
     "quant_fp8": "quant_kernel<0, 0, 32, 2, 0>",
     "quant_fp4": "quant_kernel<1, 0, 32, 2, 0>",
     "quant_fp8_moe": "quant_kernel<0, 0, 32, 2, 0>",
     "moe_ffn": "gemm_kernel<1, 256, 256, 2, 4, 64, 5, 1, true, 1, 8, 1> (up, SwiGLU epilogue) + gemm_kernel<1, 256, 256, 2, 4, 64, 5, 1, true, 1, 8, 0> (down)",
-    "masked": "gemm_kernel<1, 128, 256, 1, 4, 64, 6, 1, true, 1, 2, 0>",
+    "masked": "gemm_kernel<1, 128, 256, 1, 4, 64, 6, 1, true, 1, 0, 0>",
     "grouped_bf16": "gemm_kernel<0, 256, 256, 2, 4, 64, 5, 1, true, 0, 6, 0>",
     "grouped_fp4": "gemm_kernel<2, 256, 256, 2, 4, 64, 5, 1, true, 1, 4, 0>",
     "mqa_prefill_fp8": "mqa_logits_kernel<0, 2, true>",

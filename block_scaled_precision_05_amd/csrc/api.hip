@@ -122,11 +122,15 @@ static int launch(GemmArgs a, hipStream_t stream) {
     grid = (int)(g < cus ? g : cus);
   }
   // Leading dead stages of the first round: nk padded up to whole rounds of U
-  // stages, the padding rounded down to an even count (paired stages), at any size
-  // (at K = 16384 BF16 8 of 520 and FP4 2 of 130 stages: 0.7% and 0.4% faster than
-  // the same padding at the end, in an alternating A/B; FP8's 4 of 260 within noise).
+  // stages, the padding rounded down to an even count (paired stages).  BF16 and FP4
+  // peel it at any size (at K = 16384, 8 of 520 and 2 of 130 stages: 0.7% and 0.4%
+  // faster than the same padding at the end, in an alternating A/B).  FP8 keeps a
+  // padding under 2% of the loop at the end, where it multiplies zeros: its 8-register
+  // fragments leave the peeled round no registers to spare (the dense kernel spills
+  // there, 2% slower at K = 16384).
   constexpr int U = T::U;
-  const int koff = a.nk % U ? (U - a.nk % U) & ~1 : 0;
+  int koff = a.nk % U ? (U - a.nk % U) & ~1 : 0;
+  if (KIND == KIND_FP8 && koff * 50 <= a.nk + koff) koff = 0;
   (void)hipGetLastError();
   int st = BSG_OK;
   auto go = [&](auto kc) {

@@ -272,8 +272,9 @@ struct GemmTile {
   // took 3 to 6% off the FP4 and grouped FP8 GEMMs).  A chunk's loads stay in
   // its k-step (a scheduling barrier closes each), and inside the chunk holding
   // stage st's last copy the compiler may only move scale loads after it, which
-  // makes the wait stricter, never looser.
-  static constexpr int copies_after(int s, int st, bool sc = true) {
+  // makes the wait stricter, never looser.  kd: pairs at ring positions below kd
+  // (the first round's dead stages) issue nothing.
+  static constexpr int copies_after(int s, int st, bool sc = true, int kd = 0) {
     const int nsc = sc ? NSC : 0;
     int issued = 0, last = -1;
     if (!PR) {
@@ -290,7 +291,7 @@ struct GemmTile {
     }
     auto chunk = [&](int g) {
       const int c = chunk_at(g), t = pair_start(g) + NS - 1;
-      if (t < 0) return;
+      if (t < 0 || t < kd) return;
       if (c == 0 || (c == 1 && !SHARED_SCALES)) issued += nsc;
       for (int q = c * QPC; q < (c + 1) * QPC; ++q) {
         if (t == st) last = issued;
@@ -314,6 +315,16 @@ struct GemmTile {
               c = copies_after(si + 2 * U, si + 2 * U + 1, sc);
     const int m = a < b ? a : b;
     return m < c ? m : c;
+  }
+  // With kd leading dead positions (KOFF > 0, paired copies) the first round is
+  // peeled and its dead pairs issue nothing: the peeled round waits with its own
+  // counts (none before a dead stage), the loop's rounds with theirs.
+  static constexpr int wait_first(int si, bool sc, int kd) {
+    return si + 1 < kd ? 63 : copies_after(si, si + 1, sc, kd);
+  }
+  static constexpr int wait_steady(int si, bool sc, int kd) {
+    const int b = copies_after(si + U, si + U + 1, sc, kd), c = copies_after(si + 2 * U, si + 2 * U + 1, sc, kd);
+    return b < c ? b : c;
   }
   static constexpr bool steady(int si) {
     return copies_after(si + U, si + U + 1, true) == copies_after(si + 2 * U, si + 2 * U + 1, true) &&
@@ -513,10 +524,12 @@ void gemm_kernel(const GemmArgs args) {
   // are compile-time), so nk is padded up to whole rounds.  The padding either sits
   // at the end, where those stages multiply zeros, or (KOFF > 0) at the start of the
   // first round: KOFF stages that hold no data, an even count so that paired stages
-  // stay the two halves of one 128-byte line; their copies read nothing and the first
-  // round, peeled off the loop, leaves out their MFMAs.  The launcher picks KOFF =
-  // U - nk % U rounded down to even (one stage stays at the end when nk is odd).  Ring
-  // position p holds K stage p - KOFF.
+  // stay the two halves of one 128-byte line.  The first round, peeled off the loop,
+  // issues no copies or scale loads for them (each load instruction, even one that
+  // reads nothing, holds the CU's address unit for 16 cycles) and leaves out their
+  // MFMAs; its barriers wait with counts of their own.  The launcher picks KOFF =
+  // U - nk % U rounded down to even (one stage stays at the end when nk is odd; FP8
+  // keeps a padding under 2% at the end).  Ring position p holds K stage p - KOFF.
   static_assert(KOFF >= 0 && KOFF < T::U && KOFF % 2 == 0, "leading dead stages: even, under a round");
   constexpr int koff = KOFF;
   const int nk_pad = (nk + koff + T::U - 1) / T::U * T::U;
@@ -918,7 +931,7 @@ void gemm_kernel(const GemmArgs args) {
       if constexpr (PR) {
         // every chunk due before k-step 0 (pairs with a first stage t >= 0)
         [&]<int... gs>(std::integer_sequence<int, gs...>) {
-          ((T::pair_start(gs - (NS + 2) * J) + NS - 1 >= 0
+          ((T::pair_start(gs - (NS + 2) * J) + NS - 1 >= koff
                 ? pair_chunk(std::integral_constant<int, gs - (NS + 2) * J>{}, 0)
                 : void()),
            ...);
@@ -930,24 +943,33 @@ void gemm_kernel(const GemmArgs args) {
            ...);
         }(std::make_integer_sequence<int, NS>{});
       }
-      wait_vm_lds<T::wait_prologue(MM)>();
+      wait_vm_lds<(PR && koff > 0) ? 63 : T::wait_prologue(MM)>();
       ring_barrier();
       decode_scales(-koff, std::integral_constant<int, 0>{}, sa_cur, sb_cur);
       read_frags(0, 0, fa[0], fb[0]);
 
       // One stage at ring position s.  Every stage of the steady loop runs the same
       // code, free of branches around the MFMAs.  A DEAD stage (the first round's
-      // leading positions, which hold no data) keeps the barrier, the copies (all out
-      // of range, so no memory traffic), the scale loads and the fragment reads, so
-      // the copy schedule and its vmcnt arithmetic are those of every other round,
-      // and only leaves out the MFMAs, which would multiply zeros.
-      auto stage = [&](auto ic, auto deadc, int s) {
+      // leading positions, which hold no data) keeps the barrier and the fragment
+      // reads (of buffers no copy fills) and leaves out the MFMAs; the pairs of dead
+      // positions issue neither copies nor scale loads, and the first round's
+      // barriers wait for the live loads it did issue (wait_first).
+      auto stage = [&](auto ic, auto deadc, auto firstc, int s) {
         constexpr int si = decltype(ic)::value;   // position of the stage in the round
         constexpr bool DEAD = decltype(deadc)::value;
+        constexpr bool FIRST = decltype(firstc)::value;   // the peeled first round
+        constexpr int WAIT_SI = !PR || koff == 0 ? T::wait_at(si, MM)
+                                : (FIRST ? T::wait_first(si, MM, koff) : T::wait_steady(si, MM, koff));
         constexpr int buf = si % NS;
         constexpr int nbuf = (buf + 1) % NS;
         static_assert(!PR || T::steady(si), "the copy schedule must repeat every round");
         const int round = s - si;
+        // dead pairs of the first round issue nothing (their copies would read
+        // nothing and their scale words are never used)
+        auto chunk_at_g = [&](auto gc) __attribute__((always_inline)) {
+          constexpr int gg = decltype(gc)::value;
+          if constexpr (!(FIRST && T::pair_start(gg) + NS - 1 < koff)) pair_chunk(gc, round);
+        };
         auto body = [&](auto jc) {
           constexpr int j = decltype(jc)::value;
           constexpr int g = si * J + j;             // k-step index within the round
@@ -959,10 +981,10 @@ void gemm_kernel(const GemmArgs args) {
           if constexpr (j + 1 < J) {
             if constexpr (T::DBA) {
               read_frags(buf, j + 1, fa[na], fb[nx]);
-              if constexpr (PR) pair_chunk(std::integral_constant<int, g>{}, round);
+              if constexpr (PR) chunk_at_g(std::integral_constant<int, g>{});
               if constexpr (!DEAD) mfmas(jc, fa[ca], fb[cu], sa_cur, sb_cur);
             } else {
-              if constexpr (PR) pair_chunk(std::integral_constant<int, g>{}, round);
+              if constexpr (PR) chunk_at_g(std::integral_constant<int, g>{});
               if constexpr (!DEAD) mfmas(jc, fa[ca], fb[cu], sa_cur, sb_cur);
               read_frags(buf, j + 1, fa[na], fb[nx]);
             }
@@ -977,12 +999,12 @@ void gemm_kernel(const GemmArgs args) {
             // across the barrier, and the compiler waits for each one just before
             // the first MFMA that uses its registers.
             if constexpr (PR && T::chunk_at(g) != 0)
-              wait_vm<T::wait_at(si, MM)>();
+              wait_vm<WAIT_SI>();
             else
-              wait_vm_lds<T::wait_at(si, MM)>();
+              wait_vm_lds<WAIT_SI>();
             ring_barrier();
             if constexpr (PR) {
-              pair_chunk(std::integral_constant<int, g>{}, round);
+              chunk_at_g(std::integral_constant<int, g>{});
             } else {
               const int kt = s + NS - koff;
               load_scales(kt >= 0 && kt < nk ? kt : 0, std::integral_constant<int, buf>{});
@@ -1014,14 +1036,15 @@ void gemm_kernel(const GemmArgs args) {
           int s0 = 0;
           asm volatile("" : "+s"(s0));
           [&]<int... is>(std::integer_sequence<int, is...>) {
-            (stage(std::integral_constant<int, is>{}, std::integral_constant<bool, (is < koff)>{}, s0 + is),
+            (stage(std::integral_constant<int, is>{}, std::integral_constant<bool, (is < koff)>{},
+                   std::true_type{}, s0 + is),
              ...);
           }(std::make_integer_sequence<int, T::U>{});
         }
       }
       for (int s = koff > 0 ? T::U : 0; s < nk_pad; s += T::U) {
         [&]<int... is>(std::integer_sequence<int, is...>) {
-          (stage(std::integral_constant<int, is>{}, std::false_type{}, s + is), ...);
+          (stage(std::integral_constant<int, is>{}, std::false_type{}, std::false_type{}, s + is), ...);
         }(std::make_integer_sequence<int, T::U>{});
       }
 
