@@ -144,8 +144,9 @@ def kernels(dis):
 
 
 def stage_loops(ins, per_round):
-    """Bodies of the backward branches that hold a whole round of barriers: the
-    steady stage loops."""
+    """Bodies of the branch-free backward loops that hold a whole round of barriers:
+    the steady stage loops (every stage of the steady loop runs the same straight-line
+    code)."""
     loops = []
     for addr, text, note in ins:
         if not text.startswith("s_cbranch_"):
@@ -158,6 +159,8 @@ def stage_loops(ins, per_round):
         if target >= addr:
             continue
         body = [t for a, t, _ in ins if target <= a <= addr]
+        if any(t.startswith(("s_cbranch", "s_branch", "s_setpc")) for t in body[:-1]):
+            continue
         if sum(1 for t in body if t.startswith("s_barrier")) == per_round:
             loops.append(body)
     return loops
