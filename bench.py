@@ -57,6 +57,13 @@ rows are also compared with the GPU output of the timed calls (`parity`).
 `--operands zeros` runs the dense cases on all-zero codes instead of the random
 draws: the same instruction stream at a lower power draw, an experiment on the
 clock, never the benchmark.
+
+`mfma_only` (and each dense case's `per_dtype[...]["mfma_only"]`) is the rate the
+matrix cores sustain when every SIMD runs nothing but MFMAs on random operands, in
+the GEMM kernels' register tile and occupancy (libbsg_probe.so, include/bsg_probe.h):
+under sustained load the chip runs at the clock its power limit allows for the
+data, below the clock the published peaks assume, and `gemm_warm_frac` is the
+GEMM's warm rate against that ceiling.
 """
 from __future__ import annotations
 
@@ -496,6 +503,54 @@ def time_case(kind, steps, warmup, dev, cpu_budget=0.0, settle_s=0.2):
     return res
 
 
+# rounds of MFMAs per probe call: about half a millisecond each at the rates measured
+PROBE_ITERS = {"bf16": 800, "fp8": 400, "fp4": 800}
+PROBE_SEED = 20240607
+
+
+def mfma_only(kind, dev, calls=20, settle_s=0.2):
+    """The rate the matrix cores sustain on MFMAs alone (libbsg_probe.so): the GEMM
+    kernels' register tile and occupancy (one workgroup of eight waves per CU), random
+    operand codes and UE8M0 scales, no memory traffic.  Calls back to back after a
+    settle phase like the GEMMs' warm loop, each bracketed by HIP events on the launch
+    stream; the median.  Under sustained load the chip holds the clock its power limit
+    allows for the data, so this is the ceiling the GEMMs' warm rates compare with,
+    beside the published peak."""
+    import torch
+    from block_scaled_precision_05_amd import probe
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    iters = PROBE_ITERS[kind]
+    out = torch.empty(cus * probe.THREADS, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        probe.mfma(kind, PROBE_SEED, cus, iters, out, stream)
+
+    call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < settle_s:
+        for _ in range(4):
+            call()
+        torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(calls)]
+    for s, e in ev:
+        s.record(stream)
+        call()
+        e.record(stream)
+    torch.cuda.synchronize()
+    if not bool(torch.isfinite(out).all()):
+        raise RuntimeError("mfma probe: non-finite accumulator sums")
+    us = statistics.median(s.elapsed_time(e) * 1e3 for s, e in ev)
+    tflops = probe.flops_per_call(kind, cus, iters) / (us * 1e-6) / 1e12
+    return {"tflops": tflops, "frac_of_peak": tflops / PEAK[kind], "us_median": us,
+            "calls": calls, "workgroups": cus, "rounds": iters,
+            "kernel": f"mfma_probe_kernel<{probe.KINDS[kind]}>",
+            "what": "MFMAs alone in the GEMM's register tile and occupancy, random codes and "
+                    "scales, back to back"}
+
+
 def summarize(kind, r, steps):
     """Per-case record.  The headline figures are the cold-L2 samples (the timed
     region); `warm` holds the back-to-back rate of the same calls."""
@@ -711,6 +766,14 @@ def main():
                 f"{q['warm']['tflops']:.1f} warm, {q['cold_l2']['us_mean']:.1f} us mean launch")
         torch.cuda.empty_cache()
 
+    # the matrix cores' sustained rate on MFMAs alone, for the dense cases' warm rates
+    for kind in [k for k in ("bf16", "fp8", "fp4") if k in kinds]:
+        m = mfma_only(kind, dev)
+        m["gemm_warm_frac"] = per[kind]["warm"]["tflops"] / m["tflops"]
+        per[kind]["mfma_only"] = m
+        log(f"{kind}: MFMAs alone {m['tflops']:.1f} TFLOPS ({100 * m['frac_of_peak']:.1f}% of "
+            f"peak); the GEMM's warm rate is {100 * m['gemm_warm_frac']:.1f}% of it")
+
     b = per["bf16"]
     roof = dict(b["roofline"])
     roof["traffic"] = load_traffic("bf16", sha)
@@ -749,6 +812,7 @@ def main():
         "warm": b["warm"],
         "cold_clean": b.get("cold_clean"),
         "roofline": roof,
+        "mfma_only": b["mfma_only"],
         "cpu_baseline": cpu,
         "context": {"pages_bf16_tflops": PAGES_BF16_TFLOPS,
                     "note": "the pages' figure at this shape on another accelerator (Ascend "
