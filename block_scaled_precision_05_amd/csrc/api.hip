@@ -99,7 +99,7 @@ static int num_cus() {
 template <int KIND, int BM, int BN, int WM, int WN, int SB, int NS, int PR, bool GROUPED, int SV = 0,
           int EPI = 0>
 static int launch(GemmArgs a, hipStream_t stream) {
-  using T = GemmTile<KIND, BM, BN, WM, WN, SB, NS, PR, SV>;
+  using T = GemmTile<KIND, BM, BN, WM, WN, SB, NS, PR, SV, GROUPED>;
   a.d_vec = (((uintptr_t)a.D & 15) == 0 && (a.ldd % 8) == 0) ? 2
             : (((uintptr_t)a.D & 7) == 0 && (a.ldd % 4) == 0) ? 1 : 0;
   a.tiles_m = (a.M + BM - 1) / BM;

@@ -150,7 +150,7 @@ __device__ __forceinline__ f32x16_t mfma_scaled2(i32x8_t b, i32x8_t a, f32x16_t 
 //             its copies are spread over the next 2J k-steps (one chunk per
 //             k-step): a copy instruction waits in the address unit, and in-order
 //             issue makes the MFMAs behind it wait too, so copies must trickle.
-template <int KIND, int BM, int BN, int WM, int WN, int SB, int NS, int PR, int SV = 0>
+template <int KIND, int BM, int BN, int WM, int WN, int SB, int NS, int PR, int SV = 0, bool GR = false>
 struct GemmTile {
   static constexpr int NW = WM * WN;
   static constexpr int NT = NW * 64;
@@ -168,13 +168,22 @@ struct GemmTile {
   static constexpr int ROWS_PER_COPY = 1024 / SB;          // rows of one 1 KiB wave copy
   static constexpr int A_COPIES = BM / ROWS_PER_COPY;      // 1 KiB copies per stage
   static constexpr int B_COPIES = BN / ROWS_PER_COPY;
-  static constexpr int A_LOADS = (A_COPIES + NW - 1) / NW; // copies per wave per stage
-  static constexpr int B_LOADS = (B_COPIES + NW - 1) / NW;
+  // Waves that issue the copies.  A copy instruction holds its wave's in-order issue
+  // while the CU's address unit takes it; with eight waves the upper row (waves 0 ..
+  // NW/2-1, one on each SIMD: waves w and w + NW/2 share one) issues every copy and
+  // the lower row none, so on each SIMD one wave's MFMAs are never held behind a copy
+  // (alternating A/B at the benchmark shapes: BF16 -3.2%, FP4 -1.2%, grouped FP8 MoE
+  // -1.9%, grouped FP4 -2.2%; dense FP8, whose k-step is one stage long, +0.4%, so
+  // there every wave keeps its share).  GR: the grouped kernels.
+  static constexpr int NWC = NW > 4 && (KIND != KIND_FP8 || GR) ? NW / 2 : NW;
+  static_assert(NWC == NW || NWC == WN, "the copying waves are the upper row of waves");
+  static constexpr int A_LOADS = (A_COPIES + NWC - 1) / NWC; // copies per copying wave per stage
+  static constexpr int B_LOADS = (B_COPIES + NWC - 1) / NWC;
   static constexpr int N_DMA = A_LOADS + B_LOADS;
-  // When the copies do not split evenly over the waves, the short waves issue an
+  // When the copies do not split evenly over the copying waves, the short waves issue an
   // out-of-range copy into a spare 1 KiB of LDS instead, so every wave issues the
   // same number of copies and the vmcnt arithmetic holds for all of them.
-  static constexpr bool DUMMY = A_LOADS * NW != A_COPIES || B_LOADS * NW != B_COPIES;
+  static constexpr bool DUMMY = A_LOADS * NWC != A_COPIES || B_LOADS * NWC != B_COPIES;
   static constexpr int LDS_BYTES = NS * STAGE_BYTES + (DUMMY ? 1024 : 0);
   // Epilogue staging: each wave's TM x TN bf16 block, row-major (EPI_ROW bytes a
   // row) in the ring's LDS; 16-byte chunk c of row r sits at chunk c ^ epi_swz(r),
@@ -506,11 +515,11 @@ template <int KIND, int BM, int BN, int WM, int WN, int SB, int NS, int PR, bool
 __global__ __launch_bounds__(WM* WN * 64)
 __attribute__((amdgpu_waves_per_eu((WM * WN + 3) / 4, (WM * WN + 3) / 4)))
 void gemm_kernel(const GemmArgs args) {
-  using T = GemmTile<KIND, BM, BN, WM, WN, SB, NS, PR, SV>;
+  using T = GemmTile<KIND, BM, BN, WM, WN, SB, NS, PR, SV, GROUPED>;
   constexpr int FM = T::FM, FN = T::FN, J = T::J, RPF = T::RPF, NC = T::NC, SW = T::SW;
   // EPI: 0 = bf16 D; 1 + rule = SwiGLU and FP8 1x128 requantisation (rule CEIL / OCP_MX)
   static_assert(EPI == 0 || (KIND == KIND_FP8 && GROUPED && !T::PERM_B && T::ONE_B_SCALE &&
-                             T::NW * T::ROWS_PER_COPY == BN / 2 && BN / 2 == 128 && T::TN <= 64),
+                             (BN / 2) % (T::NWC * T::ROWS_PER_COPY) == 0 && BN / 2 == 128 && T::TN <= 64),
                 "the SwiGLU epilogue: FP8 grouped tiles whose B copies and scale blocks stay in one half");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
 
@@ -563,10 +572,10 @@ void gemm_kernel(const GemmArgs args) {
 
   // Copy lanes: lane t of a wave copy covering rows r0 .. r0 + 1024/SB - 1 writes
   // LDS bytes r0*SB + 16t, i.e. row r0 + t/NC, physical chunk t%NC, which holds
-  // logical chunk (t%NC) ^ swizzle(row).  Copy q of wave w starts at row
-  // r0 = (q*NW + w) * 1024/SB, and r0 / RPS = 4*(q*NW + w), so the swizzle of a
+  // logical chunk (t%NC) ^ swizzle(row).  Copy q of copying wave w starts at row
+  // r0 = (q*NWC + w) * 1024/SB, and r0 / RPS = 4*(q*NWC + w), so the swizzle of a
   // copy row is (4w + (t/NC)/RPS) % NC whatever q is.
-  static_assert((4 * T::NW) % NC == 0, "copy swizzle must not depend on the copy index");
+  static_assert((4 * T::NWC) % NC == 0, "copy swizzle must not depend on the copy index");
   const int cp_row = lane / NC;
   const int cp_c16 = 16 * ((lane % NC) ^ ((4 * wave + cp_row / T::RPS) % NC));
 
@@ -604,12 +613,13 @@ void gemm_kernel(const GemmArgs args) {
 
     // Waves whose rows all lie past the edge (the lower row of waves on an
     // expert's last row tile when it holds at most BM/2 rows) run the tile without
-    // MFMAs, fragment reads or stores: they still issue their share of the copies
-    // and scale loads and meet every barrier, so the workgroup's schedule and the
-    // vmcnt arithmetic are unchanged, and the SIMD they share with a computing
-    // wave is left to it.
-    auto tile_body = [&](auto mm_c) __attribute__((always_inline)) {
+    // MFMAs, fragment reads, scale loads or stores, and meet every barrier; the SIMD
+    // they share with a computing wave is left to it.  When every wave copies (NWC ==
+    // NW) they still issue their share of the copies, and their barriers wait with
+    // counts for a wave without scale loads.
+    auto tile_body = [&](auto mm_c, auto iss_c) __attribute__((always_inline)) {
       constexpr bool MM = decltype(mm_c)::value;
+      constexpr bool ISS = decltype(iss_c)::value;   // the wave issues copies
       const int n_end = n0 + BN < args.N ? n0 + BN : args.N;
       const int rows_a = m_end - m0, rows_b = n_end - n0;
 
@@ -620,7 +630,7 @@ void gemm_kernel(const GemmArgs args) {
       const __amdgpu_buffer_rsrc_t rb = make_rsrc(
           Bbase + (int64_t)n0 * args.ldb,
           (uint32_t)(((EPI ? args.inter + BN / 2 : rows_b) - 1) * args.ldb + args.k_bytes));
-      // Copy q of a wave fills LDS rows (slots) (q*NW + wave) * ROWS_PER_COPY + cp_row
+      // Copy q of a copying wave fills LDS rows (slots) (q*NWC + wave) * ROWS_PER_COPY + cp_row
       // from tile row perm(slot); the lane part and the q part of the slot occupy
       // disjoint bits, so perm splits into a per-lane row and a per-q row.
       uint32_t a_vbase = (uint32_t)(T::perm_a(T::ROWS_PER_COPY * wave + cp_row) * args.lda) + cp_c16;
@@ -640,9 +650,9 @@ void gemm_kernel(const GemmArgs args) {
         const uint32_t oob = (uint32_t)kt < (uint32_t)nk && kb + cp_c16 < args.k_bytes ? 0u : kOOB;
         uint8_t* const spare = smem + NS * T::STAGE_BYTES;
         if (q < T::A_LOADS) {
-          const int ci = q * T::NW + wave;
+          const int ci = q * T::NWC + wave;
           const bool dummy = T::DUMMY && ci >= T::A_COPIES;
-          const uint32_t qrow = (uint32_t)T::perm_a(q * T::NW * T::ROWS_PER_COPY);
+          const uint32_t qrow = (uint32_t)T::perm_a(q * T::NWC * T::ROWS_PER_COPY);
           // The row and K parts stay below 2^31 (256 rows of at most 2^31/256
           // bytes), so OR-ing or adding the out-of-range bit give the same offset;
           // the dense kernels run 1.7% faster (FP8) with the sum, the grouped ones
@@ -654,9 +664,9 @@ void gemm_kernel(const GemmArgs args) {
               16, off, 0, 0, 0);
         } else {
           const int qb = q - T::A_LOADS;
-          const int ci = qb * T::NW + wave;
+          const int ci = qb * T::NWC + wave;
           const bool dummy = T::DUMMY && ci >= T::B_COPIES;
-          const uint32_t qrow0 = (uint32_t)T::perm_b(qb * T::NW * T::ROWS_PER_COPY);
+          const uint32_t qrow0 = (uint32_t)T::perm_b(qb * T::NWC * T::ROWS_PER_COPY);
           // (SwiGLU epilogue: tile rows past BN/2 are up rows, inter rows further on)
           const uint32_t qrow = EPI && qrow0 >= (uint32_t)(BN / 2) ? qrow0 - BN / 2 + (uint32_t)args.inter : qrow0;
           const uint32_t off = GROUPED ? (b_vbase + qrow * (uint32_t)args.ldb + kb) | oob | (dummy ? kOOB : 0u)
@@ -667,16 +677,20 @@ void gemm_kernel(const GemmArgs args) {
         }
       };
       auto issue_stage = [&](int kt, int buf) {
+        if constexpr (ISS) {
 #pragma unroll
-        for (int q = 0; q < T::N_DMA; ++q) copy_one(kt, buf, q);
+          for (int q = 0; q < T::N_DMA; ++q) copy_one(kt, buf, q);
+        }
       };
       // Chunk c of pair (kt, kt+1): copies c*QPC .. (c+1)*QPC-1 of both stages, the
       // two halves of every line back to back.
       auto issue_chunk = [&](int kt, int buf0, int buf1, int c) {
+        if constexpr (ISS) {
 #pragma unroll
-        for (int q = 0; q < T::QPC; ++q) {
-          copy_one(kt, buf0, c * T::QPC + q);
-          copy_one(kt + 1, buf1, c * T::QPC + q);
+          for (int q = 0; q < T::QPC; ++q) {
+            copy_one(kt, buf0, c * T::QPC + q);
+            copy_one(kt + 1, buf1, c * T::QPC + q);
+          }
         }
       };
 
@@ -943,7 +957,7 @@ void gemm_kernel(const GemmArgs args) {
            ...);
         }(std::make_integer_sequence<int, NS>{});
       }
-      wait_vm_lds<(PR && koff > 0) ? 63 : T::wait_prologue(MM)>();
+      wait_vm_lds<(!ISS || (PR && koff > 0)) ? 63 : T::wait_prologue(MM)>();
       ring_barrier();
       decode_scales(-koff, std::integral_constant<int, 0>{}, sa_cur, sb_cur);
       read_frags(0, 0, fa[0], fb[0]);
@@ -958,8 +972,12 @@ void gemm_kernel(const GemmArgs args) {
         constexpr int si = decltype(ic)::value;   // position of the stage in the round
         constexpr bool DEAD = decltype(deadc)::value;
         constexpr bool FIRST = decltype(firstc)::value;   // the peeled first round
-        constexpr int WAIT_SI = !PR || koff == 0 ? T::wait_at(si, MM)
-                                : (FIRST ? T::wait_first(si, MM, koff) : T::wait_steady(si, MM, koff));
+        // (a wave that issues no copies has none to wait for: the copying waves'
+        // waits and the barrier cover the stage, and the compiler waits for its scale
+        // words where it decodes them)
+        constexpr int WAIT_SI = !ISS ? 63
+                                : (!PR || koff == 0 ? T::wait_at(si, MM)
+                                   : (FIRST ? T::wait_first(si, MM, koff) : T::wait_steady(si, MM, koff)));
         constexpr int buf = si % NS;
         constexpr int nbuf = (buf + 1) % NS;
         static_assert(!PR || T::steady(si), "the copy schedule must repeat every round");
@@ -973,7 +991,8 @@ void gemm_kernel(const GemmArgs args) {
         auto body = [&](auto jc) {
           constexpr int j = decltype(jc)::value;
           constexpr int g = si * J + j;             // k-step index within the round
-          constexpr int nvm = PR ? T::chunk_vmem(g) : (j + 1 < J ? 0 : T::VMEM_PER_STAGE);
+          constexpr int nvm = PR ? T::chunk_vmem(g) - (ISS ? 0 : 2 * T::QPC)
+                                 : (j + 1 < J ? 0 : (ISS ? T::VMEM_PER_STAGE : T::NSC));
           // fragment register set of this k-step: k-steps alternate sets across
           // stage boundaries too (a round has an even number of them)
           constexpr int cu = (si * J + j) & 1, nx = cu ^ 1;
@@ -1202,13 +1221,27 @@ void gemm_kernel(const GemmArgs args) {
         d += dstep;
       }
     };
-    if constexpr (GROUPED && WM > 1 && T::NW > 4) {
+    // The copying waves (ISS) run one variant of the tile body, the others another;
+    // on an expert's last row tile the lower row of waves may hold no rows (MM false).
+    // The copying waves are the upper row, which always holds rows of the tile.
+    if constexpr (T::NWC == T::NW) {
+      if constexpr (GROUPED && WM > 1 && T::NW > 4) {
+        if (m0 + wm * T::TM < m_end)
+          tile_body(std::true_type{}, std::true_type{});
+        else
+          tile_body(std::false_type{}, std::true_type{});
+      } else {
+        tile_body(std::true_type{}, std::true_type{});
+      }
+    } else if (wave < T::NWC) {
+      tile_body(std::true_type{}, std::true_type{});
+    } else if constexpr (GROUPED && WM > 1) {
       if (m0 + wm * T::TM < m_end)
-        tile_body(std::true_type{});
+        tile_body(std::true_type{}, std::false_type{});
       else
-        tile_body(std::false_type{});
+        tile_body(std::false_type{}, std::false_type{});
     } else {
-      tile_body(std::true_type{});
+      tile_body(std::true_type{}, std::false_type{});
     }
   }
 }

@@ -5,7 +5,8 @@ a load the compiler dropped or merged would let a wave pass a barrier before its
 landed.  This test disassembles the gfx950 code of the built libbsg.so (the LLVM tools
 under /opt/rocm, no GPU needed) and checks, for every GEMM instantiation, that each
 steady stage loop issues per barrier interval the copies and scale loads of an
-independent Python model of the schedule, and waits for the count that model gives."""
+independent Python model of the schedule, and, in the waves that issue the copies,
+waits for the count that model gives."""
 import os
 import re
 import subprocess
@@ -50,19 +51,29 @@ def disassemble(lib):
         return "\n".join(text)
 
 
+def copying_waves(kind, wm, wn, grouped):
+    """Waves that issue the copies: with eight waves the upper row only, except in the
+    dense FP8 kernel, where every wave does."""
+    nw = wm * wn
+    return nw // 2 if nw > 4 and (kind != FP8 or grouped) else nw
+
+
 class Schedule:
     """Python model of the kernel template's paired copy schedule (gemm_kernel.h):
     per k-step the chunk of copies (and, at a pair's first chunks, the scale loads)
-    each wave issues, and the vmcnt each barrier waits for."""
+    a wave issues, and the vmcnt each barrier of a copying wave waits for.  copies:
+    the wave is one of the copying waves; scales: it loads scale words (it runs
+    MFMAs)."""
 
-    def __init__(self, kind, bm, bn, wm, wn, sb, ns, sv, scales=True):
-        nw = wm * wn
+    def __init__(self, kind, bm, bn, wm, wn, sb, ns, sv, scales=True, grouped=False, copies=True):
+        nwc = copying_waves(kind, wm, wn, grouped)
         nc = sb // 16
         self.J = nc // 4 if kind == FP8 else nc // 2
         rows_per_copy = 1024 // sb
-        a_loads = -(-(bm // rows_per_copy) // nw)
-        b_loads = -(-(bn // rows_per_copy) // nw)
+        a_loads = -(-(bm // rows_per_copy) // nwc)
+        b_loads = -(-(bn // rows_per_copy) // nwc)
         self.n_dma = a_loads + b_loads
+        self.copies = copies
         tn, tm = bn // wn, bm // wm
         fn, fm = tn // 32, tm // 32
         wide, b_row = bool(sv & 1), kind == FP8 and bool(sv & 2)
@@ -88,7 +99,7 @@ class Schedule:
         """(scale loads, copies) of the chunk due at k-step g."""
         c = self.chunk_at(g)
         sc = self.nsc if (c == 0 or (c == 1 and not self.shared)) else 0
-        return sc, 2 * self.qpc
+        return sc, (2 * self.qpc if self.copies else 0)
 
     def interval(self, s):
         """(copies, scale loads) a wave issues between the barriers of stages s-1 and
@@ -102,7 +113,7 @@ class Schedule:
 
     def wait(self, s):
         """vmcnt at the barrier of stage s in the steady state: the loads issued
-        after the last copy of stage s+1."""
+        after the last copy of stage s+1 (a copying wave)."""
         ns, J, qpc = self.ns, self.J, self.qpc
         issued, last = 0, None
         st = s + 1
@@ -211,40 +222,56 @@ def test_every_gemm_instantiation_found(dis):
 
 
 def test_steady_loops_issue_and_wait_what_the_schedule_says(dis):
+    """Copying waves: copies, scale loads and vmcnt per barrier interval as the model
+    says.  The other waves issue no copies and wait for none (their scale words are
+    waited for by the compiler where it decodes them): their loops must issue exactly
+    the model's scale loads and no copy."""
     checked = 0
     for args, ins in kernels(dis).items():
         kind, bm, bn, wm, wn, sb, ns, pr, grouped, sv, koff, epi = args
         assert pr == 1, args
-        models = [Schedule(kind, bm, bn, wm, wn, sb, ns, sv, scales=True)]
-        if grouped and wm > 1 and wm * wn > 4:
+        nw, nwc = wm * wn, copying_waves(kind, wm, wn, grouped)
+        # (model, its waits checked, whether it runs MFMAs)
+        models = [(Schedule(kind, bm, bn, wm, wn, sb, ns, sv, True, grouped, True), True, True)]
+        if nwc < nw:
+            models.append((Schedule(kind, bm, bn, wm, wn, sb, ns, sv, True, grouped, False), False, True))
+        if grouped and wm > 1 and nw > 4:
             # the lower row of waves runs an expert's half-height last tile without
             # MFMAs and without scale loads
-            models.append(Schedule(kind, bm, bn, wm, wn, sb, ns, sv, scales=False))
-        U = models[0].U
-        want = {}
-        for m in models:
-            seq = [m.interval(s) + (m.wait(s),) for s in range(U, 2 * U)]
-            for r in rotations(seq):
-                want[r] = m.nsc > 0 or kind == BF16
+            models.append((Schedule(kind, bm, bn, wm, wn, sb, ns, sv, False, grouped, nwc == nw),
+                           nwc == nw, False))
+        U = models[0][0].U
+        keys = []   # per model: the rotations of its per-barrier sequence
+        for m, waits, _ in models:
+            seq = [m.interval(s) + ((m.wait(s),) if waits else ()) for s in range(U, 2 * U)]
+            keys.append(set(rotations(seq)))
         loops = stage_loops(ins, U)
         assert loops, f"no steady stage loop found in gemm_kernel{args}"
-        seen_scales = set()
+        matched = [False] * len(models)
         for body in loops:
             got = tuple(observed(body))
-            assert got in want, f"gemm_kernel{args}: loop issues/waits {got}"
-            seen_scales.add(want[got])
-        if len(models) > 1:
-            assert seen_scales == {True, False} or kind == BF16, args
+            hit = False
+            for i, (_, waits, _) in enumerate(models):
+                if (got if waits else tuple(x[:2] for x in got)) in keys[i]:
+                    matched[i] = hit = True
+            assert hit, f"gemm_kernel{args}: loop issues/waits {got}"
+        # every variant of the tile body has its loop (BF16's two waves without copies
+        # load no scale words either, so one loop can stand for both)
+        assert all(matched), (args, matched)
         checked += 1
     assert checked >= 60
 
 
 def test_model_matches_the_known_fp4_schedule():
-    """The waits the kernel template derives for dense FP4 (read off its assembly when
-    the scale loads were first counted): 12 and 9 at alternate barriers, the 9 after
-    the interval that holds a pair's two scale-load chunks (four loads)."""
+    """The waits the kernel template derives for dense FP4, read off its assembly: a
+    copying wave (the upper row issues every copy, eight a stage) waits for 20 and 13
+    at alternate barriers, the 13 after the interval that holds a pair's two
+    scale-load chunks (four loads); dense FP8, where every wave copies (four a stage),
+    for 10 and 7."""
     m = Schedule(FP4, 256, 256, 2, 4, 64, 5, 1)
-    assert [m.wait(s) for s in range(10, 14)] == [12, 9, 12, 9]
-    assert [m.interval(s) for s in range(10, 14)] == [(4, 0), (4, 4), (4, 0), (4, 4)]
+    assert [m.wait(s) for s in range(10, 14)] == [20, 13, 20, 13]
+    assert [m.interval(s) for s in range(10, 14)] == [(8, 0), (8, 4), (8, 0), (8, 4)]
+    m = Schedule(FP4, 256, 256, 2, 4, 64, 5, 1, copies=False)
+    assert [m.interval(s) for s in range(10, 14)] == [(0, 0), (0, 4), (0, 0), (0, 4)]
     m = Schedule(FP8, 256, 256, 2, 4, 64, 5, 1)
     assert [m.wait(s) for s in range(10, 12)] == [10, 7]
