@@ -1113,13 +1113,17 @@ void gemm_kernel(const GemmArgs args) {
             stage_quad(row, 4 * (8 * (r / 4) + 4 * elg + r % 4), acc[a][0][r], acc[a][1][r], acc[a][2][r],
                        acc[a][3][r]);
         } else if constexpr (T::PERM) {
-          // two B fragments: the same register of both holds two consecutive columns
+          // two B fragments: the same register of both holds two consecutive columns,
+          // so a register quad holds one whole 16-byte chunk (8 columns), written with
+          // one 16-byte store instead of four 4-byte ones (grouped FP4 MoE shape -0.7%)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int col = 2 * (8 * (r / 4) + 4 * elg + r % 4);
-            const int chunk = (col >> 3) ^ T::epi_swz(row);
-            *(uint32_t*)(stg + row * T::EPI_ROW + 16 * chunk + 2 * (col & 7)) =
-                pack_bf16x2(acc[a][0][r], acc[a][1][r]);
+          for (int q = 0; q < 4; ++q) {
+            const int chunk = (2 * q + elg) ^ T::epi_swz(row);
+            const i32x4_t w = {(int)pack_bf16x2(acc[a][0][4 * q], acc[a][1][4 * q]),
+                               (int)pack_bf16x2(acc[a][0][4 * q + 1], acc[a][1][4 * q + 1]),
+                               (int)pack_bf16x2(acc[a][0][4 * q + 2], acc[a][1][4 * q + 2]),
+                               (int)pack_bf16x2(acc[a][0][4 * q + 3], acc[a][1][4 * q + 3])};
+            *(i32x4_t*)(stg + row * T::EPI_ROW + 16 * chunk) = w;
           }
         } else {
 #pragma unroll
