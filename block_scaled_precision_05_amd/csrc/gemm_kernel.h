@@ -180,9 +180,9 @@ struct GemmTile {
   static constexpr int A_LOADS = (A_COPIES + NWC - 1) / NWC; // copies per copying wave per stage
   static constexpr int B_LOADS = (B_COPIES + NWC - 1) / NWC;
   static constexpr int N_DMA = A_LOADS + B_LOADS;
-  // When the copies do not split evenly over the copying waves, the short waves issue an
-  // out-of-range copy into a spare 1 KiB of LDS instead, so every wave issues the
-  // same number of copies and the vmcnt arithmetic holds for all of them.
+  // When the copies do not split evenly over the copying waves, the short waves issue
+  // an out-of-range copy into a spare 1 KiB of LDS instead, so every copying wave
+  // issues the same number of copies and the vmcnt arithmetic holds for all of them.
   static constexpr bool DUMMY = A_LOADS * NWC != A_COPIES || B_LOADS * NWC != B_COPIES;
   static constexpr int LDS_BYTES = NS * STAGE_BYTES + (DUMMY ? 1024 : 0);
   // Epilogue staging: each wave's TM x TN bf16 block, row-major (EPI_ROW bytes a
